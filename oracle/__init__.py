@@ -1,0 +1,180 @@
+"""fp64 CPU oracle for the 2D convolution forward pass.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+benchmark's CPU-baseline leg may import this package.  It shares no code with
+the GPU library and never imports it; the GPU library never imports this.
+
+The arithmetic lives in ``conv2d_oracle.c`` (plain C, fp64, the loop nest of
+the definition); this module builds it with gcc, loads it with ctypes and adds
+the explicit im2col x GEMM lowering used by the oracle's self-tests
+(page "How a GPU executes NN convolution", lincklin.cn, section 7: the
+convolution is W_matrix [Cout x Cin*Kh*Kw] times X_matrix [Cin*Kh*Kw x N*Ho*Wo];
+"lpnh.cn/news/2674933" section 4.3: a grouped convolution is G such products
+on contiguous channel blocks).
+
+Arrays are NCHW activations, [Cout][Cin/G][Kh][Kw] weights, fp64.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "conv2d_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_libs = {}
+
+
+def build(force: bool = True, src: str = _SRC, out: str = _LIB) -> str:
+    """Compile the C oracle (default ``oracle/liboracle.so``) with gcc -O2 -fopenmp."""
+    if not force and os.path.exists(out) and os.path.getmtime(out) >= os.path.getmtime(src):
+        return out
+    tmp = out + ".tmp"
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99", "-Wall", "-Wextra",
+           src, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def load_library(path: str | None = None):
+    """ctypes handle of the oracle library (the default one, built on demand,
+    or another build of the same source given by ``path``)."""
+    key = path or _LIB
+    if key in _libs:
+        return _libs[key]
+    if path is None and (not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC)):
+        build()
+    lib = ctypes.CDLL(key)
+    L, P = ctypes.c_long, ctypes.c_void_p
+    lib.oracle_out_dim.restype = L
+    lib.oracle_out_dim.argtypes = [L] * 5
+    lib.oracle_conv2d_f64.restype = ctypes.c_int
+    lib.oracle_conv2d_f64.argtypes = [P, P, P, ctypes.c_int, P, P] + [L] * 11
+    lib.oracle_conv2d_points_f64.restype = ctypes.c_int
+    lib.oracle_conv2d_points_f64.argtypes = [P, P, P, ctypes.c_int, P, L, P, P] + [L] * 11
+    lib.oracle_im2col_f64.restype = ctypes.c_int
+    lib.oracle_im2col_f64.argtypes = [P, P] + [L] * 9
+    _libs[key] = lib
+    return lib
+
+
+def _load(lib=None):
+    return lib if lib is not None else load_library()
+
+
+def _f64(a):
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def out_dim(size: int, k: int, stride: int = 1, pad: int = 0, dilation: int = 1, lib=None) -> int:
+    """floor((size + 2*pad - dilation*(k-1) - 1)/stride) + 1 (lpnh.cn section 6.2)."""
+    return int(_load(lib).oracle_out_dim(size, k, stride, pad, dilation))
+
+
+def effective_kernel(k: int, dilation: int) -> int:
+    """Span of a dilated filter: k + (k-1)(dilation-1) (lpnh.cn sections 2.3, 4.2)."""
+    return k + (k - 1) * (dilation - 1)
+
+
+def conv2d(x, w, bias=None, stride=1, pad=0, dilation=1, groups=1, relu=False,
+           with_scale=True, lib=None):
+    """Direct-loop convolution in fp64.  Returns (y, S) with S = sum|x*w| over
+    the valid taps (or (y, None) when ``with_scale`` is False)."""
+    x, w = _f64(x), _f64(w)
+    N, Cin, H, W = x.shape
+    Cout, cin_g, Kh, Kw = w.shape
+    if cin_g * groups != Cin:
+        raise ValueError("weight shape does not match Cin/groups")
+    b = None if bias is None else _f64(bias)
+    Ho = out_dim(H, Kh, stride, pad, dilation, lib=lib)
+    Wo = out_dim(W, Kw, stride, pad, dilation, lib=lib)
+    if Ho < 1 or Wo < 1:
+        raise ValueError("empty output")
+    y = np.empty((N, Cout, Ho, Wo), np.float64)
+    s = np.empty_like(y) if with_scale else None
+    rc = _load(lib).oracle_conv2d_f64(_ptr(x), _ptr(w), _ptr(b), int(bool(relu)), _ptr(y), _ptr(s),
+                                   N, Cin, H, W, Cout, Kh, Kw, stride, pad, dilation, groups)
+    if rc:
+        raise ValueError(f"oracle_conv2d_f64 rejected the shape (rc={rc})")
+    return y, s
+
+
+def conv2d_points(x, w, idx, bias=None, stride=1, pad=0, dilation=1, groups=1, relu=False,
+                  lib=None):
+    """Selected outputs by flat NCHW index.  Returns (y[idx], S[idx])."""
+    x, w = _f64(x), _f64(w)
+    N, Cin, H, W = x.shape
+    Cout, _, Kh, Kw = w.shape
+    b = None if bias is None else _f64(bias)
+    idx = np.ascontiguousarray(idx, dtype=np.int64)
+    y = np.empty(idx.shape[0], np.float64)
+    s = np.empty_like(y)
+    rc = _load(lib).oracle_conv2d_points_f64(_ptr(x), _ptr(w), _ptr(b), int(bool(relu)), _ptr(idx),
+                                          idx.shape[0], _ptr(y), _ptr(s), N, Cin, H, W, Cout,
+                                          Kh, Kw, stride, pad, dilation, groups)
+    if rc:
+        raise ValueError(f"oracle_conv2d_points_f64 rejected the call (rc={rc})")
+    return y, s
+
+
+def im2col(x, Kh, Kw, stride=1, pad=0, dilation=1, lib=None):
+    """Explicit im2col: [C*Kh*Kw][N*Ho*Wo], rows (c,kh,kw), columns (n,ho,wo)."""
+    x = _f64(x)
+    N, C, H, W = x.shape
+    Ho = out_dim(H, Kh, stride, pad, dilation, lib=lib)
+    Wo = out_dim(W, Kw, stride, pad, dilation, lib=lib)
+    xcol = np.empty((C * Kh * Kw, N * Ho * Wo), np.float64)
+    rc = _load(lib).oracle_im2col_f64(_ptr(x), _ptr(xcol), N, C, H, W, Kh, Kw, stride, pad, dilation)
+    if rc:
+        raise ValueError(f"oracle_im2col_f64 rejected the shape (rc={rc})")
+    return xcol
+
+
+def conv2d_by_gemm(x, w, bias=None, stride=1, pad=0, dilation=1, groups=1, relu=False,
+                   lib=None):
+    """Explicit lowering: per group, W_g [Cout/G x (Cin/G)*Kh*Kw] @ im2col(X_g),
+    then reshape the [Cout x N*Ho*Wo] product back to NCHW."""
+    x, w = _f64(x), _f64(w)
+    N, Cin, H, W = x.shape
+    Cout, cin_g, Kh, Kw = w.shape
+    cout_g = Cout // groups
+    Ho = out_dim(H, Kh, stride, pad, dilation, lib=lib)
+    Wo = out_dim(W, Kw, stride, pad, dilation, lib=lib)
+    parts = []
+    for g in range(groups):
+        xcol = im2col(x[:, g * cin_g:(g + 1) * cin_g], Kh, Kw, stride, pad, dilation, lib=lib)
+        wmat = w[g * cout_g:(g + 1) * cout_g].reshape(cout_g, cin_g * Kh * Kw)
+        parts.append(wmat @ xcol)
+    y = np.concatenate(parts, axis=0).reshape(Cout, N, Ho, Wo).transpose(1, 0, 2, 3)
+    if bias is not None:
+        y = y + _f64(bias)[None, :, None, None]
+    if relu:
+        y = np.maximum(y, 0.0)
+    return np.ascontiguousarray(y)
+
+
+def round_to_bf16(v):
+    """Round fp64 values to the nearest bf16 (ties to even), returned as fp64.
+
+    Used where a test compares an exactly-representable fp32 result (the
+    exact-integer mode) with a bf16 output: both sides take the fp32 -> bf16
+    decision with round-to-nearest-even.  Values here are exact in fp32, so
+    the fp64 -> fp32 step is exact.
+    """
+    a = np.ascontiguousarray(v, dtype=np.float64).astype(np.float32)
+    u = a.view(np.uint32).astype(np.uint64)
+    keep = u >> 16
+    rem = u & 0xFFFF
+    up = (rem > 0x8000) | ((rem == 0x8000) & ((keep & 1) == 1))
+    r = ((keep + up.astype(np.uint64)) << 16).astype(np.uint32)
+    out = r.view(np.float32).astype(np.float64)
+    out[np.isnan(a)] = np.nan
+    return out

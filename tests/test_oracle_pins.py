@@ -1,0 +1,460 @@
+"""Pins of the fp64 oracle to facts the pages and mathematics fix (CPU only).
+
+Each test ties the oracle to something other than itself: a matrix or a shape
+the pages print, a closed form, a library routine (torch CPU float64), or an
+independent formulation (explicit im2col x GEMM).  The planted-mistake tests
+at the end build mutated copies of the oracle source and check that these pins
+reject each mutation.
+"""
+import json
+import math
+import os
+import re
+import shutil
+import tempfile
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import conv_inputs as ci
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+FIG = json.load(open(os.path.join(GOLDEN, "page_figures.json")))
+
+
+def _torch_conv(x, w, b, stride, pad, dil, groups, relu=False):
+    y = F.conv2d(torch.from_numpy(np.asarray(x, np.float64)), torch.from_numpy(np.asarray(w, np.float64)),
+                 None if b is None else torch.from_numpy(np.asarray(b, np.float64)),
+                 stride=stride, padding=pad, dilation=dil, groups=groups)
+    if relu:
+        y = torch.relu(y)
+    return y.numpy()
+
+
+# ------------------------------------------------------------- p1: im2col matrix
+
+def test_p1_im2col_matches_printed_matrix():
+    """3x3 input a..i, 2x2 kernel, stride 1 -> the 4x4 X_col printed on the
+    lincklin.cn page, section 8.  Entries are distinct powers of two so each
+    cell identifies exactly one input symbol."""
+    rows = [ln.split() for ln in open(os.path.join(GOLDEN, "im2col_3x3_input_2x2_kernel.txt"))
+            if ln.strip() and not ln.startswith("#")]
+    sym = "abcdefghi"
+    val = {s: float(2 ** i) for i, s in enumerate(sym)}
+    x = np.array([val[s] for s in sym]).reshape(1, 1, 3, 3)
+    xcol = oracle.im2col(x, 2, 2, stride=1, pad=0)
+    expect = np.array([[val[s] for s in r] for r in rows])
+    assert xcol.shape == (4, 4)
+    np.testing.assert_array_equal(xcol, expect)
+    # columns are windows: column j is window j flattened row-major
+    np.testing.assert_array_equal(xcol[:, 0], [val[s] for s in "abde"])
+    np.testing.assert_array_equal(xcol[:, 3], [val[s] for s in "efhi"])
+
+
+# ------------------------------------------------------------- p2: small case
+
+def test_p2_small_im2col_shapes_and_gemm_equivalence():
+    f = FIG["small_im2col"]
+    rng = np.random.default_rng(7)
+    x = rng.integers(-3, 4, size=(1, f["C"], f["H"], f["W"])).astype(np.float64)
+    w = rng.integers(-3, 4, size=(1, f["C"], f["K"], f["K"])).astype(np.float64)
+    xcol = oracle.im2col(x, f["K"], f["K"], f["stride"], f["pad"])
+    assert xcol.shape == (f["xcol_rows"], f["xcol_cols"])
+    y, _ = oracle.conv2d(x, w, stride=f["stride"], pad=f["pad"])
+    assert y.shape[2:] == (f["Ho"], f["Wo"])
+    # direct loop == W_row @ X_col exactly on integer data (lpnh.cn section 3.1)
+    np.testing.assert_array_equal(y.reshape(-1), (w.reshape(1, -1) @ xcol).reshape(-1))
+    # each column is the flattened window at that output position
+    np.testing.assert_array_equal(xcol[:, 1], x[0, 0, 0:3, 1:4].reshape(-1))
+    np.testing.assert_array_equal(xcol[:, 2], x[0, 0, 1:4, 0:3].reshape(-1))
+
+
+# ------------------------------------------------------------- p3: first layer
+
+def test_p3_first_layer_shape_and_impulse_response():
+    """224x224x3 -> 112x112x32, stride 2, pad 1 (lpnh.cn section 2.1).
+    A unit impulse at input (c=1, h=113, w=57) reaches exactly the outputs
+    whose window covers it, each with the weight of the covering tap:
+    2*ho + kh - 1 = 113 and 2*wo + kw - 1 = 57."""
+    f = FIG["first_layer"]
+    x = np.zeros((1, f["Cin"], f["H"], f["W"]))
+    x[0, 1, 113, 57] = 1.0
+    rng = np.random.default_rng(3)
+    w = rng.standard_normal((f["Cout"], f["Cin"], f["K"], f["K"]))
+    y, s = oracle.conv2d(x, w, stride=f["stride"], pad=f["pad"])
+    assert y.shape == (1, f["Cout"], f["Ho"], f["Wo"])
+    expect = np.zeros_like(y)
+    # 2*57 + 0 - 1 = 113, 2*56 + 2 - 1 = 113; 2*29 + 0 - 1 = 57, 2*28 + 2 - 1 = 57
+    expect[0, :, 57, 29] = w[:, 1, 0, 0]
+    expect[0, :, 57, 28] = w[:, 1, 0, 2]
+    expect[0, :, 56, 29] = w[:, 1, 2, 0]
+    expect[0, :, 56, 28] = w[:, 1, 2, 2]
+    np.testing.assert_array_equal(y, expect)
+
+
+def test_p3_first_layer_single_point_hand_check():
+    """The page computes one output by hand: the 27 input values of the 3x3
+    neighbourhood over 3 channels times the 27 weights, summed, plus the bias.
+    Interior point (ho, wo) = (56, 56): window rows/cols 111..113."""
+    x, w, b = ci.layer_tensors(1, 0)
+    y, s = oracle.conv2d(x, w, b, stride=2, pad=1)
+    for co in (0, 13, 31):
+        terms = [float(x[0, c, 111 + dh, 111 + dw]) * float(w[co, c, dh, dw])
+                 for c in range(3) for dh in range(3) for dw in range(3)]
+        assert len(terms) == FIG["first_layer"]["products_per_output"]
+        hand = math.fsum(terms) + float(b[co])
+        assert abs(y[0, co, 56, 56] - hand) <= 1e-14 * (s[0, co, 56, 56] + abs(b[co]))
+
+
+def test_p3_corner_and_far_edge_tap_counts():
+    """With |x| = |w| = 1, S counts the valid taps: the (0,0) corner of the
+    stride-2 pad-1 layer sees 2x2 taps per channel (12), and the last output
+    row/col never reads the bottom/right padding (last hi = 2*111 + 2 - 1 = 223)."""
+    x = np.ones((1, 3, 224, 224))
+    w = np.ones((32, 3, 3, 3))
+    _, s = oracle.conv2d(x, w, stride=2, pad=1)
+    assert s[0, 0, 0, 0] == 12
+    assert s[0, 0, 111, 111] == 27
+    assert s[0, 0, 0, 111] == 18
+
+
+# ------------------------------------------------------------- p4: tap counts
+
+@pytest.mark.parametrize("entry", FIG["macs_per_output"], ids=lambda e: str(e["macs"]))
+def test_p4_macs_per_interior_output(entry):
+    Cin, K = entry["Cin"], entry["K"]
+    x = np.ones((1, Cin, 5, 5))
+    w = -np.ones((2, Cin, K, K))
+    y, s = oracle.conv2d(x, w, stride=1, pad=1)
+    assert s[0, 0, 2, 2] == entry["macs"]
+    assert y[0, 1, 2, 2] == -entry["macs"]
+
+
+# ------------------------------------------------------------- p5: output size
+
+def test_p5_output_sizes():
+    assert oracle.out_dim(224, 3, 2, 1, 1) == FIG["first_layer"]["Ho"]
+    assert oracle.out_dim(4, 3, 1, 0, 1) == FIG["small_im2col"]["Ho"]
+    assert oracle.out_dim(3, 2, 1, 0, 1) == 2            # lincklin.cn section 8 example
+    d = FIG["dilation"]
+    assert oracle.effective_kernel(d["K"], d["dilation"]) == d["K_eff"]
+    # a dilated 3x3 spans exactly as far as a 5x5: identical output sizes
+    for n in (5, 6, 7, 64, 65):
+        for s in (1, 2, 3):
+            for p in (0, 1, 2):
+                assert oracle.out_dim(n, 3, s, p, 2) == oracle.out_dim(n, 5, s, p, 1)
+    # the workloads' output sizes (the first is stated as 1x32x112x112)
+    expected = {(1, 0): 112, (2, 0): 112, (3, 0): 56, (3, 1): 56, (4, 0): 64,
+                (5, 0): 56, (5, 1): 56, (5, 2): 56, (5, 3): 28}
+    for (cid, li), ho in expected.items():
+        ly = ci.layer(cid, li)
+        assert oracle.out_dim(ly.H, ly.Kh, ly.stride, ly.pad, ly.dilation) == ho
+    # too-small inputs give an empty output, which the oracle rejects
+    assert oracle.out_dim(2, 3, 1, 0, 1) <= 0
+    assert oracle.out_dim(3, 3, 1, 0, 2) <= 0
+    with pytest.raises(ValueError):
+        oracle.conv2d(np.ones((1, 1, 2, 2)), np.ones((1, 1, 3, 3)))
+
+
+def test_p5_floor_division():
+    # (7 + 2 - 2 - 1)/2 = 3 -> 4 outputs; (6 + 0 - 2 - 1)/2 = 1.5 -> floor 1 -> 2 outputs
+    assert oracle.out_dim(7, 3, 2, 1, 1) == 4
+    assert oracle.out_dim(6, 3, 2, 0, 1) == 2
+    assert oracle.out_dim(9, 3, 3, 0, 1) == 3
+    assert oracle.out_dim(10, 3, 3, 0, 1) == 3
+
+
+# ------------------------------------------------------------- p6: dilation
+
+@pytest.mark.parametrize("dil,pad,stride", [(2, 2, 1), (2, 0, 1), (3, 1, 2), (2, 1, 2)])
+def test_p6_dilation_equals_zero_inserted_kernel(dil, pad, stride):
+    """A dilated KxK filter is a K_eff x K_eff filter with zeros between taps
+    (lpnh.cn section 4.2); on integer data the results agree exactly."""
+    rng = np.random.default_rng(11)
+    x = rng.integers(-3, 4, size=(2, 4, 13, 11)).astype(np.float64)
+    w = rng.integers(-3, 4, size=(6, 2, 3, 3)).astype(np.float64)
+    ke = oracle.effective_kernel(3, dil)
+    we = np.zeros((6, 2, ke, ke))
+    we[:, :, ::dil, ::dil] = w
+    y1, s1 = oracle.conv2d(x, w, stride=stride, pad=pad, dilation=dil, groups=2)
+    y2, _ = oracle.conv2d(x, we, stride=stride, pad=pad, dilation=1, groups=2)
+    np.testing.assert_array_equal(y1, y2)
+    # only the K*K taps are gathered: S counts at most 2*9 products per output
+    xs = np.ones_like(x)
+    _, s3 = oracle.conv2d(xs, np.ones_like(w), stride=stride, pad=pad, dilation=dil, groups=2)
+    assert s3.max() == 2 * FIG["dilation"]["valid_taps"]
+
+
+# ------------------------------------------------------------- p7: groups
+
+@pytest.mark.parametrize("G", [2, 4])
+def test_p7_groups_equal_independent_convs(G):
+    rng = np.random.default_rng(5)
+    Cin, Cout = 8, 12
+    x = rng.standard_normal((2, Cin, 9, 10))
+    w = rng.standard_normal((Cout, Cin // G, 3, 3))
+    b = rng.standard_normal(Cout)
+    y, _ = oracle.conv2d(x, w, b, stride=1, pad=1, groups=G, relu=True)
+    ci_g, co_g = Cin // G, Cout // G
+    parts = [oracle.conv2d(x[:, g * ci_g:(g + 1) * ci_g], w[g * co_g:(g + 1) * co_g],
+                           b[g * co_g:(g + 1) * co_g], stride=1, pad=1, relu=True)[0]
+             for g in range(G)]
+    np.testing.assert_array_equal(y, np.concatenate(parts, axis=1))
+
+
+# ------------------------------------------------------------- p8: depthwise
+
+def test_p8_depthwise_is_per_channel_conv():
+    rng = np.random.default_rng(8)
+    C = 6
+    x = rng.standard_normal((2, C, 8, 7))
+    wdw = rng.standard_normal((C, 1, 3, 3))
+    y, _ = oracle.conv2d(x, wdw, stride=1, pad=1, groups=C)
+    for c in range(C):
+        yc, _ = oracle.conv2d(x[:, c:c + 1], wdw[c:c + 1], stride=1, pad=1)
+        np.testing.assert_array_equal(y[:, c:c + 1], yc)
+
+
+def test_p8_separable_equals_factorised_standard_conv():
+    """Depthwise then pointwise (lnrq.cn section 3.1, no nonlinearity between)
+    is one standard conv whose weight factorises W[co,ci,kh,kw] =
+    Wpw[co,ci] * Wdw[ci,kh,kw] (linearity)."""
+    rng = np.random.default_rng(9)
+    Cin, Cout = 5, 7
+    x = rng.integers(-3, 4, size=(2, Cin, 9, 8)).astype(np.float64)
+    wdw = rng.integers(-3, 4, size=(Cin, 1, 3, 3)).astype(np.float64)
+    wpw = rng.integers(-3, 4, size=(Cout, Cin, 1, 1)).astype(np.float64)
+    t, _ = oracle.conv2d(x, wdw, stride=2, pad=1, groups=Cin)
+    y, _ = oracle.conv2d(t, wpw)
+    wstd = wpw[:, :, 0, 0][:, :, None, None] * wdw[:, 0][None, :, :, :]
+    y2, _ = oracle.conv2d(x, wstd, stride=2, pad=1)
+    np.testing.assert_array_equal(y, y2)
+
+
+# ------------------------------------------------------------- p9: 1x1 = GEMM
+
+def test_p9_pointwise_is_gemm():
+    rng = np.random.default_rng(10)
+    x = rng.standard_normal((3, 16, 7, 9))
+    w = rng.standard_normal((24, 16, 1, 1))
+    b = rng.standard_normal(24)
+    y, s = oracle.conv2d(x, w, b)
+    for n in range(3):
+        g = w[:, :, 0, 0] @ x[n].reshape(16, -1) + b[:, None]
+        assert np.all(np.abs(y[n].reshape(24, -1) - g) <= 1e-12 * (s[n].reshape(24, -1) + 1))
+
+
+# ------------------------------------------------------------- p10: padding
+
+def test_p10_all_ones_input_border_closed_form():
+    """All-ones input (lpnh.cn section 6.4): each output is the bias plus the
+    sum of the weights whose tap lands inside the image; at a 3x3 pad-1 border
+    the zero ring removes a row and/or column of the filter (lincklin.cn
+    section 26)."""
+    rng = np.random.default_rng(12)
+    w = rng.integers(-5, 6, size=(1, 1, 3, 3)).astype(np.float64)
+    b = np.array([0.5])
+    y, _ = oracle.conv2d(np.ones((1, 1, 5, 6)), w, b, stride=1, pad=1)
+    k = w[0, 0]
+    Y = y[0, 0] - 0.5
+    assert Y[0, 0] == k[1:, 1:].sum() and Y[0, 5] == k[1:, :2].sum()
+    assert Y[4, 0] == k[:2, 1:].sum() and Y[4, 5] == k[:2, :2].sum()
+    assert Y[0, 3] == k[1:, :].sum() and Y[4, 2] == k[:2, :].sum()
+    assert Y[2, 0] == k[:, 1:].sum() and Y[1, 5] == k[:, :2].sum()
+    assert np.all(Y[1:4, 1:5] == k.sum())
+
+
+def test_p10_dilated_border_closed_form():
+    """Dilation 2, pad 2: the zero border is two pixels thick, and a border
+    output loses the whole first (or last) tap row/column."""
+    rng = np.random.default_rng(13)
+    w = rng.integers(-5, 6, size=(1, 1, 3, 3)).astype(np.float64)
+    y, _ = oracle.conv2d(np.ones((1, 1, 8, 8)), w, stride=1, pad=2, dilation=2)
+    k, Y = w[0, 0], y[0, 0]
+    for i in (0, 1):
+        assert Y[i, 4] == k[1:, :].sum() and Y[4, i] == k[:, 1:].sum()
+        assert Y[7 - i, 4] == k[:2, :].sum() and Y[4, 7 - i] == k[:, :2].sum()
+    assert Y[0, 0] == k[1:, 1:].sum() and Y[1, 7] == k[1:, :2].sum()
+    assert np.all(Y[2:6, 2:6] == k.sum())
+
+
+# ------------------------------------------------------------- p11: sweep
+
+def _sweep_cases():
+    cases = []
+    rng = np.random.default_rng(2024)
+    for S in (1, 2, 3):
+        for P in (0, 1, 2):
+            for D in (1, 2, 3):
+                for K in (1, 2, 3, 5):
+                    Gs = (1, 2, 4)
+                    G = Gs[int(rng.integers(0, 3))]
+                    H = int(rng.integers(5, 12)) | 1
+                    W = int(rng.integers(4, 13))
+                    cases.append((S, P, D, K, G, H, W))
+    return cases
+
+
+def test_p11_direct_equals_im2col_gemm_and_torch_sweep():
+    rng = np.random.default_rng(99)
+    checked = 0
+    for S, P, D, K, G, H, W in _sweep_cases():
+        Kh, Kw = K, max(1, K - 1) if K > 2 else K
+        if oracle.out_dim(H, Kh, S, P, D) < 1 or oracle.out_dim(W, Kw, S, P, D) < 1:
+            continue
+        Cin, Cout = 4, 8 if G != 4 else 4
+        x = rng.standard_normal((2, Cin, H, W))
+        w = rng.standard_normal((Cout, Cin // G, Kh, Kw))
+        b = rng.standard_normal(Cout)
+        y, s = oracle.conv2d(x, w, b, S, P, D, G, relu=False)
+        tol = 1e-12 * (s + np.abs(b)[None, :, None, None] + 1e-300)
+        yg = oracle.conv2d_by_gemm(x, w, b, S, P, D, G)
+        yt = _torch_conv(x, w, b, S, P, D, G)
+        assert yg.shape == y.shape == yt.shape
+        assert np.all(np.abs(y - yg) <= tol), (S, P, D, K, G, H, W)
+        assert np.all(np.abs(y - yt) <= tol), (S, P, D, K, G, H, W)
+        checked += 1
+    assert checked > 60
+
+
+def test_p11_depthwise_groups_equal_channels():
+    rng = np.random.default_rng(77)
+    x = rng.standard_normal((2, 8, 9, 7))
+    w = rng.standard_normal((8, 1, 3, 3))
+    b = rng.standard_normal(8)
+    for S, P, D in ((1, 1, 1), (2, 1, 1), (1, 2, 2), (2, 0, 1)):
+        y, s = oracle.conv2d(x, w, b, S, P, D, 8, relu=True)
+        yt = _torch_conv(x, w, b, S, P, D, 8, relu=True)
+        assert np.all(np.abs(y - yt) <= 1e-12 * (s + 1))
+
+
+# ------------------------------------------------------------- p12: torch at workload shapes
+
+@pytest.mark.parametrize("cid,li", [(1, 0), (2, 0), (3, 0), (3, 1), (4, 0), (5, 0), (5, 1), (5, 2), (5, 3)])
+def test_p12_torch_float64_at_workload_shapes(cid, li):
+    """Every workload layer at its real channel/spatial shape (batch 1) agrees
+    with torch's CPU float64 convolution within 1e-12 * S."""
+    ly = ci.layer(cid, li)
+    x, w, b = ci.layer_tensors(cid, li, N=1)
+    relu = bool(ly.epilogue & ci.EPI_RELU)
+    y, s = oracle.conv2d(x, w, b, ly.stride, ly.pad, ly.dilation, ly.groups, relu=relu)
+    yt = _torch_conv(x, w, b, ly.stride, ly.pad, ly.dilation, ly.groups, relu=relu)
+    bb = 0 if b is None else np.abs(b.astype(np.float64))[None, :, None, None]
+    assert y.shape == yt.shape
+    assert np.all(np.abs(y - yt) <= 1e-12 * (s + bb) + 1e-300)
+
+
+def test_p12_points_match_full_convolution():
+    x, w, b = ci.layer_tensors(4, 0, N=2, H=17, W=13)
+    y, s = oracle.conv2d(x, w, None, 1, 2, 2, 4)
+    rng = np.random.default_rng(1)
+    idx = rng.integers(0, y.size, size=500)
+    yp, sp = oracle.conv2d_points(x, w, idx, None, 1, 2, 2, 4)
+    np.testing.assert_array_equal(yp, y.reshape(-1)[idx])
+    np.testing.assert_array_equal(sp, s.reshape(-1)[idx])
+
+
+# ------------------------------------------------------------- p13: size arithmetic
+
+def test_p13_big_im2col_size_figures():
+    """X_col of a 112x112x128 input under a 3x3 filter is 1152 x 12544,
+    about 14.47 million entries / 55 MB in fp32, about 9x the 6.3 MB input
+    (lpnh.cn sections 3.2-3.3)."""
+    f = FIG["big_im2col"]
+    x = np.zeros((1, f["Cin"], f["H"], f["W"]))
+    xcol = oracle.im2col(x, f["K"], f["K"], f["stride"], f["pad"])
+    assert xcol.shape == (f["xcol_rows"], f["xcol_cols"])
+    assert f["weight_cols"] == f["Cin"] * f["K"] * f["K"]
+    n = xcol.size
+    assert abs(n - f["elements_approx"]) / f["elements_approx"] < 2e-3
+    mib = n * 4 / 2 ** 20
+    assert abs(mib - f["xcol_fp32_MB_approx"]) < 0.5
+    in_mb = f["Cin"] * f["H"] * f["W"] * 4 / 1e6
+    assert abs(in_mb - f["input_fp32_MB_approx"]) < 0.2
+    assert n / (f["Cin"] * f["H"] * f["W"]) == f["inflation_approx"]
+
+
+def test_p13_flop_counts():
+    """Nominal FLOPs = 2*N*Ho*Wo*Cout*(Cin/G)*Kh*Kw; depthwise drops the
+    Cout*Cin channel product to Cin (lincklin.cn section 23)."""
+    def flops(ly):
+        Ho = oracle.out_dim(ly.H, ly.Kh, ly.stride, ly.pad, ly.dilation)
+        Wo = oracle.out_dim(ly.W, ly.Kw, ly.stride, ly.pad, ly.dilation)
+        return 2 * ly.N * Ho * Wo * ly.Cout * (ly.Cin // ly.groups) * ly.Kh * ly.Kw
+    assert flops(ci.layer(2, 0)) == 2 * 32 * 112 * 112 * 256 * 1152
+    dw = ci.layer(3, 0)
+    assert flops(dw) == 2 * 32 * 56 * 56 * 144 * 9
+
+
+# ------------------------------------------------------------- generator
+
+def test_generator_bf16_round_to_nearest_even():
+    vals = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 1.0 + 2 ** -7 + 2 ** -9,
+                     -2.5, 3.0e38, np.inf], np.float32)
+    got = ci.bf16_bits_to_f32(ci.f32_to_bf16_bits(vals))
+    # ties at 1 + 2^-8 go to even (1.0); 1 + 3*2^-8 ties up to 1 + 2^-6
+    np.testing.assert_array_equal(got[:3], np.array([1.0, 1.0, 1.0 + 2 ** -6], np.float32))
+    assert got[3] == np.float32(1.0 + 2 ** -7)
+    assert got[4] == -2.5 and np.isinf(got[6])
+    assert np.all(oracle.round_to_bf16(vals[:6].astype(np.float64)) == got[:6])
+
+
+def test_generator_is_deterministic_and_bf16_exact():
+    a = ci.layer_tensors(5, 1, N=2, H=6, W=6)
+    b = ci.layer_tensors(5, 1, N=2, H=6, W=6)
+    for u, v in zip(a, b):
+        np.testing.assert_array_equal(u, v)
+    x, w, bias = a
+    np.testing.assert_array_equal(ci.bf16_bits_to_f32(ci.f32_to_bf16_bits(x)), x)
+    np.testing.assert_array_equal(ci.bf16_bits_to_f32(ci.f32_to_bf16_bits(w)), w)
+    assert abs(w.std() - ci.layer(5, 1).weight_std) < 0.01
+    assert bias is not None and bias.dtype == np.float32
+
+
+# ------------------------------------------------------------- planted mistakes
+
+_MUTATIONS = {
+    "drop_last_kw_tap": ("for (long kw = 0; kw < Kw; ++kw)", "for (long kw = 0; kw < Kw - (Kw > 1); ++kw)"),
+    "flipped_kernel": ("const long hi = ho * stride + kh * dil - pad;",
+                       "const long hi = ho * stride + (Kh - 1 - kh) * dil - pad;"),
+    "pad_sign": ("const long wi = wo * stride + kw * dil - pad;",
+                 "const long wi = wo * stride + kw * dil + pad;"),
+    "no_dilation": ("const long hi = ho * stride + kh * dil - pad;",
+                    "const long hi = ho * stride + kh - pad;"),
+    "wrong_group_base": ("const long c = g * cin_g + ci;", "const long c = ci;"),
+    "relu_before_bias": ("double v = acc + (bias ? bias[co] : 0.0);\n    if (relu && v < 0.0) v = 0.0;",
+                         "double v = (relu && acc < 0.0) ? 0.0 : acc;\n    v += (bias ? bias[co] : 0.0);"),
+}
+
+
+@pytest.fixture(scope="module")
+def mutant_libs():
+    src = open(os.path.join(os.path.dirname(oracle.__file__), "conv2d_oracle.c")).read()
+    tmp = tempfile.mkdtemp(prefix="oracle_mut_")
+    libs = {}
+    try:
+        for name, (a, b) in _MUTATIONS.items():
+            assert src.count(a) >= 1, name
+            path = os.path.join(tmp, f"{name}.c")
+            open(path, "w").write(src.replace(a, b, 1))
+            libs[name] = oracle.load_library(oracle.build(src=path, out=os.path.join(tmp, f"lib{name}.so")))
+        yield libs
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+
+
+@pytest.mark.parametrize("name", list(_MUTATIONS))
+def test_planted_mistake_is_caught(name, mutant_libs):
+    """Each planted mistake makes the torch cross-check of a small
+    dilated/grouped/padded conv with bias+ReLU fail."""
+    lib = mutant_libs[name]
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((2, 4, 9, 8))
+    w = rng.standard_normal((6, 2, 3, 3))
+    b = rng.standard_normal(6)
+    y, s = oracle.conv2d(x, w, b, 1, 2, 2, 2, relu=True, lib=lib)
+    yt = _torch_conv(x, w, b, 1, 2, 2, 2, relu=True)
+    assert not np.all(np.abs(y - yt) <= 1e-12 * (s + np.abs(b)[None, :, None, None]))
