@@ -1,0 +1,270 @@
+#!/usr/bin/env python3
+"""conv2d forward throughput on one MI355X, against the kernel's roofline.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--layer CID:LI | --all]
+
+A step is one forward pass of the workload layer through the timed C entry
+``conv2d_fwd_nhwc_packed`` (channels-last activations already resident in
+HBM, weights packed once beforehand): host plan -> kernel with the fused
+bias+ReLU epilogue.  The default workload is the 3x3 bf16 layer
+N=32, 128x112x112 -> 256, stride 1, pad 1, bias+ReLU (implicit GEMM with
+M=256, K=1152, N*Ho*Wo=401408).  ``--layer`` / ``--all`` time the other
+workload layers (one JSON line each).
+
+Timing: W untimed warm-up steps, then exactly K steps between two
+torch.cuda.synchronize() calls (wall clock -> ms_per_step and value).  Input
+and output buffers rotate over R sets whose total size is >= 512 MB, so the
+256 MB Infinity Cache cannot hold the working set across steps.  Each launch
+is also bracketed by HIP events on the stream it runs on; their mean is the
+kernel duration used for the roofline figures.
+
+Roofline: achieved = algorithmic FLOPs (2*N*Ho*Wo*Cout*(Cin/G)*Kh*Kw) or
+algorithmic bytes (x, w, bias and y each moved once) per launch / mean launch
+duration; peak = MI355X dense bf16 MFMA 2516.6 TFLOP/s (256 CU x 2.4 GHz x
+4096 FLOP/clk), fp32 vector 157.3 TFLOP/s, or HBM3E 8000 GB/s.  traffic is the
+HBM byte count measured with rocprofv3 counters for this kernel source, read
+from profiles/traffic.json, or null when the kernel source changed since.
+
+cpu_baseline: the fp64 oracle (test infrastructure) on a bounded sample of the
+same workload -- whole images, all channels -- run on the host cores until
+about --cpu-seconds have passed, scaled to the metric's unit.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import conv_inputs as ci  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2516.6
+PEAK_FP32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+ROTATE_BYTES = 512 << 20
+METRIC = "conv2d fwd TFLOP/s (GB/s for depthwise) and % of MI355X roofline, 1 GPU"
+KERNEL_SOURCES = {"direct": "direct.hip", "depthwise": "depthwise.hip", "gemm1x1": "igemm.hip",
+                  "igemm": "igemm.hip"}
+
+
+def out_hw(ly):
+    ho = (ly.H + 2 * ly.pad - ly.dilation * (ly.Kh - 1) - 1) // ly.stride + 1
+    wo = (ly.W + 2 * ly.pad - ly.dilation * (ly.Kw - 1) - 1) // ly.stride + 1
+    return ho, wo
+
+
+def algorithmic(ly):
+    """Nominal FLOPs and bytes (each tensor moved once) of one launch."""
+    ho, wo = out_hw(ly)
+    esz = 4 if ly.dtype == ci.F32 else 2
+    flops = 2 * ly.N * ho * wo * ly.Cout * (ly.Cin // ly.groups) * ly.Kh * ly.Kw
+    nbytes = esz * (ly.N * ly.Cin * ly.H * ly.W + ly.Cout * (ly.Cin // ly.groups) * ly.Kh * ly.Kw
+                    + ly.N * ly.Cout * ho * wo)
+    if ly.epilogue & ci.EPI_BIAS:
+        nbytes += 4 * ly.Cout
+    return flops, nbytes
+
+
+def bound_of(ly):
+    """Binding roof: FLOP/byte against the ridge of the layer's dtype."""
+    flops, nbytes = algorithmic(ly)
+    peak = PEAK_FP32_TFLOPS if ly.dtype == ci.F32 else PEAK_BF16_TFLOPS
+    ridge = peak * 1e12 / (PEAK_HBM_GBS * 1e9)
+    return ("mfma" if ly.dtype != ci.F32 else "alu") if flops / nbytes >= ridge else "hbm"
+
+
+def source_digest(path_name):
+    src = os.path.join(ROOT, "cnn_convolution_conv2d_amd", "csrc", KERNEL_SOURCES[path_name])
+    h = hashlib.sha256()
+    for p in (src, os.path.join(ROOT, "cnn_convolution_conv2d_amd", "csrc", "common.hpp")):
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(key, path_name):
+    """HBM bytes per launch from rocprofv3 counters, if taken on this source."""
+    f = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(f):
+        return None
+    entry = json.load(open(f)).get(key)
+    if not entry or entry.get("source_digest") != source_digest(path_name):
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+def host_cpu():
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(cid, li, x, w, b, target_s, unit):
+    """The fp64 oracle on whole images of the workload until target_s elapses."""
+    import oracle
+    ly = ci.layer(cid, li)
+    flops, nbytes = algorithmic(ly)
+    relu = bool(ly.epilogue & ci.EPI_RELU)
+    k = 0
+    t0 = time.perf_counter()
+    while k < ly.N and (k == 0 or time.perf_counter() - t0 < target_s):
+        oracle.conv2d(x[k:k + 1], w, b, ly.stride, ly.pad, ly.dilation, ly.groups, relu=relu,
+                      with_scale=False)
+        k += 1
+    dt = time.perf_counter() - t0
+    frac = k / ly.N
+    value = (flops * frac / dt / 1e12) if unit == "TFLOP/s" else (nbytes * frac / dt / 1e9)
+    return {"value": round(value, 6), "unit": unit, "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"first {k} of {ly.N} images, all {ly.Cout} output channels, fp64 direct "
+                      f"loop ({dt:.1f} s)",
+            "host_cpu": host_cpu()}
+
+
+def bench_layer(cid, li, steps, warmup, cpu_seconds, with_cpu):
+    import torch
+    import cnn_convolution_conv2d_amd as c2
+
+    ly = ci.layer(cid, li)
+    ho, wo = out_hw(ly)
+    dt_lib = c2.F32 if ly.dtype == ci.F32 else c2.BF16
+    tdt = torch.float32 if ly.dtype == ci.F32 else torch.bfloat16
+    esz = 4 if ly.dtype == ci.F32 else 2
+    path = c2.conv2d_select_path(ly.N, ly.Cin, ly.H, ly.W, ly.Cout, ly.Kh, ly.Kw, ly.stride, ly.pad,
+                                 ly.dilation, ly.groups, dt_lib)
+    pname = c2.PATH_NAMES[path]
+    flops, nbytes = algorithmic(ly)
+    bound = bound_of(ly)
+
+    x, w, b = ci.layer_tensors(cid, li)
+    dev = torch.device("cuda", torch.cuda.current_device())
+    stream = torch.cuda.current_stream()
+    # inputs resident in HBM, channels-last, before the timed region
+    x_nchw = torch.from_numpy(x).to(dev).to(tdt)
+    w_dev = torch.from_numpy(w).to(dev).to(tdt)
+    wp = torch.empty(c2.conv2d_packed_weight_bytes(ly.Cout, ly.Cin, ly.Kh, ly.Kw, ly.groups, dt_lib)
+                     // esz, dtype=tdt, device=dev)
+    c2.conv2d_pack_weights(w_dev, wp, ly.Cout, ly.Cin, ly.Kh, ly.Kw, ly.groups, dt_lib)
+    bias = torch.from_numpy(b).to(dev) if b is not None else None
+    set_bytes = esz * (x.size + ly.N * ly.Cout * ho * wo)
+    R = max(1, min(16, math.ceil(ROTATE_BYTES / set_bytes)))
+    x0 = torch.empty((ly.N, ly.H, ly.W, ly.Cin), dtype=tdt, device=dev)
+    c2.conv2d_nchw_to_nhwc(x_nchw, x0, ly.N, ly.Cin, ly.H, ly.W, dt_lib)
+    xs = [x0] + [x0.clone() for _ in range(R - 1)]
+    ys = [torch.empty((ly.N, ho, wo, ly.Cout), dtype=tdt, device=dev) for _ in range(R)]
+    del x_nchw, w_dev
+
+    def step(i):
+        j = i % R
+        c2.conv2d_fwd_nhwc_packed(xs[j], wp, bias, ys[j], ly.N, ly.Cin, ly.H, ly.W, ly.Cout, ly.Kh,
+                                  ly.Kw, ly.stride, ly.pad, ly.dilation, ly.groups, dt_lib,
+                                  ly.epilogue, stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = np.array([a.elapsed_time(e) for a, e in ev])
+    mean_ms = float(launch_ms.mean())
+    ms_per_step = wall * 1e3 / steps
+
+    unit = "TFLOP/s" if bound in ("mfma", "alu") else "GB/s"
+    if unit == "TFLOP/s":
+        value = flops / (ms_per_step * 1e-3) / 1e12
+        achieved = flops / (mean_ms * 1e-3) / 1e12
+        peak = PEAK_FP32_TFLOPS if ly.dtype == ci.F32 else PEAK_BF16_TFLOPS
+    else:
+        value = nbytes / (ms_per_step * 1e-3) / 1e9
+        achieved = nbytes / (mean_ms * 1e-3) / 1e9
+        peak = PEAK_HBM_GBS
+    key = f"cfg{cid}:{ly.name}"
+    traffic = measured_traffic(key, pname)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if ly.dtype == ci.F32 else "bf16",
+        "data": "synthetic (seeded, workload shapes and distributions; no dataset)",
+        "config": {
+            "workload": f"cfg{cid} {ly.name}: N={ly.N} Cin={ly.Cin} {ly.H}x{ly.W} -> Cout={ly.Cout} "
+                        f"{ly.Kh}x{ly.Kw} s{ly.stride} p{ly.pad} d{ly.dilation} g{ly.groups}"
+                        f"{' bias' if ly.epilogue & ci.EPI_BIAS else ''}"
+                        f"{' relu' if ly.epilogue & ci.EPI_RELU else ''}",
+            "layout": "NHWC activations, packed weights", "path": pname,
+            "gflop_per_step": round(flops / 1e9, 4), "algorithmic_mb_per_step": round(nbytes / 1e6, 3),
+            "rotating_buffer_sets": R, "device": torch.cuda.get_device_name(dev),
+        },
+        "roofline": {
+            "bound": bound, "achieved": round(achieved, 3), "peak": peak,
+            "unit": "TFLOP/s" if unit == "TFLOP/s" else "GB/s",
+            "frac": round(achieved / peak, 4), "traffic": traffic,
+            "kernel_mean_us": round(mean_ms * 1e3, 3),
+            "kernel_median_us": round(float(np.median(launch_ms)) * 1e3, 3),
+        },
+    }
+    if with_cpu:
+        line["cpu_baseline"] = cpu_baseline(cid, li, x, w, b, cpu_seconds, unit)
+    return line
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--layer", default="2:0", help="workload layer as CID:LAYER_INDEX")
+    ap.add_argument("--all", action="store_true", help="time every workload layer")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    a = ap.parse_args(argv)
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if a.gpus != 1 or world != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {a.gpus}, WORLD_SIZE "
+              f"{world}); a multi-GPU batch split is described in DESIGN.md but not built.",
+              file=sys.stderr)
+        return 2
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    from cnn_convolution_conv2d_amd import build as b
+    if not os.path.exists(b.OUT):
+        b.build()
+    layers = [(c, i) for c in sorted(ci.WORKLOADS) for i in range(len(ci.WORKLOADS[c].layers))] \
+        if a.all else [tuple(int(v) for v in a.layer.split(":"))]
+    for cid, li in layers:
+        line = bench_layer(cid, li, a.steps, a.warmup, a.cpu_seconds,
+                           with_cpu=not a.no_cpu_baseline)
+        print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

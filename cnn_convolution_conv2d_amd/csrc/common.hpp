@@ -1,0 +1,79 @@
+// common.hpp -- types and small device helpers shared by the conv2d kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace conv2d {
+
+// One convolution call, validated on the host.  All sizes fit int32; element
+// offsets of x and y fit int32 (checked by the dispatcher).
+struct Shape {
+    int N, Cin, H, W, Cout, Kh, Kw;
+    int stride, pad, dil, groups;
+    int Ho, Wo;
+    int cin_g, cout_g;   // channels per group
+    int dtype;           // CONV2D_F32 / CONV2D_BF16
+    int epilogue;        // CONV2D_EPI_* bits
+};
+
+enum Layout { NCHW = 0, NHWC = 1 };
+enum WLayout { W_OIHW = 0, W_PACKED = 1, W_DW = 2 };  // raw, [Cout][Kh][Kw][Cin/G], [Kh][Kw][C]
+
+typedef uint16_t bf16_t;   // raw bf16 bit pattern
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// fp32 -> bf16, round to nearest, ties to even; NaN stays a quiet NaN.
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>(0x7fc0u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<bf16_t>(u >> 16);
+}
+
+// Two fp32 -> two packed bf16 in one 32-bit word (low half = a).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+}
+
+template <typename T> __device__ __forceinline__ float load_f32(const T* p, int i);
+template <> __device__ __forceinline__ float load_f32<float>(const float* p, int i) { return p[i]; }
+template <> __device__ __forceinline__ float load_f32<bf16_t>(const bf16_t* p, int i) { return bf16_to_f32(p[i]); }
+
+template <typename T> __device__ __forceinline__ void store_f32(T* p, int i, float v);
+template <> __device__ __forceinline__ void store_f32<float>(float* p, int i, float v) { p[i] = v; }
+template <> __device__ __forceinline__ void store_f32<bf16_t>(bf16_t* p, int i, float v) { p[i] = f32_to_bf16(v); }
+
+// Epilogue of every kernel: bias after the full sum, then ReLU (the fused
+// bias -> activation -> single store of the "Epilogue Fusion" passage).
+template <bool BIAS, bool RELU>
+__device__ __forceinline__ float epilogue(float acc, const float* bias, int co) {
+    float v = acc;
+    if (BIAS) v += bias[co];
+    if (RELU) v = fmaxf(v, 0.0f);
+    return v;
+}
+
+// Host-side launchers (each defined in its kernel's source file).  They
+// return hipSuccess or the launch error.
+hipError_t launch_direct(const Shape& s, const void* x, int xl, const void* w, int wl,
+                         const float* bias, void* y, int yl, hipStream_t st);
+hipError_t launch_depthwise(const Shape& s, const void* x, const void* w_dw, const float* bias,
+                            void* y, hipStream_t st);
+hipError_t launch_gemm1x1(const Shape& s, const void* x, const void* w_packed, const float* bias,
+                          void* y, hipStream_t st);
+hipError_t launch_igemm(const Shape& s, const void* x, const void* w_packed, const float* bias,
+                        void* y, hipStream_t st);
+bool igemm_supports(const Shape& s);
+bool gemm1x1_supports(const Shape& s);
+bool depthwise_supports(const Shape& s);
+
+hipError_t launch_transpose(const void* src, void* dst, int batch, int rows, int cols,
+                            int elem_bytes, hipStream_t st);
+hipError_t launch_pack_weights(const void* w, void* wp, int Cout, int cin_g, int Kh, int Kw,
+                               int depthwise, int elem_bytes, hipStream_t st);
+
+}  // namespace conv2d

@@ -1,0 +1,332 @@
+// conv2d_api.hip -- C ABI of libconv2d.so: argument validation, output size,
+// path selection, NCHW-entry scratch, and launches on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/conv2d.h"
+#include "common.hpp"
+
+using namespace conv2d;
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int set_error(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+    return set_error(CONV2D_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int g_path_override = CONV2D_PATH_AUTO;
+
+// Output extent: floor((in + 2p - d(k-1) - 1)/s) + 1 (floor division of a
+// possibly negative numerator).
+long long out_extent(long long in, long long k, long long s, long long p, long long d) {
+    long long num = in + 2 * p - d * (k - 1) - 1;
+    long long q = num / s;
+    if (num % s != 0 && num < 0) q -= 1;
+    return q + 1;
+}
+
+int validate(const void* x, const void* w, const float* bias, const void* y,
+             int N, int Cin, int H, int W, int Cout, int Kh, int Kw,
+             int stride, int pad, int dilation, int groups, int dtype, int epilogue,
+             Shape* out) {
+    if (dtype != CONV2D_F32 && dtype != CONV2D_BF16)
+        return set_error(CONV2D_ERR_DTYPE, "unknown dtype %d", dtype);
+    if (epilogue < 0 || (epilogue & ~(CONV2D_EPI_BIAS | CONV2D_EPI_RELU)))
+        return set_error(CONV2D_ERR_EPILOGUE, "unknown epilogue bits 0x%x", epilogue);
+    if (N < 1 || Cin < 1 || H < 1 || W < 1 || Cout < 1 || Kh < 1 || Kw < 1)
+        return set_error(CONV2D_ERR_ARG, "sizes must be >= 1 (N=%d Cin=%d H=%d W=%d Cout=%d Kh=%d Kw=%d)",
+                         N, Cin, H, W, Cout, Kh, Kw);
+    if (stride < 1 || dilation < 1 || pad < 0 || groups < 1)
+        return set_error(CONV2D_ERR_ARG, "need stride>=1, dilation>=1, pad>=0, groups>=1 (got %d %d %d %d)",
+                         stride, dilation, pad, groups);
+    if (Cin % groups || Cout % groups)
+        return set_error(CONV2D_ERR_GROUPS, "Cin=%d and Cout=%d must be divisible by groups=%d", Cin, Cout, groups);
+    if (!x || !w || !y) return set_error(CONV2D_ERR_NULL, "x, w and y must be non-NULL");
+    if ((epilogue & CONV2D_EPI_BIAS) && !bias)
+        return set_error(CONV2D_ERR_NULL, "bias is NULL but the epilogue asks for it");
+    long long Ho = out_extent(H, Kh, stride, pad, dilation);
+    long long Wo = out_extent(W, Kw, stride, pad, dilation);
+    if (Ho < 1 || Wo < 1)
+        return set_error(CONV2D_ERR_EMPTY_OUTPUT, "empty output (Ho=%lld Wo=%lld)", Ho, Wo);
+    long long xe = (long long)N * Cin * H * W;
+    long long ye = (long long)N * Cout * Ho * Wo;
+    long long we = (long long)Cout * (Cin / groups) * Kh * Kw;
+    if (xe >= INT_MAX || ye >= INT_MAX || we >= INT_MAX || (long long)H + 2LL * pad >= INT_MAX / 2)
+        return set_error(CONV2D_ERR_UNSUPPORTED, "tensor too large for 32-bit element offsets");
+    if (out) {
+        Shape s;
+        s.N = N; s.Cin = Cin; s.H = H; s.W = W; s.Cout = Cout; s.Kh = Kh; s.Kw = Kw;
+        s.stride = stride; s.pad = pad; s.dil = dilation; s.groups = groups;
+        s.Ho = (int)Ho; s.Wo = (int)Wo;
+        s.cin_g = Cin / groups; s.cout_g = Cout / groups;
+        s.dtype = dtype; s.epilogue = epilogue;
+        *out = s;
+    }
+    return CONV2D_OK;
+}
+
+bool is_depthwise(const Shape& s) { return s.groups == s.Cin && s.Cout == s.Cin; }
+
+bool path_can_run(int path, const Shape& s) {
+    switch (path) {
+    case CONV2D_PATH_DIRECT: return true;
+    case CONV2D_PATH_DEPTHWISE: return s.dtype == CONV2D_BF16 && is_depthwise(s) && depthwise_supports(s);
+    case CONV2D_PATH_GEMM1X1: return s.dtype == CONV2D_BF16 && gemm1x1_supports(s);
+    case CONV2D_PATH_IGEMM: return s.dtype == CONV2D_BF16 && !is_depthwise(s) && igemm_supports(s);
+    default: return false;
+    }
+}
+
+// Automatic choice (host only): 1x1 -> GEMM; depthwise -> depthwise direct;
+// channel-aligned bf16 -> implicit GEMM; anything else -> direct loop.
+int auto_path(const Shape& s) {
+    if (s.dtype != CONV2D_BF16) return CONV2D_PATH_DIRECT;
+    if (is_depthwise(s)) return depthwise_supports(s) ? CONV2D_PATH_DEPTHWISE : CONV2D_PATH_DIRECT;
+    if (gemm1x1_supports(s)) return CONV2D_PATH_GEMM1X1;
+    if (igemm_supports(s)) return CONV2D_PATH_IGEMM;
+    return CONV2D_PATH_DIRECT;
+}
+
+int choose_path(const Shape& s) {
+    int forced = __atomic_load_n(&g_path_override, __ATOMIC_RELAXED);
+    if (forced == CONV2D_PATH_AUTO) return auto_path(s);
+    if (!path_can_run(forced, s))
+        return set_error(CONV2D_ERR_UNSUPPORTED, "forced path %d cannot run this shape", forced);
+    return forced;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int run_nhwc(int path, const Shape& s, const void* x, const void* wp, const float* bias, void* y,
+             hipStream_t st) {
+    hipError_t e = hipSuccess;
+    if (path != CONV2D_PATH_DIRECT && !(aligned16(x) && aligned16(wp) && aligned16(y)))
+        return set_error(CONV2D_ERR_ALIGN, "x, w_packed and y must be 16-byte aligned for path %d", path);
+    switch (path) {
+    case CONV2D_PATH_DIRECT:
+        e = launch_direct(s, x, NHWC, wp, is_depthwise(s) ? W_DW : W_PACKED, bias, y, NHWC, st);
+        break;
+    case CONV2D_PATH_DEPTHWISE: e = launch_depthwise(s, x, wp, bias, y, st); break;
+    case CONV2D_PATH_GEMM1X1: e = launch_gemm1x1(s, x, wp, bias, y, st); break;
+    case CONV2D_PATH_IGEMM: e = launch_igemm(s, x, wp, bias, y, st); break;
+    default: return set_error(CONV2D_ERR_UNSUPPORTED, "unknown path %d", path);
+    }
+    if (e != hipSuccess) return hip_fail(e, "kernel launch");
+    return CONV2D_OK;
+}
+
+size_t elem_bytes(int dtype) { return dtype == CONV2D_F32 ? 4 : 2; }
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Per-device scratch of the NCHW entry.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+size_t g_scratch_bytes[kMaxDevices] = {};
+
+int get_scratch(size_t bytes, void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return set_error(CONV2D_ERR_UNSUPPORTED, "device id %d", dev);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (g_scratch_bytes[dev] < bytes) {
+        if (g_scratch[dev]) {
+            // Earlier work on any stream may still read the old block.
+            e = hipDeviceSynchronize();
+            if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+            e = hipFree(g_scratch[dev]);
+            g_scratch[dev] = nullptr;
+            g_scratch_bytes[dev] = 0;
+            if (e != hipSuccess) return hip_fail(e, "hipFree");
+        }
+        size_t want = round_up(bytes, size_t(1) << 21);
+        e = hipMalloc(&g_scratch[dev], want);
+        if (e != hipSuccess) {
+            g_scratch[dev] = nullptr;
+            return hip_fail(e, "hipMalloc(scratch)");
+        }
+        g_scratch_bytes[dev] = want;
+    }
+    *out = g_scratch[dev];
+    return CONV2D_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int conv2d_out_dim(int in, int k, int stride, int pad, int dilation) {
+    if (stride < 1 || dilation < 1 || k < 1 || pad < 0 || in < 1) return CONV2D_ERR_ARG;
+    long long r = out_extent(in, k, stride, pad, dilation);
+    if (r > INT_MAX) return CONV2D_ERR_ARG;
+    return r < 0 ? 0 : (int)r;
+}
+
+int conv2d_check_args(const void* x, const void* w, const float* bias, const void* y,
+                      int N, int Cin, int H, int W, int Cout, int Kh, int Kw,
+                      int stride, int pad, int dilation, int groups, int dtype, int epilogue) {
+    return validate(x, w, bias, y, N, Cin, H, W, Cout, Kh, Kw, stride, pad, dilation, groups,
+                    dtype, epilogue, nullptr);
+}
+
+int conv2d_select_path(int N, int Cin, int H, int W, int Cout, int Kh, int Kw,
+                       int stride, int pad, int dilation, int groups, int dtype) {
+    Shape s;
+    static const char dummy[16] = {};
+    int rc = validate(dummy, dummy, nullptr, dummy, N, Cin, H, W, Cout, Kh, Kw, stride, pad,
+                      dilation, groups, dtype, 0, &s);
+    if (rc) return rc;
+    return choose_path(s);
+}
+
+int conv2d_set_path_override(int path) {
+    if (path < CONV2D_PATH_AUTO || path > CONV2D_PATH_IGEMM) return CONV2D_ERR_ARG;
+    return __atomic_exchange_n(&g_path_override, path, __ATOMIC_RELAXED);
+}
+
+size_t conv2d_packed_weight_bytes(int Cout, int Cin, int Kh, int Kw, int groups, int dtype) {
+    if (Cout < 1 || Cin < 1 || Kh < 1 || Kw < 1 || groups < 1 || Cin % groups || Cout % groups)
+        return 0;
+    if (dtype != CONV2D_F32 && dtype != CONV2D_BF16) return 0;
+    return (size_t)Cout * (Cin / groups) * Kh * Kw * elem_bytes(dtype);
+}
+
+int conv2d_pack_weights(const void* w, void* w_packed, int Cout, int Cin, int Kh, int Kw,
+                        int groups, int dtype, hipStream_t stream) {
+    if (dtype != CONV2D_F32 && dtype != CONV2D_BF16) return set_error(CONV2D_ERR_DTYPE, "unknown dtype %d", dtype);
+    if (Cout < 1 || Cin < 1 || Kh < 1 || Kw < 1 || groups < 1)
+        return set_error(CONV2D_ERR_ARG, "sizes must be >= 1");
+    if (Cin % groups || Cout % groups) return set_error(CONV2D_ERR_GROUPS, "channels not divisible by groups");
+    if (!w || !w_packed) return set_error(CONV2D_ERR_NULL, "w and w_packed must be non-NULL");
+    if ((long long)Cout * (Cin / groups) * Kh * Kw >= INT_MAX)
+        return set_error(CONV2D_ERR_UNSUPPORTED, "weight too large");
+    int dw = (groups == Cin && Cout == Cin) ? 1 : 0;
+    hipError_t e = launch_pack_weights(w, w_packed, Cout, Cin / groups, Kh, Kw, dw,
+                                       (int)elem_bytes(dtype), stream);
+    return e == hipSuccess ? CONV2D_OK : hip_fail(e, "pack_weights launch");
+}
+
+static int transpose_args(const void* src, void* dst, int N, int C, int H, int W, int dtype) {
+    if (dtype != CONV2D_F32 && dtype != CONV2D_BF16) return set_error(CONV2D_ERR_DTYPE, "unknown dtype %d", dtype);
+    if (N < 1 || C < 1 || H < 1 || W < 1) return set_error(CONV2D_ERR_ARG, "sizes must be >= 1");
+    if (!src || !dst) return set_error(CONV2D_ERR_NULL, "src and dst must be non-NULL");
+    if ((long long)N * C * H * W >= INT_MAX) return set_error(CONV2D_ERR_UNSUPPORTED, "tensor too large");
+    return CONV2D_OK;
+}
+
+int conv2d_nchw_to_nhwc(const void* src, void* dst, int N, int C, int H, int W, int dtype,
+                        hipStream_t stream) {
+    int rc = transpose_args(src, dst, N, C, H, W, dtype);
+    if (rc) return rc;
+    hipError_t e = launch_transpose(src, dst, N, C, H * W, (int)elem_bytes(dtype), stream);
+    return e == hipSuccess ? CONV2D_OK : hip_fail(e, "nchw_to_nhwc launch");
+}
+
+int conv2d_nhwc_to_nchw(const void* src, void* dst, int N, int C, int H, int W, int dtype,
+                        hipStream_t stream) {
+    int rc = transpose_args(src, dst, N, C, H, W, dtype);
+    if (rc) return rc;
+    hipError_t e = launch_transpose(src, dst, N, H * W, C, (int)elem_bytes(dtype), stream);
+    return e == hipSuccess ? CONV2D_OK : hip_fail(e, "nhwc_to_nchw launch");
+}
+
+int conv2d_fwd_nhwc_packed(const void* x, const void* w_packed, const float* bias, void* y,
+                           int N, int Cin, int H, int W, int Cout, int Kh, int Kw,
+                           int stride, int pad, int dilation, int groups,
+                           int dtype, int epilogue, hipStream_t stream) {
+    Shape s;
+    int rc = validate(x, w_packed, bias, y, N, Cin, H, W, Cout, Kh, Kw, stride, pad, dilation,
+                      groups, dtype, epilogue, &s);
+    if (rc) return rc;
+    int path = choose_path(s);
+    if (path < 0) return path;
+    return run_nhwc(path, s, x, w_packed, bias, y, stream);
+}
+
+int conv2d_fwd(const void* x, const void* w, const float* bias, void* y,
+               int N, int Cin, int H, int W, int Cout, int Kh, int Kw,
+               int stride, int pad, int dilation, int groups,
+               int dtype, int epilogue, hipStream_t stream) {
+    Shape s;
+    int rc = validate(x, w, bias, y, N, Cin, H, W, Cout, Kh, Kw, stride, pad, dilation, groups,
+                      dtype, epilogue, &s);
+    if (rc) return rc;
+    int path = choose_path(s);
+    if (path < 0) return path;
+    if (path == CONV2D_PATH_DIRECT) {
+        // The direct loop reads the pages' layouts as they are: no repack.
+        hipError_t e = launch_direct(s, x, NCHW, w, W_OIHW, bias, y, NCHW, stream);
+        return e == hipSuccess ? CONV2D_OK : hip_fail(e, "direct launch");
+    }
+    const size_t eb = elem_bytes(dtype);
+    const size_t wb = round_up(conv2d_packed_weight_bytes(Cout, Cin, Kh, Kw, groups, dtype), 256);
+    const size_t xb = round_up((size_t)N * Cin * H * W * eb, 256);
+    const size_t yb = round_up((size_t)N * Cout * s.Ho * s.Wo * eb, 256);
+    void* scratch = nullptr;
+    rc = get_scratch(wb + xb + yb, &scratch);
+    if (rc) return rc;
+    char* base = static_cast<char*>(scratch);
+    void* wp = base;
+    void* xn = base + wb;
+    void* yn = base + wb + xb;
+    rc = conv2d_pack_weights(w, wp, Cout, Cin, Kh, Kw, groups, dtype, stream);
+    if (rc) return rc;
+    rc = conv2d_nchw_to_nhwc(x, xn, N, Cin, H, W, dtype, stream);
+    if (rc) return rc;
+    rc = run_nhwc(path, s, xn, wp, bias, yn, stream);
+    if (rc) return rc;
+    return conv2d_nhwc_to_nchw(yn, y, N, Cout, s.Ho, s.Wo, dtype, stream);
+}
+
+void conv2d_release_scratch(void) {
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess) return;
+    for (int d = 0; d < kMaxDevices; ++d) {
+        if (!g_scratch[d]) continue;
+        if (hipSetDevice(d) == hipSuccess) {
+            (void)hipDeviceSynchronize();
+            (void)hipFree(g_scratch[d]);
+        }
+        g_scratch[d] = nullptr;
+        g_scratch_bytes[d] = 0;
+    }
+    (void)hipSetDevice(cur);
+}
+
+const char* conv2d_strerror(int code) {
+    switch (code) {
+    case CONV2D_OK: return "ok";
+    case CONV2D_ERR_ARG: return "invalid size, stride, padding or dilation";
+    case CONV2D_ERR_GROUPS: return "channels not divisible by groups";
+    case CONV2D_ERR_EMPTY_OUTPUT: return "output would be empty";
+    case CONV2D_ERR_UNSUPPORTED: return "unsupported by this path or build";
+    case CONV2D_ERR_HIP: return "HIP runtime error";
+    case CONV2D_ERR_NULL: return "required pointer is NULL";
+    case CONV2D_ERR_DTYPE: return "unknown dtype";
+    case CONV2D_ERR_EPILOGUE: return "unknown epilogue flags";
+    case CONV2D_ERR_ALIGN: return "pointer not 16-byte aligned";
+    default: return "unknown error code";
+    }
+}
+
+const char* conv2d_last_error(void) { return g_last_error; }
+
+}  // extern "C"

@@ -1,0 +1,198 @@
+// depthwise.hip -- depthwise convolution (groups == Cin == Cout), bf16 NHWC.
+//
+// Each channel is filtered by its own Kh x Kw kernel with no sum across
+// channels (lincklin.cn lesson 9, section 23; lpnh.cn section 4.1), so the
+// arithmetic intensity is a few FLOPs per byte and the kernel is bound by HBM
+// bandwidth (lincklin.cn section 24).  No MFMA: the work is a handful of FMAs
+// per loaded value, kept on the vector ALUs.
+//
+// Mapping.  A channels-last output row is W*C contiguous bf16 = W*C/8 16-byte
+// vectors.  Thread v of the row owns vector v: output column wo = v / (C/8)
+// and 8 channels.  Consecutive threads therefore touch consecutive 16-byte
+// chunks of memory, so every load and store of a wave is fully coalesced, and
+// the horizontal neighbours a tap needs (wo +- 1) are the vectors C/8 lanes
+// away, already on their way into L1 for the neighbouring threads.  Each
+// thread walks a strip of TH output rows (vertical input reuse).
+//
+// 3x3 stride-1 dilation-1 (the MobileNet case): the thread keeps the three
+// input rows of its window in registers and loads only the one new row per
+// output row (3 vector loads per output vector instead of 9; adjacent outputs
+// share overlapping windows, lincklin.cn section 18).  Its 9 x 8 filter taps
+// stay in registers for the whole strip (lincklin.cn section 14).
+//
+// Other kernel sizes, strides and dilations: the same mapping, all taps
+// loaded per output (dilated taps at kh*D, kw*D only, never a zero-filled
+// window; lpnh.cn section 4.2).
+#include "common.hpp"
+#include "../../include/conv2d.h"
+
+namespace conv2d {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+struct alignas(16) V8 { uint32_t u[4]; };  // 8 bf16
+
+__device__ __forceinline__ V8 load_v8(const bf16_t* p) {
+    return *reinterpret_cast<const V8*>(p);
+}
+__device__ __forceinline__ V8 zero_v8() { V8 v; v.u[0] = v.u[1] = v.u[2] = v.u[3] = 0; return v; }
+
+__device__ __forceinline__ float lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+__device__ __forceinline__ void fma_v8(float acc[8], const V8& x, const float w[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        acc[2 * i] = fmaf(lo(x.u[i]), w[2 * i], acc[2 * i]);
+        acc[2 * i + 1] = fmaf(hi(x.u[i]), w[2 * i + 1], acc[2 * i + 1]);
+    }
+}
+
+template <bool BIAS, bool RELU>
+__device__ __forceinline__ V8 finish(const float acc[8], const float b[8]) {
+    V8 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float a0 = acc[2 * i], a1 = acc[2 * i + 1];
+        if (BIAS) { a0 += b[2 * i]; a1 += b[2 * i + 1]; }
+        if (RELU) { a0 = fmaxf(a0, 0.0f); a1 = fmaxf(a1, 0.0f); }
+        o.u[i] = pack_bf16x2(a0, a1);
+    }
+    return o;
+}
+
+// 3x3, stride 1, dilation 1, any padding; rolling three-row register window.
+template <int TH, bool BIAS, bool RELU>
+__global__ __launch_bounds__(kThreads) void dw3x3s1_kernel(const bf16_t* __restrict__ x,
+                                                           const bf16_t* __restrict__ w,   // [3][3][C]
+                                                           const float* __restrict__ bias,
+                                                           bf16_t* __restrict__ y, Shape s) {
+    const int CV = s.Cin >> 3;                       // 16-byte vectors per pixel
+    const int v = blockIdx.x * kThreads + threadIdx.x;
+    if (v >= s.Wo * CV) return;
+    const int wo = v / CV;
+    const int c0 = (v - wo * CV) << 3;
+    const int n = blockIdx.z;
+    const int ho0 = blockIdx.y * TH;
+    const int ho1 = min(ho0 + TH, s.Ho);
+
+    float wr[9][8];
+#pragma unroll
+    for (int t = 0; t < 9; ++t) {
+        const V8 wv = load_v8(w + t * s.Cin + c0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { wr[t][2 * i] = lo(wv.u[i]); wr[t][2 * i + 1] = hi(wv.u[i]); }
+    }
+    float br[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) br[i] = BIAS ? bias[c0 + i] : 0.0f;
+
+    // input columns of the window and whether each lies inside the image
+    const int wi0 = wo - s.pad;
+    bool colok[3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) colok[k] = (wi0 + k >= 0) && (wi0 + k < s.W);
+    const bf16_t* xn = x + (size_t)n * s.H * s.W * s.Cin + c0;
+
+    auto load_row = [&](int hi_, V8 r[3]) {
+        const bool rok = (hi_ >= 0) && (hi_ < s.H);
+#pragma unroll
+        for (int k = 0; k < 3; ++k)
+            r[k] = (rok && colok[k]) ? load_v8(xn + (hi_ * s.W + wi0 + k) * s.Cin) : zero_v8();
+    };
+
+    V8 r0[3], r1[3], r2[3];
+    load_row(ho0 - s.pad, r0);
+    load_row(ho0 - s.pad + 1, r1);
+    bf16_t* yrow = y + ((size_t)n * s.Ho * s.Wo + wo) * s.Cout + c0;
+    for (int ho = ho0; ho < ho1; ++ho) {
+        load_row(ho - s.pad + 2, r2);
+        float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            fma_v8(acc, r0[k], wr[k]);
+            fma_v8(acc, r1[k], wr[3 + k]);
+            fma_v8(acc, r2[k], wr[6 + k]);
+        }
+        *reinterpret_cast<V8*>(yrow + (size_t)ho * s.Wo * s.Cout) = finish<BIAS, RELU>(acc, br);
+#pragma unroll
+        for (int k = 0; k < 3; ++k) { r0[k] = r1[k]; r1[k] = r2[k]; }
+    }
+}
+
+// Any Kh, Kw, stride, padding, dilation.
+template <int TH, bool BIAS, bool RELU>
+__global__ __launch_bounds__(kThreads) void dw_generic_kernel(const bf16_t* __restrict__ x,
+                                                              const bf16_t* __restrict__ w,  // [Kh][Kw][C]
+                                                              const float* __restrict__ bias,
+                                                              bf16_t* __restrict__ y, Shape s) {
+    const int CV = s.Cin >> 3;
+    const int v = blockIdx.x * kThreads + threadIdx.x;
+    if (v >= s.Wo * CV) return;
+    const int wo = v / CV;
+    const int c0 = (v - wo * CV) << 3;
+    const int n = blockIdx.z;
+    const int ho0 = blockIdx.y * TH;
+    const int ho1 = min(ho0 + TH, s.Ho);
+    float br[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) br[i] = BIAS ? bias[c0 + i] : 0.0f;
+    const bf16_t* xn = x + (size_t)n * s.H * s.W * s.Cin + c0;
+    for (int ho = ho0; ho < ho1; ++ho) {
+        float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        for (int kh = 0; kh < s.Kh; ++kh) {
+            const int hi_ = ho * s.stride + kh * s.dil - s.pad;
+            if (hi_ < 0 || hi_ >= s.H) continue;
+            for (int kw = 0; kw < s.Kw; ++kw) {
+                const int wi = wo * s.stride + kw * s.dil - s.pad;
+                if (wi < 0 || wi >= s.W) continue;
+                const V8 xv = load_v8(xn + (hi_ * s.W + wi) * s.Cin);
+                const V8 wv = load_v8(w + (kh * s.Kw + kw) * s.Cin + c0);
+                float wf[8];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) { wf[2 * i] = lo(wv.u[i]); wf[2 * i + 1] = hi(wv.u[i]); }
+                fma_v8(acc, xv, wf);
+            }
+        }
+        *reinterpret_cast<V8*>(y + (((size_t)n * s.Ho + ho) * s.Wo + wo) * s.Cout + c0) =
+            finish<BIAS, RELU>(acc, br);
+    }
+}
+
+constexpr int kTH = 8;  // output rows per thread
+
+template <bool BIAS, bool RELU>
+hipError_t launch_epi(const Shape& s, const bf16_t* x, const bf16_t* w, const float* b, bf16_t* y,
+                      hipStream_t st) {
+    const int CV = s.Cin / 8;
+    dim3 grid((s.Wo * CV + kThreads - 1) / kThreads, (s.Ho + kTH - 1) / kTH, s.N);
+    if (s.Kh == 3 && s.Kw == 3 && s.stride == 1 && s.dil == 1)
+        hipLaunchKernelGGL((dw3x3s1_kernel<kTH, BIAS, RELU>), grid, dim3(kThreads), 0, st, x, w, b, y, s);
+    else
+        hipLaunchKernelGGL((dw_generic_kernel<kTH, BIAS, RELU>), grid, dim3(kThreads), 0, st, x, w, b, y, s);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool depthwise_supports(const Shape& s) {
+    // 16-byte channel vectors; the grid's y/z extents within launch limits
+    return s.Cin % 8 == 0 && s.N <= 65535 && (s.Ho + kTH - 1) / kTH <= 65535;
+}
+
+hipError_t launch_depthwise(const Shape& s, const void* x, const void* w_dw, const float* bias,
+                            void* y, hipStream_t st) {
+    (void)hipGetLastError();  // report only this launch's error
+    const bf16_t* xt = static_cast<const bf16_t*>(x);
+    const bf16_t* wt = static_cast<const bf16_t*>(w_dw);
+    bf16_t* yt = static_cast<bf16_t*>(y);
+    const bool b = s.epilogue & CONV2D_EPI_BIAS, r = s.epilogue & CONV2D_EPI_RELU;
+    if (b && r) return launch_epi<true, true>(s, xt, wt, bias, yt, st);
+    if (b) return launch_epi<true, false>(s, xt, wt, bias, yt, st);
+    if (r) return launch_epi<false, true>(s, xt, wt, bias, yt, st);
+    return launch_epi<false, false>(s, xt, wt, bias, yt, st);
+}
+
+}  // namespace conv2d

@@ -1,0 +1,165 @@
+/*
+ * conv2d.h -- C ABI of the gfx950 (MI355X) 2D convolution forward library,
+ * libconv2d.so.
+ *
+ * The operation (page "How a GPU executes NN convolution", lincklin.cn,
+ * sections 1-2, with dilation from its section 28 and groups from
+ * "lpnh.cn/news/2674933" sections 2.2 and 4.3):
+ *
+ *   Y[n,co,ho,wo] = epi( sum_{ci<Cin/G, kh<Kh, kw<Kw}
+ *                        X[n, g*Cin/G + ci, ho*S + kh*D - P, wo*S + kw*D - P]
+ *                        * W[co, ci, kh, kw] )
+ *   g = co / (Cout/G);  taps outside the input read 0 (zero padding,
+ *   lincklin.cn section 26);  epi(v) = [max](v [+ bias[co]]), bias added after
+ *   the full sum and ReLU last (lincklin.cn section 31);
+ *   Ho = floor((H + 2P - D(Kh-1) - 1)/S) + 1, likewise Wo
+ *   (lpnh.cn section 6.2).
+ *
+ * Stride S, padding P and dilation D apply equally to both spatial axes;
+ * Kh and Kw are independent.
+ *
+ * Types.  dtype CONV2D_F32: x, w, y are fp32.  dtype CONV2D_BF16: x, w, y are
+ * bf16 (raw 16-bit patterns), products are accumulated in fp32 and the result
+ * is rounded to bf16 to nearest-even once, after the epilogue.  bias is always
+ * fp32 [Cout].
+ *
+ * Memory.  Every tensor pointer is device memory owned by the caller; the
+ * library never frees or keeps it.  Element counts of x and y must each stay
+ * below 2^31 (32-bit element offsets in the kernels).  The MFMA paths need
+ * x, w and y 16-byte aligned (any hipMalloc / torch allocation is).
+ *
+ * Streams.  Every call that takes a stream only enqueues work on it and
+ * returns; nothing synchronises the host.  Errors of the asynchronous work
+ * surface at the caller's next synchronisation.  Passing 0 means the null
+ * stream.
+ *
+ * Errors.  Arguments are validated on the host before anything is enqueued;
+ * an invalid call returns a negative CONV2D_ERR_* code and touches no memory.
+ * A failed launch returns CONV2D_ERR_HIP.  conv2d_strerror() names a code and
+ * conv2d_last_error() gives the calling thread's last detailed message.
+ */
+#ifndef CONV2D_H
+#define CONV2D_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element types */
+enum { CONV2D_F32 = 0, CONV2D_BF16 = 1 };
+
+/* epilogue flags (bitwise or): bias is added after the sum, ReLU last */
+enum { CONV2D_EPI_NONE = 0, CONV2D_EPI_BIAS = 1, CONV2D_EPI_RELU = 2 };
+
+/* kernel paths (see conv2d_select_path) */
+enum {
+    CONV2D_PATH_AUTO = 0,
+    CONV2D_PATH_DIRECT = 1,     /* direct loop, any shape and dtype             */
+    CONV2D_PATH_DEPTHWISE = 2,  /* bf16, groups == Cin == Cout                  */
+    CONV2D_PATH_GEMM1X1 = 3,    /* bf16, 1x1, stride 1, pad 0, groups 1         */
+    CONV2D_PATH_IGEMM = 4       /* bf16 implicit GEMM on MFMA, Cin/G % 8 == 0   */
+};
+
+/* return codes */
+enum {
+    CONV2D_OK = 0,
+    CONV2D_ERR_ARG = -1,          /* a size, stride, pad or dilation out of range   */
+    CONV2D_ERR_GROUPS = -2,       /* Cin or Cout not divisible by groups            */
+    CONV2D_ERR_EMPTY_OUTPUT = -3, /* Ho or Wo < 1                                   */
+    CONV2D_ERR_UNSUPPORTED = -4,  /* valid convolution this path/build cannot run   */
+    CONV2D_ERR_HIP = -5,          /* a HIP runtime call or launch failed            */
+    CONV2D_ERR_NULL = -6,         /* a required pointer is NULL                     */
+    CONV2D_ERR_DTYPE = -7,        /* unknown dtype                                  */
+    CONV2D_ERR_EPILOGUE = -8,     /* unknown epilogue bits                          */
+    CONV2D_ERR_ALIGN = -9         /* pointer not aligned as the chosen path needs   */
+};
+
+/*
+ * conv2d_fwd -- the forward pass in the pages' own layouts.
+ *   x    [N][Cin][H][W]            (NCHW, lincklin.cn section 1)
+ *   w    [Cout][Cin/G][Kh][Kw]     (lincklin.cn section 1; grouped weight of
+ *                                   lpnh.cn section 4.1)
+ *   bias fp32 [Cout], required iff epilogue has CONV2D_EPI_BIAS (else ignored)
+ *   y    [N][Cout][Ho][Wo]         (NCHW), written completely
+ * fp32 runs the direct kernel on these layouts.  bf16 repacks x to NHWC and
+ * w to the packed layout, runs the chosen kernel and repacks y back to NCHW
+ * (lincklin.cn sections 29-30), using a per-device scratch block that the
+ * library grows on demand with hipMalloc (so this entry may allocate and may
+ * block while it does) and frees in conv2d_release_scratch().  Calls that
+ * share a device share that scratch: issue them on one stream.
+ */
+int conv2d_fwd(const void* x, const void* w, const float* bias, void* y,
+               int N, int Cin, int H, int W, int Cout, int Kh, int Kw,
+               int stride, int pad, int dilation, int groups,
+               int dtype, int epilogue, hipStream_t stream);
+
+/*
+ * conv2d_fwd_nhwc_packed -- the same operation on channels-last data
+ * (lincklin.cn section 29; lnrq.cn section 5.3); allocates nothing.
+ *   x        [N][H][W][Cin]        (NHWC)
+ *   w_packed output of conv2d_pack_weights for the same Cout, Cin, Kh, Kw,
+ *            groups and dtype
+ *   y        [N][Ho][Wo][Cout]     (NHWC), written completely
+ */
+int conv2d_fwd_nhwc_packed(const void* x, const void* w_packed, const float* bias, void* y,
+                           int N, int Cin, int H, int W, int Cout, int Kh, int Kw,
+                           int stride, int pad, int dilation, int groups,
+                           int dtype, int epilogue, hipStream_t stream);
+
+/*
+ * Packed weight layout (the reduction order the NHWC kernels walk: tap
+ * (kh, kw) outer, input channel inner; the row/column order of W_matrix,
+ * lincklin.cn section 7, with K ordered to match channels-last input):
+ *   depthwise (groups == Cin == Cout):  [Kh][Kw][C]
+ *   otherwise:                          [Cout][Kh][Kw][Cin/G]
+ * conv2d_packed_weight_bytes returns its size in bytes (0 on bad arguments).
+ */
+size_t conv2d_packed_weight_bytes(int Cout, int Cin, int Kh, int Kw, int groups, int dtype);
+int conv2d_pack_weights(const void* w, void* w_packed, int Cout, int Cin, int Kh, int Kw,
+                        int groups, int dtype, hipStream_t stream);
+
+/* Activation layout passes (a full read and write of the tensor,
+ * lincklin.cn section 30).  src and dst must not overlap. */
+int conv2d_nchw_to_nhwc(const void* src, void* dst, int N, int C, int H, int W, int dtype,
+                        hipStream_t stream);
+int conv2d_nhwc_to_nchw(const void* src, void* dst, int N, int C, int H, int W, int dtype,
+                        hipStream_t stream);
+
+/* floor((in + 2*pad - dilation*(k-1) - 1)/stride) + 1, or a value <= 0 when
+ * the window does not fit (lpnh.cn section 6.2); CONV2D_ERR_ARG on a bad
+ * stride/dilation/k/pad. Host only. */
+int conv2d_out_dim(int in, int k, int stride, int pad, int dilation);
+
+/* Host-only validation of a conv2d_fwd / conv2d_fwd_nhwc_packed call: returns
+ * CONV2D_OK or the code the call would return.  Needs no GPU. */
+int conv2d_check_args(const void* x, const void* w, const float* bias, const void* y,
+                      int N, int Cin, int H, int W, int Cout, int Kh, int Kw,
+                      int stride, int pad, int dilation, int groups, int dtype, int epilogue);
+
+/* Path the NHWC entry would run for this shape (a CONV2D_PATH_* value > 0), or
+ * a negative error code.  Honours conv2d_set_path_override.  Host only. */
+int conv2d_select_path(int N, int Cin, int H, int W, int Cout, int Kh, int Kw,
+                       int stride, int pad, int dilation, int groups, int dtype);
+
+/* Force a path for both forward entries (CONV2D_PATH_AUTO restores automatic
+ * choice); a forced path that cannot run a shape makes the call return
+ * CONV2D_ERR_UNSUPPORTED.  Process-wide; returns the previous setting, or
+ * CONV2D_ERR_ARG for an unknown path.  Meant for tests and A/B timing. */
+int conv2d_set_path_override(int path);
+
+/* Free the conv2d_fwd scratch of every device (after synchronising them). */
+void conv2d_release_scratch(void);
+
+/* Static text for a return code, and the calling thread's last detailed
+ * error message ("" if none). */
+const char* conv2d_strerror(int code);
+const char* conv2d_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CONV2D_H */

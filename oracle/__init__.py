@@ -58,6 +58,8 @@ def load_library(path: str | None = None):
     lib.oracle_conv2d_points_f64.argtypes = [P, P, P, ctypes.c_int, P, L, P, P] + [L] * 11
     lib.oracle_im2col_f64.restype = ctypes.c_int
     lib.oracle_im2col_f64.argtypes = [P, P] + [L] * 9
+    lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_num_threads.argtypes = []
     _libs[key] = lib
     return lib
 
@@ -77,6 +79,11 @@ def _ptr(a):
 def out_dim(size: int, k: int, stride: int = 1, pad: int = 0, dilation: int = 1, lib=None) -> int:
     """floor((size + 2*pad - dilation*(k-1) - 1)/stride) + 1 (lpnh.cn section 6.2)."""
     return int(_load(lib).oracle_out_dim(size, k, stride, pad, dilation))
+
+
+def num_threads(lib=None) -> int:
+    """OpenMP threads the oracle's loops use."""
+    return int(_load(lib).oracle_num_threads())
 
 
 def effective_kernel(k: int, dilation: int) -> int:

@@ -45,6 +45,10 @@
  */
 #include <stddef.h>
 #include <math.h>
+#include <omp.h>
+
+/* Threads the OpenMP loops below will use (for reporting timings). */
+int oracle_num_threads(void) { return omp_get_max_threads(); }
 
 /* floor division for possibly negative numerators, positive divisor */
 static long floordiv(long a, long b) {

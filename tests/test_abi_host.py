@@ -1,0 +1,137 @@
+"""Host-side tests of the C ABI (no GPU): the library loads, exports every
+symbol the header declares, and validates arguments before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import conv_inputs as ci
+import oracle
+from helpers import ROOT, ensure_built
+
+ensure_built()
+import cnn_convolution_conv2d_amd as c2  # noqa: E402
+
+HEADER = os.path.join(ROOT, "include", "conv2d.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(conv2d_\w+)\s*\(", text)))
+
+
+def test_header_declares_what_binding_lists():
+    assert header_functions() == sorted(c2.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    raw = ctypes.CDLL(c2.LIB_PATH)
+    for name in header_functions():
+        assert hasattr(raw, name), name
+
+
+def test_out_dim_agrees_with_oracle():
+    for n in (1, 2, 3, 5, 7, 56, 64, 112, 224):
+        for k in (1, 2, 3, 5, 7):
+            for s in (1, 2, 3):
+                for p in (0, 1, 2, 3):
+                    for d in (1, 2, 3):
+                        want = oracle.out_dim(n, k, s, p, d)
+                        assert c2.conv2d_out_dim(n, k, s, p, d) == max(want, 0), (n, k, s, p, d)
+    assert c2.conv2d_out_dim(224, 3, 0, 1, 1) == c2.ERR_ARG
+    assert c2.conv2d_out_dim(224, 3, 1, -1, 1) == c2.ERR_ARG
+    assert c2.conv2d_out_dim(224, 3, 1, 1, 0) == c2.ERR_ARG
+
+
+GOOD = dict(N=2, Cin=8, H=9, W=9, Cout=16, Kh=3, Kw=3, stride=1, pad=1, dilation=1, groups=2,
+            dtype=c2.BF16, epilogue=c2.EPI_BIAS | c2.EPI_RELU)
+P = 0x1000  # a non-NULL address; nothing is dereferenced by validation
+
+
+def _check(**over):
+    a = dict(GOOD)
+    a.update(over)
+    ptrs = dict(x=P, w=P, bias=P, y=P)
+    for k in ("x", "w", "bias", "y"):
+        if k in a:
+            ptrs[k] = a.pop(k)
+    return c2.conv2d_check_args(ptrs["x"], ptrs["w"], ptrs["bias"], ptrs["y"], **a)
+
+
+@pytest.mark.parametrize("over,code", [
+    ({}, c2.OK),
+    ({"N": 0}, c2.ERR_ARG), ({"Cin": -1}, c2.ERR_ARG), ({"H": 0}, c2.ERR_ARG),
+    ({"Kh": 0}, c2.ERR_ARG), ({"stride": 0}, c2.ERR_ARG), ({"dilation": 0}, c2.ERR_ARG),
+    ({"pad": -1}, c2.ERR_ARG), ({"groups": 0}, c2.ERR_ARG),
+    ({"groups": 3}, c2.ERR_GROUPS), ({"Cout": 15}, c2.ERR_GROUPS),
+    ({"H": 2, "pad": 0}, c2.ERR_EMPTY_OUTPUT), ({"W": 4, "pad": 0, "dilation": 2}, c2.ERR_EMPTY_OUTPUT),
+    ({"dtype": 7}, c2.ERR_DTYPE), ({"epilogue": 4}, c2.ERR_EPILOGUE), ({"epilogue": -1}, c2.ERR_EPILOGUE),
+    ({"x": None}, c2.ERR_NULL), ({"w": None}, c2.ERR_NULL), ({"y": None}, c2.ERR_NULL),
+    ({"bias": None}, c2.ERR_NULL),
+    ({"bias": None, "epilogue": c2.EPI_RELU}, c2.OK),
+    ({"N": 1 << 20, "Cin": 64, "H": 64, "W": 64, "groups": 1}, c2.ERR_UNSUPPORTED),
+])
+def test_check_args_codes(over, code):
+    assert _check(**over) == code
+
+
+def test_forward_entries_reject_bad_args_before_any_gpu_work():
+    # invalid calls return their code without enqueueing anything, GPU or not
+    for fn in (c2.lib.conv2d_fwd, c2.lib.conv2d_fwd_nhwc_packed):
+        rc = fn(P, P, P, P, 0, 8, 9, 9, 16, 3, 3, 1, 1, 1, 1, c2.BF16, 0, None)
+        assert rc == c2.ERR_ARG
+        rc = fn(P, P, None, P, 1, 8, 9, 9, 16, 3, 3, 1, 1, 1, 1, c2.BF16, c2.EPI_BIAS, None)
+        assert rc == c2.ERR_NULL
+        assert "bias" in c2.last_error()
+    assert c2.lib.conv2d_pack_weights(P, P, 16, 8, 3, 3, 3, c2.BF16, None) == c2.ERR_GROUPS
+    assert c2.lib.conv2d_nchw_to_nhwc(P, None, 1, 8, 9, 9, c2.BF16, None) == c2.ERR_NULL
+    assert c2.lib.conv2d_nhwc_to_nchw(P, P, 1, 8, 9, 9, 5, None) == c2.ERR_DTYPE
+
+
+def test_strerror_names_every_code():
+    seen = set()
+    for code in range(0, -10, -1):
+        s = c2.strerror(code)
+        assert s and s != "unknown error code"
+        seen.add(s)
+    assert len(seen) == 10
+    assert c2.strerror(-100) == "unknown error code"
+
+
+def test_packed_weight_bytes():
+    assert c2.conv2d_packed_weight_bytes(256, 128, 3, 3, 1, c2.BF16) == 256 * 128 * 9 * 2
+    assert c2.conv2d_packed_weight_bytes(256, 256, 3, 3, 4, c2.BF16) == 256 * 64 * 9 * 2
+    assert c2.conv2d_packed_weight_bytes(32, 3, 3, 3, 1, c2.F32) == 32 * 27 * 4
+    assert c2.conv2d_packed_weight_bytes(16, 8, 3, 3, 3, c2.BF16) == 0
+
+
+@pytest.mark.parametrize("cid,li,path", [
+    (1, 0, c2.PATH_DIRECT), (2, 0, c2.PATH_IGEMM), (3, 0, c2.PATH_DEPTHWISE), (3, 1, c2.PATH_GEMM1X1),
+    (4, 0, c2.PATH_IGEMM), (5, 0, c2.PATH_GEMM1X1), (5, 1, c2.PATH_IGEMM), (5, 2, c2.PATH_GEMM1X1),
+    (5, 3, c2.PATH_IGEMM),
+])
+def test_path_selection_for_workloads(cid, li, path):
+    ly = ci.layer(cid, li)
+    dt = c2.F32 if ly.dtype == ci.F32 else c2.BF16
+    assert c2.conv2d_select_path(ly.N, ly.Cin, ly.H, ly.W, ly.Cout, ly.Kh, ly.Kw, ly.stride, ly.pad,
+                                 ly.dilation, ly.groups, dt) == path
+
+
+def test_path_selection_fallbacks_and_override():
+    # channels not a multiple of 8 -> direct loop; depthwise with odd C -> direct
+    assert c2.conv2d_select_path(1, 3, 9, 9, 16, 3, 3, 1, 1, 1, 1, c2.BF16) == c2.PATH_DIRECT
+    assert c2.conv2d_select_path(1, 6, 9, 9, 6, 3, 3, 1, 1, 1, 6, c2.BF16) == c2.PATH_DIRECT
+    # 1x1 with stride 2 is not a plain GEMM -> implicit GEMM
+    assert c2.conv2d_select_path(1, 64, 9, 9, 64, 1, 1, 2, 0, 1, 1, c2.BF16) == c2.PATH_IGEMM
+    prev = c2.conv2d_set_path_override(c2.PATH_DIRECT)
+    try:
+        assert prev == c2.PATH_AUTO
+        assert c2.conv2d_select_path(1, 64, 9, 9, 64, 3, 3, 1, 1, 1, 1, c2.BF16) == c2.PATH_DIRECT
+        c2.conv2d_set_path_override(c2.PATH_GEMM1X1)
+        with pytest.raises(c2.Conv2dError):
+            c2.conv2d_select_path(1, 64, 9, 9, 64, 3, 3, 1, 1, 1, 1, c2.BF16)
+    finally:
+        c2.conv2d_set_path_override(c2.PATH_AUTO)
+    assert c2.lib.conv2d_set_path_override(9) == c2.ERR_ARG

@@ -1,0 +1,322 @@
+"""GPU parity: every kernel path against the fp64 oracle through the C ABI.
+
+Tolerances (written here, applied element by element):
+  fp32  max |y - yref| / (S + |b|) <= 1e-5
+  bf16  |y - yref| <= 1e-2 * S + 1e-3
+  exact-integer mode: x in {-2..2}, w in {-1,0,1}, integer bias; every
+  partial sum is an integer below 2^24, exact in fp32 in any order, so the
+  bf16 output must equal round-to-nearest-even(yref) bit for bit.
+S = sum |x*w| over the valid taps of each output (from the oracle).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import conv_inputs as ci
+import oracle
+from helpers import check_bf16, check_f32, ensure_built, gpu_available, run_nchw, run_nhwc
+
+pytestmark = pytest.mark.gpu
+
+if gpu_available():
+    ensure_built()
+    import torch
+    import cnn_convolution_conv2d_amd as c2
+
+
+def say(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not gpu_available():
+        pytest.skip("no GPU")
+    yield
+    c2.conv2d_set_path_override(c2.PATH_AUTO)
+
+
+def _relu(ly):
+    return bool(ly.epilogue & ci.EPI_RELU)
+
+
+def _ref(x, w, b, ly):
+    return oracle.conv2d(x, w, b, ly.stride, ly.pad, ly.dilation, ly.groups, relu=_relu(ly))
+
+
+def _compare(y, yref, s, b, dtype, what):
+    if dtype == ci.F32:
+        bb = 0.0 if b is None else np.abs(b.astype(np.float64))[None, :, None, None]
+        return check_f32(y, yref, s, bb, what)
+    return check_bf16(y, yref, s, what)
+
+
+# Reduced activation sizes that still span several tiles and end in a
+# ragged tile; channel counts, kernels, strides, groups stay those of the layer.
+SMALL = {(1, 0): dict(N=1), (2, 0): dict(N=2, H=23, W=23), (3, 0): dict(N=2, H=19, W=21),
+         (3, 1): dict(N=2, H=19, W=21), (4, 0): dict(N=2, H=19, W=17), (5, 0): dict(N=2, H=21, W=21),
+         (5, 1): dict(N=2, H=21, W=21), (5, 2): dict(N=2, H=21, W=21), (5, 3): dict(N=2, H=21, W=23)}
+LAYERS = list(SMALL)
+
+
+@pytest.mark.parametrize("cid,li", LAYERS, ids=[f"cfg{c}-{ci.layer(c, l).name}" for c, l in LAYERS])
+def test_layer_small_random(cid, li):
+    ly = ci.layer(cid, li)
+    x, w, b = ci.layer_tensors(cid, li, **SMALL[(cid, li)])
+    say(f"[parity] cfg{cid} {ly.name} random x{x.shape}")
+    y = run_nhwc(x, w, b, ly.stride, ly.pad, ly.dilation, ly.groups, ly.dtype, ly.epilogue)
+    yref, s = _ref(x, w, b, ly)
+    _compare(y, yref, s, b, ly.dtype, f"cfg{cid} {ly.name}")
+
+
+@pytest.mark.parametrize("cid,li", LAYERS, ids=[f"cfg{c}-{ci.layer(c, l).name}" for c, l in LAYERS])
+def test_layer_small_exact_integer(cid, li):
+    ly = ci.layer(cid, li)
+    x, w, b = ci.layer_tensors(cid, li, mode="int", **SMALL[(cid, li)])
+    say(f"[parity] cfg{cid} {ly.name} exact-integer x{x.shape}")
+    y = run_nhwc(x, w, b, ly.stride, ly.pad, ly.dilation, ly.groups, ly.dtype, ly.epilogue)
+    yref, _ = _ref(x, w, b, ly)
+    want = yref if ly.dtype == ci.F32 else oracle.round_to_bf16(yref)
+    np.testing.assert_array_equal(y, want)
+
+
+def _sample_indices(shape, rng, n_random=4096):
+    N, C, Ho, Wo = shape
+    idx = [rng.integers(0, N * C * Ho * Wo, size=n_random)]
+    for _ in range(2):  # the whole border of two output planes (padding taps)
+        n, c = int(rng.integers(0, N)), int(rng.integers(0, C))
+        base = (n * C + c) * Ho * Wo
+        hh, ww = np.meshgrid(np.arange(Ho), np.arange(Wo), indexing="ij")
+        border = (hh == 0) | (ww == 0) | (hh == Ho - 1) | (ww == Wo - 1)
+        idx.append(base + (hh * Wo + ww)[border])
+    idx.append(np.array([0, N * C * Ho * Wo - 1]))
+    return np.concatenate(idx).astype(np.int64)
+
+
+@pytest.mark.parametrize("mode", ["random", "int"])
+@pytest.mark.parametrize("cid,li", LAYERS, ids=[f"cfg{c}-{ci.layer(c, l).name}" for c, l in LAYERS])
+def test_layer_full_size_sampled(cid, li, mode):
+    """Full workload size, the same NHWC entry and launch the benchmark times;
+    outputs sampled (random + whole borders of two planes + first/last)."""
+    ly = ci.layer(cid, li)
+    x, w, b = ci.layer_tensors(cid, li, mode=mode)
+    say(f"[parity] cfg{cid} {ly.name} full {mode} x{x.shape}")
+    yd = run_nhwc(x, w, b, ly.stride, ly.pad, ly.dilation, ly.groups, ly.dtype, ly.epilogue,
+                  return_dev=True)
+    N, Ho, Wo, Cout = yd.shape
+    rng = np.random.default_rng(1000 * cid + li)
+    idx = _sample_indices((N, Cout, Ho, Wo), rng)
+    # flat NCHW index -> NHWC position on the device
+    wo = idx % Wo
+    ho = (idx // Wo) % Ho
+    co = (idx // (Wo * Ho)) % Cout
+    n = idx // (Wo * Ho * Cout)
+    nhwc = torch.from_numpy(((n * Ho + ho) * Wo + wo) * Cout + co).cuda()
+    y = yd.reshape(-1)[nhwc].float().cpu().numpy().astype(np.float64)
+    yref, s = oracle.conv2d_points(x, w, idx, b, ly.stride, ly.pad, ly.dilation, ly.groups,
+                                   relu=_relu(ly))
+    if mode == "int":
+        want = yref if ly.dtype == ci.F32 else oracle.round_to_bf16(yref)
+        np.testing.assert_array_equal(y, want)
+    elif ly.dtype == ci.F32:
+        bb = 0.0 if b is None else np.abs(b[co].astype(np.float64))
+        check_f32(y, yref, s, bb, f"cfg{cid} {ly.name} full")
+    else:
+        check_bf16(y, yref, s, f"cfg{cid} {ly.name} full")
+    assert not torch.isnan(yd.float()).any().item()
+
+
+def test_chained_separable_pair():
+    """Pointwise takes the GPU's own depthwise output (each kernel checked on
+    exactly the input it saw)."""
+    dw, pw = ci.layer(3, 0), ci.layer(3, 1)
+    x, wdw, bdw = ci.layer_tensors(3, 0, N=2, H=23, W=23)
+    _, wpw, bpw = ci.layer_tensors(3, 1)
+    say("[parity] cfg3 chained depthwise -> pointwise")
+    t = run_nhwc(x, wdw, bdw, dw.stride, dw.pad, dw.dilation, dw.groups, dw.dtype, dw.epilogue)
+    tref, ts = _ref(x, wdw, bdw, dw)
+    check_bf16(t, tref, ts, "depthwise")
+    y = run_nhwc(t.astype(np.float32), wpw, bpw, pw.stride, pw.pad, pw.dilation, pw.groups, pw.dtype,
+                 pw.epilogue)
+    yref, s = _ref(t, wpw, bpw, pw)
+    check_bf16(y, yref, s, "pointwise on GPU depthwise output")
+
+
+def test_chained_bottleneck():
+    lys = [ci.layer(5, i) for i in range(3)]
+    x, _, _ = ci.layer_tensors(5, 0, N=2, H=15, W=17)
+    for i, ly in enumerate(lys):
+        _, w, b = ci.layer_tensors(5, i)
+        say(f"[parity] cfg5 chained {ly.name}")
+        y = run_nhwc(x, w, b, ly.stride, ly.pad, ly.dilation, ly.groups, ly.dtype, ly.epilogue)
+        yref, s = _ref(x, w, b, ly)
+        check_bf16(y, yref, s, ly.name)
+        x = y.astype(np.float32)
+
+
+# ------------------------------------------------------------------ path sweep
+
+def _sweep():
+    cases = []
+    # (N, Cin, H, W, Cout, Kh, Kw, S, P, D, G)
+    for S in (1, 2, 3):
+        for P in (0, 1, 2):
+            for D in (1, 2):
+                cases.append((2, 16, 11, 9, 32, 3, 3, S, P, D, 1))
+    cases += [
+        (1, 8, 5, 7, 8, 1, 1, 1, 0, 1, 1), (3, 24, 6, 5, 40, 1, 1, 1, 0, 1, 1),
+        (1, 32, 9, 9, 16, 5, 5, 1, 2, 1, 1), (2, 64, 7, 8, 64, 3, 2, 2, 1, 1, 2),
+        (1, 16, 4, 4, 16, 3, 3, 1, 0, 1, 1), (1, 16, 1, 1, 16, 3, 3, 1, 1, 1, 1),
+        (2, 48, 13, 3, 12, 3, 3, 1, 1, 3, 1), (1, 8, 3, 3, 4, 7, 7, 1, 3, 1, 1),
+        (1, 96, 10, 10, 96, 1, 1, 2, 0, 1, 1), (2, 32, 8, 8, 32, 3, 3, 1, 1, 1, 4),
+        (1, 256, 5, 6, 8, 3, 3, 1, 1, 1, 1), (1, 8, 6, 6, 260, 3, 3, 1, 1, 1, 1),
+    ]
+    return cases
+
+
+DW_CASES = [(2, 16, 11, 9, 3, 3, 1, 1, 1), (1, 32, 7, 8, 3, 3, 2, 1, 1), (2, 8, 9, 9, 5, 5, 1, 2, 1),
+            (1, 24, 10, 7, 3, 3, 1, 2, 2), (1, 16, 1, 1, 3, 3, 1, 1, 1), (1, 8, 6, 5, 3, 3, 1, 0, 1),
+            (2, 144, 9, 13, 3, 3, 1, 1, 1), (1, 40, 8, 8, 1, 1, 1, 0, 1)]
+
+
+@pytest.mark.parametrize("path", ["direct", "igemm", "gemm1x1"])
+@pytest.mark.parametrize("mode", ["random", "int"])
+def test_path_sweep(path, mode):
+    pid = {"direct": c2.PATH_DIRECT, "igemm": c2.PATH_IGEMM, "gemm1x1": c2.PATH_GEMM1X1}[path]
+    ran = 0
+    for k, (N, Cin, H, W, Cout, Kh, Kw, S, P, D, G) in enumerate(_sweep()):
+        if path == "gemm1x1" and not (Kh == Kw == 1 and S == 1 and P == 0 and G == 1):
+            continue
+        if oracle.out_dim(H, Kh, S, P, D) < 1 or oracle.out_dim(W, Kw, S, P, D) < 1:
+            continue
+        c2.conv2d_set_path_override(pid)
+        for epi in (0, 3):
+            x, w, b = ci.random_tensors(100 + k, N, Cin, H, W, Cout, Kh, Kw, G, mode=mode, bias=epi & 1)
+            say(f"[sweep] {path} {mode} case {k} {(N, Cin, H, W, Cout, Kh, Kw, S, P, D, G)} epi {epi}")
+            y = run_nhwc(x, w, b, S, P, D, G, ci.BF16, epi)
+            yref, s = oracle.conv2d(x, w, b, S, P, D, G, relu=bool(epi & 2))
+            if mode == "int":
+                np.testing.assert_array_equal(y, oracle.round_to_bf16(yref))
+            else:
+                check_bf16(y, yref, s, f"{path} case {k}")
+            ran += 1
+    assert ran >= 4
+
+
+@pytest.mark.parametrize("path", ["depthwise", "direct"])
+@pytest.mark.parametrize("mode", ["random", "int"])
+def test_depthwise_sweep(path, mode):
+    c2.conv2d_set_path_override(c2.PATH_DEPTHWISE if path == "depthwise" else c2.PATH_DIRECT)
+    for k, (N, C, H, W, Kh, Kw, S, P, D) in enumerate(DW_CASES):
+        for epi in (0, 1, 3):
+            x, w, b = ci.random_tensors(300 + k, N, C, H, W, C, Kh, Kw, C, mode=mode, bias=epi & 1)
+            say(f"[sweep] {path} {mode} dw case {k} epi {epi}")
+            y = run_nhwc(x, w, b, S, P, D, C, ci.BF16, epi)
+            yref, s = oracle.conv2d(x, w, b, S, P, D, C, relu=bool(epi & 2))
+            if mode == "int":
+                np.testing.assert_array_equal(y, oracle.round_to_bf16(yref))
+            else:
+                check_bf16(y, yref, s, f"dw case {k}")
+
+
+@pytest.mark.parametrize("mode", ["random", "int"])
+def test_direct_fp32_sweep(mode):
+    for k, (N, Cin, H, W, Cout, Kh, Kw, S, P, D, G) in enumerate(_sweep()[:10]):
+        if oracle.out_dim(H, Kh, S, P, D) < 1 or oracle.out_dim(W, Kw, S, P, D) < 1:
+            continue
+        x, w, b = ci.random_tensors(500 + k, N, Cin, H, W, Cout, Kh, Kw, G, dtype=ci.F32, mode=mode)
+        say(f"[sweep] fp32 {mode} case {k}")
+        y = run_nhwc(x, w, b, S, P, D, G, ci.F32, 3)
+        yref, s = oracle.conv2d(x, w, b, S, P, D, G, relu=True)
+        if mode == "int":
+            np.testing.assert_array_equal(y, yref)
+        else:
+            check_f32(y, yref, s, np.abs(b)[None, :, None, None].astype(np.float64), f"fp32 case {k}")
+
+
+# ------------------------------------------------------------------ NCHW entry
+
+@pytest.mark.parametrize("cid,li", [(1, 0), (2, 0), (3, 0), (3, 1), (4, 0), (5, 3)])
+def test_nchw_entry(cid, li):
+    ly = ci.layer(cid, li)
+    x, w, b = ci.layer_tensors(cid, li, **SMALL[(cid, li)])
+    say(f"[parity] NCHW entry cfg{cid} {ly.name}")
+    y = run_nchw(x, w, b, ly.stride, ly.pad, ly.dilation, ly.groups, ly.dtype, ly.epilogue)
+    yref, s = _ref(x, w, b, ly)
+    _compare(y, yref, s, b, ly.dtype, f"NCHW cfg{cid} {ly.name}")
+
+
+def test_nchw_entry_full_first_layer():
+    """The fp32 first layer at its full stated size, NCHW in and out."""
+    ly = ci.layer(1, 0)
+    x, w, b = ci.layer_tensors(1, 0)
+    say("[parity] NCHW entry cfg1 full")
+    y = run_nchw(x, w, b, ly.stride, ly.pad, ly.dilation, ly.groups, ly.dtype, ly.epilogue)
+    yref, s = _ref(x, w, b, ly)
+    assert y.shape == (1, 32, 112, 112)
+    check_f32(y, yref, s, np.abs(b)[None, :, None, None].astype(np.float64), "cfg1 full NCHW")
+
+
+# ------------------------------------------------------------------ repacks
+
+@pytest.mark.parametrize("dtype", [ci.F32, ci.BF16])
+@pytest.mark.parametrize("shape", [(2, 3, 5, 7), (1, 144, 56, 56), (3, 65, 1, 130), (1, 1, 1, 1)])
+def test_layout_repack_roundtrip(dtype, shape):
+    from helpers import lib_dtype, to_dev
+    rng = np.random.default_rng(1)
+    a = ci.to_storage(rng.standard_normal(shape), dtype)
+    N, C, H, W = shape
+    say(f"[repack] {dtype} {shape}")
+    src = to_dev(a, dtype)
+    mid = torch.empty_like(src)
+    back = torch.empty_like(src)
+    c2.conv2d_nchw_to_nhwc(src, mid, N, C, H, W, lib_dtype(dtype))
+    c2.conv2d_nhwc_to_nchw(mid, back, N, C, H, W, lib_dtype(dtype))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(mid.float().cpu().numpy().reshape(N, H, W, C), ci.nchw_to_nhwc(a))
+    np.testing.assert_array_equal(back.float().cpu().numpy(), a)
+
+
+def test_weight_pack_layouts():
+    from helpers import pack_weights, to_dev
+    rng = np.random.default_rng(2)
+    w = ci.to_storage(rng.standard_normal((12, 4, 3, 2)), ci.BF16)
+    wp = pack_weights(to_dev(w, ci.BF16), 12, 8, 3, 2, 2, ci.BF16).float().cpu().numpy()
+    np.testing.assert_array_equal(wp.reshape(12, 3, 2, 4), w.transpose(0, 2, 3, 1))
+    wd = ci.to_storage(rng.standard_normal((16, 1, 3, 3)), ci.BF16)
+    wdp = pack_weights(to_dev(wd, ci.BF16), 16, 16, 3, 3, 16, ci.BF16).float().cpu().numpy()
+    np.testing.assert_array_equal(wdp.reshape(3, 3, 16), wd[:, 0].transpose(1, 2, 0))
+
+
+# ------------------------------------------------------------------ errors on GPU
+
+def test_forced_path_that_cannot_run_is_an_error():
+    x, w, b = ci.random_tensors(1, 1, 16, 8, 8, 16, 3, 3)
+    c2.conv2d_set_path_override(c2.PATH_GEMM1X1)
+    with pytest.raises(c2.Conv2dError) as e:
+        run_nhwc(x, w, b, 1, 1, 1, 1, ci.BF16, 1)
+    assert e.value.code == c2.ERR_UNSUPPORTED
+
+
+def test_misaligned_pointer_is_rejected():
+    from helpers import to_dev
+    x, w, b = ci.random_tensors(1, 1, 16, 8, 8, 16, 3, 3)
+    xd = to_dev(np.concatenate([np.zeros(1, np.float32), ci.nchw_to_nhwc(x).reshape(-1)]), ci.BF16)
+    wd = to_dev(w.transpose(0, 2, 3, 1), ci.BF16)
+    yd = torch.empty(1 * 8 * 8 * 16, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(c2.Conv2dError) as e:
+        c2.conv2d_fwd_nhwc_packed(xd.data_ptr() + 2, wd, None, yd, 1, 16, 8, 8, 16, 3, 3, 1, 1, 1, 1,
+                                  c2.BF16, 0)
+    assert e.value.code == c2.ERR_ALIGN
+
+
+def test_single_hip_runtime_in_process():
+    """libconv2d.so and torch must share one HIP runtime (torch bundles its own
+    under the same soname); two runtimes would not share devices or pointers."""
+    libs = set()
+    for ln in open("/proc/self/maps"):
+        if "libamdhip64" in ln:
+            libs.add(ln.split()[-1])
+    assert len(libs) == 1, libs
+    assert any("libconv2d.so" in ln for ln in open("/proc/self/maps"))
