@@ -53,7 +53,7 @@ PEAK_HBM_GBS = 8000.0
 ROTATE_BYTES = 512 << 20
 METRIC = "conv2d fwd TFLOP/s (GB/s for depthwise) and % of MI355X roofline, 1 GPU"
 KERNEL_SOURCES = {"direct": "direct.hip", "depthwise": "depthwise.hip", "gemm1x1": "igemm.hip",
-                  "igemm": "igemm.hip"}
+                  "igemm_gather": "igemm.hip", "igemm_halo": "igemm_halo.hip"}
 
 
 def out_hw(ly):

@@ -14,13 +14,15 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libconv2d.so")
+# CONV2D_LIBRARY may name another build of the same sources (tuning sweeps).
+LIB_PATH = os.environ.get("CONV2D_LIBRARY") or os.path.join(_HERE, "libconv2d.so")
 
 F32, BF16 = 0, 1
 EPI_NONE, EPI_BIAS, EPI_RELU = 0, 1, 2
 PATH_AUTO, PATH_DIRECT, PATH_DEPTHWISE, PATH_GEMM1X1, PATH_IGEMM = 0, 1, 2, 3, 4
+PATH_IGEMM_GATHER, PATH_IGEMM_HALO = 5, 6
 PATH_NAMES = {PATH_DIRECT: "direct", PATH_DEPTHWISE: "depthwise", PATH_GEMM1X1: "gemm1x1",
-              PATH_IGEMM: "igemm"}
+              PATH_IGEMM: "igemm", PATH_IGEMM_GATHER: "igemm_gather", PATH_IGEMM_HALO: "igemm_halo"}
 
 OK = 0
 ERR_ARG, ERR_GROUPS, ERR_EMPTY_OUTPUT, ERR_UNSUPPORTED, ERR_HIP = -1, -2, -3, -4, -5

@@ -26,17 +26,17 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t b) {
     return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// fp32 -> bf16, round to nearest, ties to even; NaN stays a quiet NaN.
+// fp32 -> bf16, round to nearest, ties to even (v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>(0x7fc0u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return static_cast<bf16_t>(u >> 16);
+    return __builtin_bit_cast(bf16_t, static_cast<__bf16>(f));
 }
 
-// Two fp32 -> two packed bf16 in one 32-bit word (low half = a).
+// Two fp32 -> two packed bf16 in one 32-bit word (low half = a), one
+// v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-    return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 template <typename T> __device__ __forceinline__ float load_f32(const T* p, int i);
@@ -67,7 +67,10 @@ hipError_t launch_gemm1x1(const Shape& s, const void* x, const void* w_packed, c
                           void* y, hipStream_t st);
 hipError_t launch_igemm(const Shape& s, const void* x, const void* w_packed, const float* bias,
                         void* y, hipStream_t st);
+hipError_t launch_igemm_halo(const Shape& s, const void* x, const void* w_packed, const float* bias,
+                             void* y, hipStream_t st);
 bool igemm_supports(const Shape& s);
+bool igemm_halo_supports(const Shape& s);
 bool gemm1x1_supports(const Shape& s);
 bool depthwise_supports(const Shape& s);
 

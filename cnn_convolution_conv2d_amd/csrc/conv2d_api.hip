@@ -87,9 +87,17 @@ bool path_can_run(int path, const Shape& s) {
     case CONV2D_PATH_DIRECT: return true;
     case CONV2D_PATH_DEPTHWISE: return s.dtype == CONV2D_BF16 && is_depthwise(s) && depthwise_supports(s);
     case CONV2D_PATH_GEMM1X1: return s.dtype == CONV2D_BF16 && gemm1x1_supports(s);
-    case CONV2D_PATH_IGEMM: return s.dtype == CONV2D_BF16 && !is_depthwise(s) && igemm_supports(s);
+    case CONV2D_PATH_IGEMM:
+    case CONV2D_PATH_IGEMM_GATHER: return s.dtype == CONV2D_BF16 && !is_depthwise(s) && igemm_supports(s);
+    case CONV2D_PATH_IGEMM_HALO: return s.dtype == CONV2D_BF16 && !is_depthwise(s) && igemm_halo_supports(s);
     default: return false;
     }
+}
+
+// Implicit-GEMM variant: the halo-tile kernel where it applies (stride 1,
+// small filter span, enough output channels), else the per-tap gather.
+int igemm_variant(const Shape& s) {
+    return igemm_halo_supports(s) ? CONV2D_PATH_IGEMM_HALO : CONV2D_PATH_IGEMM_GATHER;
 }
 
 // Automatic choice (host only): 1x1 -> GEMM; depthwise -> depthwise direct;
@@ -98,7 +106,7 @@ int auto_path(const Shape& s) {
     if (s.dtype != CONV2D_BF16) return CONV2D_PATH_DIRECT;
     if (is_depthwise(s)) return depthwise_supports(s) ? CONV2D_PATH_DEPTHWISE : CONV2D_PATH_DIRECT;
     if (gemm1x1_supports(s)) return CONV2D_PATH_GEMM1X1;
-    if (igemm_supports(s)) return CONV2D_PATH_IGEMM;
+    if (igemm_supports(s)) return igemm_variant(s);
     return CONV2D_PATH_DIRECT;
 }
 
@@ -107,7 +115,7 @@ int choose_path(const Shape& s) {
     if (forced == CONV2D_PATH_AUTO) return auto_path(s);
     if (!path_can_run(forced, s))
         return set_error(CONV2D_ERR_UNSUPPORTED, "forced path %d cannot run this shape", forced);
-    return forced;
+    return forced == CONV2D_PATH_IGEMM ? igemm_variant(s) : forced;
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -123,7 +131,8 @@ int run_nhwc(int path, const Shape& s, const void* x, const void* wp, const floa
         break;
     case CONV2D_PATH_DEPTHWISE: e = launch_depthwise(s, x, wp, bias, y, st); break;
     case CONV2D_PATH_GEMM1X1: e = launch_gemm1x1(s, x, wp, bias, y, st); break;
-    case CONV2D_PATH_IGEMM: e = launch_igemm(s, x, wp, bias, y, st); break;
+    case CONV2D_PATH_IGEMM_GATHER: e = launch_igemm(s, x, wp, bias, y, st); break;
+    case CONV2D_PATH_IGEMM_HALO: e = launch_igemm_halo(s, x, wp, bias, y, st); break;
     default: return set_error(CONV2D_ERR_UNSUPPORTED, "unknown path %d", path);
     }
     if (e != hipSuccess) return hip_fail(e, "kernel launch");
@@ -197,7 +206,7 @@ int conv2d_select_path(int N, int Cin, int H, int W, int Cout, int Kh, int Kw,
 }
 
 int conv2d_set_path_override(int path) {
-    if (path < CONV2D_PATH_AUTO || path > CONV2D_PATH_IGEMM) return CONV2D_ERR_ARG;
+    if (path < CONV2D_PATH_AUTO || path > CONV2D_PATH_IGEMM_HALO) return CONV2D_ERR_ARG;
     return __atomic_exchange_n(&g_path_override, path, __ATOMIC_RELAXED);
 }
 

@@ -63,7 +63,19 @@ __device__ __forceinline__ V8 finish(const float acc[8], const float b[8]) {
     return o;
 }
 
+// Raw buffer loads: an offset beyond the tensor returns zero, so padding taps
+// and rows outside the image cost no branch.
+constexpr int kOOB = 0x7ffffff0;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ V8 load_v8(__amdgpu_buffer_rsrc_t r, int byte_off) {
+    return __builtin_bit_cast(V8, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+
 // 3x3, stride 1, dilation 1, any padding; rolling three-row register window.
+// The next input row is requested before the current output row is computed,
+// so one row of loads is always in flight behind the arithmetic.
 template <int TH, bool BIAS, bool RELU>
 __global__ __launch_bounds__(kThreads) void dw3x3s1_kernel(const bf16_t* __restrict__ x,
                                                            const bf16_t* __restrict__ w,   // [3][3][C]
@@ -89,26 +101,32 @@ __global__ __launch_bounds__(kThreads) void dw3x3s1_kernel(const bf16_t* __restr
 #pragma unroll
     for (int i = 0; i < 8; ++i) br[i] = BIAS ? bias[c0 + i] : 0.0f;
 
-    // input columns of the window and whether each lies inside the image
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)s.N * s.H * s.W * s.Cin * 2u);
+    // byte offsets of the window's three input columns in row 0 of image n;
+    // a column outside the image gets an offset past the end (reads 0)
     const int wi0 = wo - s.pad;
-    bool colok[3];
+    const int img = n * s.H * s.W * s.Cin + c0;
+    int coff[3];
 #pragma unroll
-    for (int k = 0; k < 3; ++k) colok[k] = (wi0 + k >= 0) && (wi0 + k < s.W);
-    const bf16_t* xn = x + (size_t)n * s.H * s.W * s.Cin + c0;
+    for (int k = 0; k < 3; ++k)
+        coff[k] = ((unsigned)(wi0 + k) < (unsigned)s.W) ? (img + (wi0 + k) * s.Cin) * 2 : kOOB;
+    const int rstride = s.W * s.Cin * 2;
 
-    auto load_row = [&](int hi_, V8 r[3]) {
-        const bool rok = (hi_ >= 0) && (hi_ < s.H);
-#pragma unroll
-        for (int k = 0; k < 3; ++k)
-            r[k] = (rok && colok[k]) ? load_v8(xn + (hi_ * s.W + wi0 + k) * s.Cin) : zero_v8();
+    auto row_off = [&](int hi_, int k) {
+        return ((unsigned)hi_ < (unsigned)s.H && coff[k] != kOOB) ? coff[k] + hi_ * rstride : kOOB;
     };
 
-    V8 r0[3], r1[3], r2[3];
-    load_row(ho0 - s.pad, r0);
-    load_row(ho0 - s.pad + 1, r1);
+    V8 r0[3], r1[3], r2[3], rn[3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        r0[k] = load_v8(xr, row_off(ho0 - s.pad, k));
+        r1[k] = load_v8(xr, row_off(ho0 - s.pad + 1, k));
+        r2[k] = load_v8(xr, row_off(ho0 - s.pad + 2, k));
+    }
     bf16_t* yrow = y + ((size_t)n * s.Ho * s.Wo + wo) * s.Cout + c0;
     for (int ho = ho0; ho < ho1; ++ho) {
-        load_row(ho - s.pad + 2, r2);
+#pragma unroll
+        for (int k = 0; k < 3; ++k) rn[k] = load_v8(xr, row_off(ho - s.pad + 3, k));
         float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
         for (int k = 0; k < 3; ++k) {
@@ -118,7 +136,7 @@ __global__ __launch_bounds__(kThreads) void dw3x3s1_kernel(const bf16_t* __restr
         }
         *reinterpret_cast<V8*>(yrow + (size_t)ho * s.Wo * s.Cout) = finish<BIAS, RELU>(acc, br);
 #pragma unroll
-        for (int k = 0; k < 3; ++k) { r0[k] = r1[k]; r1[k] = r2[k]; }
+        for (int k = 0; k < 3; ++k) { r0[k] = r1[k]; r1[k] = r2[k]; r2[k] = rn[k]; }
     }
 }
 
@@ -161,7 +179,10 @@ __global__ __launch_bounds__(kThreads) void dw_generic_kernel(const bf16_t* __re
     }
 }
 
-constexpr int kTH = 8;  // output rows per thread
+#ifndef DW_ROWS_PER_THREAD
+#define DW_ROWS_PER_THREAD 8
+#endif
+constexpr int kTH = DW_ROWS_PER_THREAD;  // output rows per thread
 
 template <bool BIAS, bool RELU>
 hipError_t launch_epi(const Shape& s, const bf16_t* x, const bf16_t* w, const float* b, bf16_t* y,

@@ -21,7 +21,7 @@
 // stages the BM x 32 weight slice and the BN x 32 im2col slice in LDS
 // (double-buffered: the next step's global loads are in flight while the
 // current step runs on the matrix cores), and each wave runs
-// v_mfma_f32_16x16x32_bf16 on its (BM/WGM) x (BN/WGN) sub-tile.  fp32
+// v_mfma_f32_32x32x16_bf16 on its (BM/WGM) x (BN/WGN) sub-tile.  fp32
 // accumulators stay in registers for the whole K loop (output stationary,
 // lincklin.cn section 15) and the epilogue adds the bias, applies ReLU,
 // rounds to bf16 and stores once (lincklin.cn section 31).
@@ -29,200 +29,266 @@
 // 1x1 / stride 1 / pad 0 / groups 1 (lincklin.cn sections 21-22; lpnh.cn
 // section 4.3): B[k][p] = X[p][k], the NHWC activation read as a row-major
 // [N*H*W][Cin] matrix -- a plain GEMM with no window arithmetic.
-#include "common.hpp"
+#include "mfma.hpp"
 #include "../../include/conv2d.h"
 
 namespace conv2d {
 
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+// Tile shapes (BM output channels, BN pixels, WGM x WGN waves, BK channels
+// per K-step) per range of
+// output channels per group; overridable at build time for tuning sweeps.
+#ifndef IGEMM_TILE_M256
+#define IGEMM_TILE_M256 128, 128, 2, 2, 64
+#endif
+#ifndef IGEMM_TILE_M128
+#define IGEMM_TILE_M128 128, 128, 2, 2, 64
+#endif
+#ifndef IGEMM_TILE_M64
+#define IGEMM_TILE_M64 64, 256, 1, 4, 64
+#endif
+#ifndef IGEMM_TILE_M32
+#define IGEMM_TILE_M32 32, 256, 1, 4, 32
+#endif
 
 constexpr int kThreads = 256;
-constexpr int kBK = 32;           // K per step (one MFMA K)
-constexpr int kChunks = kBK / 8;  // 16-byte chunks per LDS row
 
-// LDS rows are 64 bytes (32 bf16).  The 16-byte chunk index is XOR-swizzled
-// with the row so that the 16 rows one MFMA operand read touches spread over
-// all banks.
-__device__ __forceinline__ int swz(int row, int chunk) { return row * kChunks + (chunk ^ ((row >> 1) & 3)); }
-
-template <int BM, int BN, int WGM, int WGN, bool IS1X1, bool BIAS, bool RELU>
+template <int BM, int BN, int WGM, int WGN, int BK, bool IS1X1, bool BIAS, bool RELU>
 __global__ __launch_bounds__(kThreads) void igemm_kernel(const bf16_t* __restrict__ x,
                                                          const bf16_t* __restrict__ wp,
                                                          const float* __restrict__ bias,
                                                          bf16_t* __restrict__ y, Shape s,
                                                          int n_ptiles, int n_ctiles) {
+    static_assert(BK == 32 || BK == 64, "K step of 32 or 64 channels");
+    constexpr int kChunks = BK / 8;                // 16-byte chunks per LDS row
+    constexpr int KS = BK / 16;                    // MFMA K slices per step
     constexpr int WTM = BM / WGM, WTN = BN / WGN;  // wave tile
-    constexpr int TM = WTM / 16, TN = WTN / 16;    // MFMA tiles per wave
+    constexpr int TM = WTM / 32, TN = WTN / 32;    // 32x32 MFMA tiles per wave
     constexpr int AQ = BM * kChunks, BQ = BN * kChunks;  // 16-byte vectors per step
     constexpr int AV = (AQ + kThreads - 1) / kThreads, BV = BQ / kThreads;
     static_assert(BQ % kThreads == 0, "B tile must split evenly");
-    __shared__ uint4 lds[2][(BM + BN) * kChunks];
+    constexpr int STAGE = (BM + BN) * kChunks;            // 16-byte units per stage
+    constexpr int ERS = BM * 2 + 16;                       // epilogue LDS row stride (bytes)
+    constexpr int LDS_UNITS = (2 * STAGE > BN * ERS / 16) ? 2 * STAGE : BN * ERS / 16;
+    __shared__ uint4 lds_raw[LDS_UNITS];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WGN, wn = wave % WGN;
 
-    int bid = blockIdx.x;
-    const int pt = bid % n_ptiles;
-    bid /= n_ptiles;
-    const int ct = bid % n_ctiles;
-    const int g = bid / n_ctiles;
+    int tile = xcd_tile_index();
+    const int ct = tile % n_ctiles;          // output-channel tile (fastest)
+    tile /= n_ctiles;
+    const int g = tile % s.groups;           // group
+    const int pt = tile / s.groups;          // pixel tile (slowest)
 
     const int npix = s.N * s.Ho * s.Wo;
     const int KK = s.Kh * s.Kw;
-    const int nchunk = (s.cin_g + kBK - 1) / kBK;
+    const int nchunk = (s.cin_g + BK - 1) / BK;
     const int nsteps = KK * nchunk;
     const int co_tile = ct * BM;
 
-    // ---- per-thread A (weight) load slots
-    const bf16_t* a_src[AV];
-    bool a_ok[AV];
-    int a_lds[AV], a_c[AV];
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)s.N * s.H * s.W * s.Cin * 2u);
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(wp, (uint32_t)s.Cout * KK * s.cin_g * 2u);
+
+    // ---- per-thread A (weight) slots: byte offset of the row's K start
+    int a_off[AV], a_c[AV], a_lds[AV];
 #pragma unroll
     for (int i = 0; i < AV; ++i) {
         const int q = tid + i * kThreads;
         const int row = q / kChunks, ch = q % kChunks;
         const int co = co_tile + row;
-        a_ok[i] = (q < AQ) && (co < s.cout_g);
-        a_src[i] = wp + (size_t)(g * s.cout_g + (a_ok[i] ? co : 0)) * KK * s.cin_g + ch * 8;
-        a_c[i] = ch * 8;
-        a_lds[i] = swz(row, ch);
+        const bool ok = (q < AQ) && (co < s.cout_g);
+        a_off[i] = ok ? ((g * s.cout_g + co) * KK * s.cin_g + ch * 8) * 2 : kOOB;
+        a_c[i] = ok ? ch * 8 : (1 << 29);   // channel of the chunk (huge: never valid)
+        a_lds[i] = (q < AQ) ? swz<BK>(row, ch) : 0;
     }
-    // ---- per-thread B (im2col) load slots
-    int b_base[BV], b_hb[BV], b_wb[BV], b_lds[BV], b_c[BV];
-    bool b_ok[BV];
+    // ---- per-thread B (im2col) slots
+    int b_base[BV], b_hb[BV], b_wb[BV], b_c[BV], b_lds[BV];
 #pragma unroll
     for (int i = 0; i < BV; ++i) {
         const int q = tid + i * kThreads;
         const int prow = q / kChunks, ch = q % kChunks;
         const int p = pt * BN + prow;
-        b_ok[i] = p < npix;
-        const int pp = b_ok[i] ? p : 0;
+        const bool ok = p < npix;
+        const int pp = ok ? p : 0;
         const int wo = pp % s.Wo;
         const int t = pp / s.Wo;
         const int ho = t % s.Ho;
         const int n = t / s.Ho;
         if (IS1X1) {
             b_base[i] = pp * s.Cin + ch * 8;
-            b_hb[i] = b_wb[i] = 0;
+            b_hb[i] = 0;
+            b_wb[i] = 0;
         } else {
             b_base[i] = n * s.H * s.W * s.Cin + g * s.cin_g + ch * 8;
-            b_hb[i] = ho * s.stride - s.pad;
+            b_hb[i] = ok ? ho * s.stride - s.pad : -(1 << 29);  // never inside the image
             b_wb[i] = wo * s.stride - s.pad;
         }
-        b_c[i] = ch * 8;
-        b_lds[i] = (BM + prow) * kChunks + (ch ^ ((prow >> 1) & 3));
+        b_c[i] = ok ? ch * 8 : (1 << 29);
+        b_lds[i] = swz<BK>(BM + prow, ch);
     }
 
-    uint4 ra[AV], rb[BV];
-    const uint4 z4 = make_uint4(0, 0, 0, 0);
-
-    // global -> registers for step (tap, c0)
-    auto load_step = [&](int tap, int kh, int kw, int c0) {
-#pragma unroll
-        for (int i = 0; i < AV; ++i) {
-            const bool ok = a_ok[i] && (c0 + a_c[i] < s.cin_g);
-            ra[i] = ok ? *reinterpret_cast<const uint4*>(a_src[i] + tap * s.cin_g + c0) : z4;
-        }
-#pragma unroll
-        for (int i = 0; i < BV; ++i) {
-            bool ok = b_ok[i] && (c0 + b_c[i] < s.cin_g);
-            int off;
-            if (IS1X1) {
-                off = b_base[i] + c0;
-            } else {
-                const int hi = b_hb[i] + kh * s.dil;
-                const int wi = b_wb[i] + kw * s.dil;
-                ok = ok && hi >= 0 && hi < s.H && wi >= 0 && wi < s.W;
-                off = b_base[i] + (hi * s.W + wi) * s.Cin + c0;
-            }
-            rb[i] = ok ? *reinterpret_cast<const uint4*>(x + off) : z4;
-        }
-    };
-    auto store_step = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < AV; ++i)
-            if (tid + i * kThreads < AQ) lds[buf][a_lds[i]] = ra[i];
-#pragma unroll
-        for (int i = 0; i < BV; ++i) lds[buf][b_lds[i]] = rb[i];
-    };
-
-    f32x4 acc[TM][TN];
+    f32x16 acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
 
-    // step counters: tap (kh, kw) outer, channel chunk inner
-    int tap = 0, kh = 0, kw = 0, c0 = 0;
-    load_step(tap, kh, kw, c0);
-    store_step(0);
-    __syncthreads();
+    // Load cursor: the next K-step to fetch, tap (kh, kw) outer, channel chunk
+    // inner.
+    int ltap = 0, lkh = 0, lkw = 0, lc0 = 0;
 
-    const int frow = lane & 15, fch = lane >> 4;
-    for (int st = 0; st < nsteps; ++st) {
-        const int buf = st & 1;
-        const bool more = st + 1 < nsteps;
-        if (more) {
-            c0 += kBK;
-            if (c0 >= s.cin_g) {
-                c0 = 0;
-                ++tap;
-                if (++kw == s.Kw) { kw = 0; ++kh; }
-            }
-            load_step(tap, kh, kw, c0);
-        }
-        bf16x8 af[TM], bfr[TN];
+    // global -> registers for the cursor's K-step, then advance the cursor;
+    // out-of-range reads give 0
+#define IGEMM_LOAD_STEP(RA, RB)                                                             \
+    do {                                                                                    \
+        _Pragma("unroll") for (int i = 0; i < AV; ++i) {                                    \
+            const bool ok = lc0 + a_c[i] < s.cin_g && ltap < KK;                            \
+            RA[i] = load16(wr, ok ? a_off[i] + (ltap * s.cin_g + lc0) * 2 : kOOB);          \
+        }                                                                                   \
+        _Pragma("unroll") for (int i = 0; i < BV; ++i) {                                    \
+            int off;                                                                        \
+            bool ok = lc0 + b_c[i] < s.cin_g && ltap < KK;                                  \
+            if (IS1X1) {                                                                    \
+                off = b_base[i] + lc0;                                                      \
+            } else {                                                                        \
+                const int hi = b_hb[i] + lkh * s.dil;                                       \
+                const int wi = b_wb[i] + lkw * s.dil;                                       \
+                ok = ok && (unsigned)hi < (unsigned)s.H && (unsigned)wi < (unsigned)s.W;    \
+                off = b_base[i] + (hi * s.W + wi) * s.Cin + lc0;                            \
+            }                                                                               \
+            RB[i] = load16(xr, ok ? off * 2 : kOOB);                                        \
+        }                                                                                   \
+        lc0 += BK;                                                                          \
+        if (lc0 >= s.cin_g) {                                                               \
+            lc0 = 0;                                                                        \
+            ++ltap;                                                                         \
+            if (++lkw == s.Kw) { lkw = 0; ++lkh; }                                          \
+        }                                                                                   \
+    } while (0)
+
+#define IGEMM_STORE_STEP(RA, RB, BUF)                                                       \
+    do {                                                                                    \
+        uint4* st_ = lds_raw + (BUF) * STAGE;                                               \
+        _Pragma("unroll") for (int i = 0; i < AV; ++i)                                      \
+            if (AQ % kThreads == 0 || tid + i * kThreads < AQ) st_[a_lds[i]] = RA[i];       \
+        _Pragma("unroll") for (int i = 0; i < BV; ++i) st_[b_lds[i]] = RB[i];               \
+    } while (0)
+
+    // v_mfma_f32_32x32x16_bf16 operands: lane l supplies row (l % 32) and the
+    // 8 K values 8*(l / 32) .. +7 of the 16-wide K slice; a BK-wide K step is
+    // BK/16 such slices (16-byte chunks 2*ks and 2*ks+1 of the LDS row).
+    const int frow = lane & 31, fch = lane >> 5;
+    int a_rd[KS][TM], b_rd[KS][TN];
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            const int row = wm * WTM + i * 16 + frow;
-            af[i] = __builtin_bit_cast(bf16x8, lds[buf][swz(row, fch)]);
-        }
+    for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int prow = wn * WTN + j * 16 + frow;
-            bfr[j] = __builtin_bit_cast(bf16x8, lds[buf][(BM + prow) * kChunks + (fch ^ ((prow >> 1) & 3))]);
-        }
+        for (int i = 0; i < TM; ++i) a_rd[ks][i] = swz<BK>(wm * WTM + i * 32 + frow, 2 * ks + fch);
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-        if (more) store_step(buf ^ 1);
-        __syncthreads();
+        for (int j = 0; j < TN; ++j) b_rd[ks][j] = swz<BK>(BM + wn * WTN + j * 32 + frow, 2 * ks + fch);
     }
 
-    // ---- epilogue: lane holds D[co0 + r][p] for r = 0..3 (4 consecutive
-    // output channels of one pixel) -> one 8-byte store per MFMA tile.
+#define IGEMM_COMPUTE(BUF)                                                                  \
+    do {                                                                                    \
+        const uint4* cur = lds_raw + (BUF) * STAGE;                                         \
+        _Pragma("unroll") for (int ks = 0; ks < KS; ++ks) {                                 \
+            bf16x8 af[TM], bfr[TN];                                                         \
+            _Pragma("unroll") for (int i = 0; i < TM; ++i)                                  \
+                af[i] = __builtin_bit_cast(bf16x8, cur[a_rd[ks][i]]);                       \
+            _Pragma("unroll") for (int j = 0; j < TN; ++j)                                  \
+                bfr[j] = __builtin_bit_cast(bf16x8, cur[b_rd[ks][j]]);                      \
+            _Pragma("unroll") for (int i = 0; i < TM; ++i)                                  \
+                _Pragma("unroll") for (int j = 0; j < TN; ++j)                              \
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j],      \
+                                                                        acc[i][j], 0, 0, 0); \
+        }                                                                                   \
+    } while (0)
+
+    // Software pipeline, two K-steps of global loads in flight: while LDS
+    // stage b holds step st for the matrix cores, the registers of one set
+    // hold step st+1 (arriving) and the other set receives step st+2.  The
+    // step count is rounded up to even so the loop body has no early exit; the
+    // padding step (cursor past the last tap) loads zeros.
+    const int nsteps2 = (nsteps + 1) & ~1;
+    uint4 ra0[AV], rb0[BV], ra1[AV], rb1[BV];
+    IGEMM_LOAD_STEP(ra0, rb0);
+    IGEMM_LOAD_STEP(ra1, rb1);
+    IGEMM_STORE_STEP(ra0, rb0, 0);
+    __syncthreads();
+    // Loads and stores are unconditional (past the last step they read zeros)
+    // so the loop body has no branch and the wait before each LDS store
+    // counts exactly the older step's loads.
+    // The scheduling fences keep each step's loads ahead of the matrix work
+    // (the scheduler would otherwise sink them towards their LDS stores).
+    for (int st = 0; st < nsteps2; st += 2) {
+        IGEMM_LOAD_STEP(ra0, rb0);
+        __builtin_amdgcn_sched_barrier(0);
+        IGEMM_COMPUTE(0);
+        IGEMM_STORE_STEP(ra1, rb1, 1);
+        __syncthreads();
+        IGEMM_LOAD_STEP(ra1, rb1);
+        __builtin_amdgcn_sched_barrier(0);
+        IGEMM_COMPUTE(1);
+        IGEMM_STORE_STEP(ra0, rb0, 0);
+        __syncthreads();
+    }
+#undef IGEMM_LOAD_STEP
+#undef IGEMM_STORE_STEP
+#undef IGEMM_COMPUTE
+
+    // ---- epilogue: bias, ReLU, bf16 rounding in registers; the tile is
+    // staged through LDS as [pixel][channel] rows so that every pixel's BM
+    // output channels leave as contiguous 16-byte stores.
+    // 32x32 MFMA result layout: lane l holds D[8*q + 4*(l/32) + r][l % 32]
+    // in acc[16*0 + 4*q + r] for q, r = 0..3, i.e. four runs of four
+    // consecutive output channels of one pixel.
+    char* ep = reinterpret_cast<char*>(lds_raw);
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-        const int co = co_tile + wm * WTM + i * 16 + 4 * (lane >> 4);
-        if (co >= s.cout_g) continue;
-        const int cg = g * s.cout_g + co;
-        float b4[4] = {0.f, 0.f, 0.f, 0.f};
-        if (BIAS) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) b4[r] = bias[cg + r];
-        }
+        for (int q = 0; q < 4; ++q) {
+            const int col = wm * WTM + i * 32 + 8 * q + 4 * (lane >> 5);  // channel within the tile
+            const int co = co_tile + col;
+            float b4[4] = {0.f, 0.f, 0.f, 0.f};
+            if (BIAS && co < s.cout_g) {
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int p = pt * BN + wn * WTN + j * 16 + (lane & 15);
-            if (p >= npix) continue;
-            float v[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                v[r] = acc[i][j][r] + b4[r];
-                if (RELU) v[r] = fmaxf(v[r], 0.0f);
+                for (int r = 0; r < 4; ++r) b4[r] = bias[g * s.cout_g + co + r];
             }
-            uint2 o = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-            *reinterpret_cast<uint2*>(y + (size_t)p * s.Cout + cg) = o;
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int row = wn * WTN + j * 32 + (lane & 31);      // pixel within the tile
+                float v[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    v[r] = acc[i][j][4 * q + r] + b4[r];
+                    if (RELU) v[r] = fmaxf(v[r], 0.0f);
+                }
+                *reinterpret_cast<uint2*>(ep + row * ERS + col * 2) =
+                    make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+            }
+        }
+    }
+    __syncthreads();
+    const bool vec16 = (s.Cout % 8 == 0) && (s.cout_g % 8 == 0);
+    constexpr int RCH = BM / 8;   // 16-byte chunks per pixel row of the tile
+    for (int q = tid; q < BN * RCH; q += kThreads) {
+        const int row = q / RCH, c = q % RCH;
+        const int p = pt * BN + row;
+        const int co = co_tile + c * 8;
+        if (p >= npix || co >= s.cout_g) continue;
+        const uint4 v = *reinterpret_cast<const uint4*>(ep + row * ERS + c * 16);
+        bf16_t* dst = y + (size_t)p * s.Cout + g * s.cout_g + co;
+        if (vec16 && co + 8 <= s.cout_g) {
+            *reinterpret_cast<uint4*>(dst) = v;
+        } else {
+            *reinterpret_cast<uint2*>(dst) = make_uint2(v.x, v.y);
+            if (co + 8 <= s.cout_g) *reinterpret_cast<uint2*>(dst + 4) = make_uint2(v.z, v.w);
         }
     }
 }
 
-template <int BM, int BN, int WGM, int WGN, bool IS1X1>
+template <int BM, int BN, int WGM, int WGN, int BK, bool IS1X1>
 hipError_t launch_cfg(const Shape& s, const bf16_t* x, const bf16_t* w, const float* b, bf16_t* y,
                       hipStream_t st) {
     const int npix = s.N * s.Ho * s.Wo;
@@ -233,13 +299,13 @@ hipError_t launch_cfg(const Shape& s, const bf16_t* x, const bf16_t* w, const fl
     dim3 grid((unsigned)blocks);
     const bool bias = s.epilogue & CONV2D_EPI_BIAS, relu = s.epilogue & CONV2D_EPI_RELU;
     if (bias && relu)
-        hipLaunchKernelGGL((igemm_kernel<BM, BN, WGM, WGN, IS1X1, true, true>), grid, dim3(kThreads), 0, st, x, w, b, y, s, n_ptiles, n_ctiles);
+        hipLaunchKernelGGL((igemm_kernel<BM, BN, WGM, WGN, BK, IS1X1, true, true>), grid, dim3(kThreads), 0, st, x, w, b, y, s, n_ptiles, n_ctiles);
     else if (bias)
-        hipLaunchKernelGGL((igemm_kernel<BM, BN, WGM, WGN, IS1X1, true, false>), grid, dim3(kThreads), 0, st, x, w, b, y, s, n_ptiles, n_ctiles);
+        hipLaunchKernelGGL((igemm_kernel<BM, BN, WGM, WGN, BK, IS1X1, true, false>), grid, dim3(kThreads), 0, st, x, w, b, y, s, n_ptiles, n_ctiles);
     else if (relu)
-        hipLaunchKernelGGL((igemm_kernel<BM, BN, WGM, WGN, IS1X1, false, true>), grid, dim3(kThreads), 0, st, x, w, b, y, s, n_ptiles, n_ctiles);
+        hipLaunchKernelGGL((igemm_kernel<BM, BN, WGM, WGN, BK, IS1X1, false, true>), grid, dim3(kThreads), 0, st, x, w, b, y, s, n_ptiles, n_ctiles);
     else
-        hipLaunchKernelGGL((igemm_kernel<BM, BN, WGM, WGN, IS1X1, false, false>), grid, dim3(kThreads), 0, st, x, w, b, y, s, n_ptiles, n_ctiles);
+        hipLaunchKernelGGL((igemm_kernel<BM, BN, WGM, WGN, BK, IS1X1, false, false>), grid, dim3(kThreads), 0, st, x, w, b, y, s, n_ptiles, n_ctiles);
     return hipGetLastError();
 }
 
@@ -248,9 +314,12 @@ hipError_t launch_any(const Shape& s, const void* x, const void* w, const float*
     const bf16_t* xt = static_cast<const bf16_t*>(x);
     const bf16_t* wt = static_cast<const bf16_t*>(w);
     bf16_t* yt = static_cast<bf16_t*>(y);
-    if (s.cout_g > 64) return launch_cfg<128, 128, 2, 2, IS1X1>(s, xt, wt, b, yt, st);
-    if (s.cout_g > 32) return launch_cfg<64, 256, 1, 4, IS1X1>(s, xt, wt, b, yt, st);
-    return launch_cfg<32, 256, 1, 4, IS1X1>(s, xt, wt, b, yt, st);
+    // Tile shape by output channels per group: cover them in as few tiles as
+    // possible so each input pixel is fetched once per tap for all of them.
+    if (s.cout_g > 128) return launch_cfg<IGEMM_TILE_M256, IS1X1>(s, xt, wt, b, yt, st);
+    if (s.cout_g > 64) return launch_cfg<IGEMM_TILE_M128, IS1X1>(s, xt, wt, b, yt, st);
+    if (s.cout_g > 32) return launch_cfg<IGEMM_TILE_M64, IS1X1>(s, xt, wt, b, yt, st);
+    return launch_cfg<IGEMM_TILE_M32, IS1X1>(s, xt, wt, b, yt, st);
 }
 
 bool mfma_channels_ok(const Shape& s) {

@@ -1,0 +1,55 @@
+// mfma.hpp -- device helpers shared by the MFMA implicit-GEMM kernels:
+// operand vector types, raw buffer loads with hardware zero for
+// out-of-range offsets, and the LDS chunk swizzle.
+#pragma once
+
+#include "common.hpp"
+
+namespace conv2d {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Raw buffer access: a load whose byte offset lies beyond the descriptor's
+// size returns zero, which is how out-of-image taps (zero padding) and
+// out-of-range rows read 0 without a branch.
+constexpr int kOOB = 0x7ffffff0;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, int byte_off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+
+// Same, with a wave-uniform part of the offset in the instruction's scalar
+// offset (added by the hardware, no vector arithmetic).
+__device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, int byte_off, int uniform_off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, uniform_off, 0));
+}
+
+// An LDS row holds the BK channels of one K-step for one output channel (A)
+// or one pixel (B): BK*2 bytes = BK/8 16-byte chunks.  The chunk index is
+// XOR-swizzled with the row so that any 16 consecutive rows read at the same
+// logical chunk land in 16 distinct 16-byte slots of a 256-byte bank line
+// (conflict-free ds_read_b128 / ds_write_b128): 64-byte rows swizzle with
+// row/4, 128-byte rows with row/2.
+template <int BK>
+__device__ __forceinline__ int swz(int row, int chunk) {
+    if (BK == 32) return row * 4 + (chunk ^ ((row >> 2) & 3));
+    return row * 8 + (chunk ^ ((row >> 1) & 7));
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs (block b runs on XCD
+// b % 8), each with its own L2.  Renumber blocks so that every XCD walks one
+// contiguous run of tiles: neighbouring tiles, which share input rows, then
+// meet in the same L2.
+__device__ __forceinline__ int xcd_tile_index() {
+    const int nblk = gridDim.x;
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int per = nblk >> 3, rem = nblk & 7;
+    return xcd * per + min(xcd, rem) + slot;
+}
+
+}  // namespace conv2d

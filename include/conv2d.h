@@ -60,7 +60,14 @@ enum {
     CONV2D_PATH_DIRECT = 1,     /* direct loop, any shape and dtype             */
     CONV2D_PATH_DEPTHWISE = 2,  /* bf16, groups == Cin == Cout                  */
     CONV2D_PATH_GEMM1X1 = 3,    /* bf16, 1x1, stride 1, pad 0, groups 1         */
-    CONV2D_PATH_IGEMM = 4       /* bf16 implicit GEMM on MFMA, Cin/G % 8 == 0   */
+    CONV2D_PATH_IGEMM = 4,      /* bf16 implicit GEMM on MFMA (as an override:
+                                   the library picks one of the two below)      */
+    CONV2D_PATH_IGEMM_GATHER = 5, /* implicit GEMM gathering every tap from
+                                     memory; any stride, Cin/G % 8 == 0,
+                                     Cout/G % 4 == 0                             */
+    CONV2D_PATH_IGEMM_HALO = 6  /* implicit GEMM on an LDS halo tile; stride 1,
+                                   (K-1)*D+1 <= 5, Cin/G % 8 == 0,
+                                   Cout/G % 4 == 0 and > 32                      */
 };
 
 /* return codes */
@@ -139,8 +146,9 @@ int conv2d_check_args(const void* x, const void* w, const float* bias, const voi
                       int N, int Cin, int H, int W, int Cout, int Kh, int Kw,
                       int stride, int pad, int dilation, int groups, int dtype, int epilogue);
 
-/* Path the NHWC entry would run for this shape (a CONV2D_PATH_* value > 0), or
- * a negative error code.  Honours conv2d_set_path_override.  Host only. */
+/* Kernel the NHWC entry would run for this shape (CONV2D_PATH_DIRECT,
+ * _DEPTHWISE, _GEMM1X1, _IGEMM_GATHER or _IGEMM_HALO), or a negative error
+ * code.  Honours conv2d_set_path_override.  Host only. */
 int conv2d_select_path(int N, int Cin, int H, int W, int Cout, int Kh, int Kw,
                        int stride, int pad, int dilation, int groups, int dtype);
 

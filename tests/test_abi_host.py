@@ -108,9 +108,9 @@ def test_packed_weight_bytes():
 
 
 @pytest.mark.parametrize("cid,li,path", [
-    (1, 0, c2.PATH_DIRECT), (2, 0, c2.PATH_IGEMM), (3, 0, c2.PATH_DEPTHWISE), (3, 1, c2.PATH_GEMM1X1),
-    (4, 0, c2.PATH_IGEMM), (5, 0, c2.PATH_GEMM1X1), (5, 1, c2.PATH_IGEMM), (5, 2, c2.PATH_GEMM1X1),
-    (5, 3, c2.PATH_IGEMM),
+    (1, 0, c2.PATH_DIRECT), (2, 0, c2.PATH_IGEMM_HALO), (3, 0, c2.PATH_DEPTHWISE),
+    (3, 1, c2.PATH_GEMM1X1), (4, 0, c2.PATH_IGEMM_HALO), (5, 0, c2.PATH_GEMM1X1),
+    (5, 1, c2.PATH_IGEMM_HALO), (5, 2, c2.PATH_GEMM1X1), (5, 3, c2.PATH_IGEMM_GATHER),
 ])
 def test_path_selection_for_workloads(cid, li, path):
     ly = ci.layer(cid, li)
@@ -123,8 +123,12 @@ def test_path_selection_fallbacks_and_override():
     # channels not a multiple of 8 -> direct loop; depthwise with odd C -> direct
     assert c2.conv2d_select_path(1, 3, 9, 9, 16, 3, 3, 1, 1, 1, 1, c2.BF16) == c2.PATH_DIRECT
     assert c2.conv2d_select_path(1, 6, 9, 9, 6, 3, 3, 1, 1, 1, 6, c2.BF16) == c2.PATH_DIRECT
-    # 1x1 with stride 2 is not a plain GEMM -> implicit GEMM
-    assert c2.conv2d_select_path(1, 64, 9, 9, 64, 1, 1, 2, 0, 1, 1, c2.BF16) == c2.PATH_IGEMM
+    # 1x1 with stride 2 is not a plain GEMM -> implicit GEMM (gather: stride 2)
+    assert c2.conv2d_select_path(1, 64, 9, 9, 64, 1, 1, 2, 0, 1, 1, c2.BF16) == c2.PATH_IGEMM_GATHER
+    # few output channels per group, or a filter span beyond the halo buffer -> gather
+    assert c2.conv2d_select_path(1, 64, 9, 9, 32, 3, 3, 1, 1, 1, 1, c2.BF16) == c2.PATH_IGEMM_GATHER
+    assert c2.conv2d_select_path(1, 64, 19, 19, 64, 3, 3, 1, 3, 3, 1, c2.BF16) == c2.PATH_IGEMM_GATHER
+    assert c2.conv2d_select_path(1, 64, 19, 19, 64, 5, 5, 1, 2, 1, 1, c2.BF16) == c2.PATH_IGEMM_HALO
     prev = c2.conv2d_set_path_override(c2.PATH_DIRECT)
     try:
         assert prev == c2.PATH_AUTO
@@ -132,6 +136,15 @@ def test_path_selection_fallbacks_and_override():
         c2.conv2d_set_path_override(c2.PATH_GEMM1X1)
         with pytest.raises(c2.Conv2dError):
             c2.conv2d_select_path(1, 64, 9, 9, 64, 3, 3, 1, 1, 1, 1, c2.BF16)
+    finally:
+        c2.conv2d_set_path_override(c2.PATH_AUTO)
+    c2.conv2d_set_path_override(c2.PATH_IGEMM)
+    try:
+        assert c2.conv2d_select_path(1, 64, 9, 9, 64, 3, 3, 1, 1, 1, 1, c2.BF16) == c2.PATH_IGEMM_HALO
+        assert c2.conv2d_select_path(1, 64, 9, 9, 64, 3, 3, 2, 1, 1, 1, c2.BF16) == c2.PATH_IGEMM_GATHER
+        c2.conv2d_set_path_override(c2.PATH_IGEMM_HALO)
+        with pytest.raises(c2.Conv2dError):
+            c2.conv2d_select_path(1, 64, 9, 9, 64, 3, 3, 2, 1, 1, 1, c2.BF16)
     finally:
         c2.conv2d_set_path_override(c2.PATH_AUTO)
     assert c2.lib.conv2d_set_path_override(9) == c2.ERR_ARG

@@ -171,6 +171,14 @@ def _sweep():
         (2, 48, 13, 3, 12, 3, 3, 1, 1, 3, 1), (1, 8, 3, 3, 4, 7, 7, 1, 3, 1, 1),
         (1, 96, 10, 10, 96, 1, 1, 2, 0, 1, 1), (2, 32, 8, 8, 32, 3, 3, 1, 1, 1, 4),
         (1, 256, 5, 6, 8, 3, 3, 1, 1, 1, 1), (1, 8, 6, 6, 260, 3, 3, 1, 1, 1, 1),
+        # shapes for the halo-tile kernel (stride 1, Cout/G > 32): ragged 16x16
+        # and 8x32 pixel blocks, dilation, 5x5, groups, Cin/G not a multiple of
+        # the 32-channel chunk, Cout/G not a multiple of the channel tile
+        (2, 64, 19, 21, 64, 3, 3, 1, 1, 1, 1), (1, 32, 17, 40, 48, 3, 3, 1, 1, 1, 1),
+        (2, 128, 9, 35, 256, 3, 3, 1, 1, 1, 1), (1, 40, 12, 12, 36, 3, 3, 1, 2, 2, 1),
+        (1, 64, 11, 13, 128, 5, 5, 1, 2, 1, 1), (2, 96, 10, 10, 192, 3, 3, 1, 1, 1, 2),
+        (1, 16, 20, 18, 300, 3, 1, 1, 0, 1, 1), (1, 24, 7, 33, 72, 1, 3, 1, 1, 2, 1),
+        (1, 8, 2, 3, 40, 3, 3, 1, 1, 1, 1), (1, 136, 6, 5, 64, 3, 3, 1, 0, 1, 1),
     ]
     return cases
 
@@ -180,17 +188,25 @@ DW_CASES = [(2, 16, 11, 9, 3, 3, 1, 1, 1), (1, 32, 7, 8, 3, 3, 2, 1, 1), (2, 8, 
             (2, 144, 9, 13, 3, 3, 1, 1, 1), (1, 40, 8, 8, 1, 1, 1, 0, 1)]
 
 
-@pytest.mark.parametrize("path", ["direct", "igemm", "gemm1x1"])
+PATHS = {"direct": "PATH_DIRECT", "igemm_gather": "PATH_IGEMM_GATHER", "igemm_halo": "PATH_IGEMM_HALO",
+         "gemm1x1": "PATH_GEMM1X1"}
+
+
+@pytest.mark.parametrize("path", list(PATHS))
 @pytest.mark.parametrize("mode", ["random", "int"])
 def test_path_sweep(path, mode):
-    pid = {"direct": c2.PATH_DIRECT, "igemm": c2.PATH_IGEMM, "gemm1x1": c2.PATH_GEMM1X1}[path]
+    """Every case the forced path can run (the library's own support check),
+    each with and without the bias+ReLU epilogue."""
+    pid = getattr(c2, PATHS[path])
     ran = 0
     for k, (N, Cin, H, W, Cout, Kh, Kw, S, P, D, G) in enumerate(_sweep()):
-        if path == "gemm1x1" and not (Kh == Kw == 1 and S == 1 and P == 0 and G == 1):
-            continue
         if oracle.out_dim(H, Kh, S, P, D) < 1 or oracle.out_dim(W, Kw, S, P, D) < 1:
             continue
         c2.conv2d_set_path_override(pid)
+        try:
+            c2.conv2d_select_path(N, Cin, H, W, Cout, Kh, Kw, S, P, D, G, c2.BF16)
+        except c2.Conv2dError:
+            continue
         for epi in (0, 3):
             x, w, b = ci.random_tensors(100 + k, N, Cin, H, W, Cout, Kh, Kw, G, mode=mode, bias=epi & 1)
             say(f"[sweep] {path} {mode} case {k} {(N, Cin, H, W, Cout, Kh, Kw, S, P, D, G)} epi {epi}")
@@ -222,7 +238,7 @@ def test_depthwise_sweep(path, mode):
 
 @pytest.mark.parametrize("mode", ["random", "int"])
 def test_direct_fp32_sweep(mode):
-    for k, (N, Cin, H, W, Cout, Kh, Kw, S, P, D, G) in enumerate(_sweep()[:10]):
+    for k, (N, Cin, H, W, Cout, Kh, Kw, S, P, D, G) in enumerate(_sweep()[:24]):
         if oracle.out_dim(H, Kh, S, P, D) < 1 or oracle.out_dim(W, Kw, S, P, D) < 1:
             continue
         x, w, b = ci.random_tensors(500 + k, N, Cin, H, W, Cout, Kh, Kw, G, dtype=ci.F32, mode=mode)
