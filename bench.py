@@ -243,17 +243,31 @@ def main(argv=None):
     ap.add_argument("--all", action="store_true", help="time every workload layer")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run 5 plain device copies of 256 MiB (known HBM traffic), for "
+                         "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
     a = ap.parse_args(argv)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {a.gpus}, WORLD_SIZE "
-              f"{world}); a multi-GPU batch split is described in DESIGN.md but not built.",
+              f"{world}); a multi-GPU split of the batch is not built.",
               file=sys.stderr)
         return 2
     import torch
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
+    if a.copy_calibration:
+        n = 256 << 20
+        src = torch.ones(n // 2, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
+                          "dispatches": 5}))
+        return 0
     from cnn_convolution_conv2d_amd import build as b
     if not os.path.exists(b.OUT):
         b.build()

@@ -73,14 +73,52 @@ __device__ __forceinline__ V8 load_v8(__amdgpu_buffer_rsrc_t r, int byte_off) {
     return __builtin_bit_cast(V8, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }
 
-// 3x3, stride 1, dilation 1, any padding; rolling three-row register window.
-// The next input row is requested before the current output row is computed,
-// so one row of loads is always in flight behind the arithmetic.
+// 3x3, stride 1, dilation 1, any padding.
+//
+// Each input row the thread touches (its 3 columns wo-1..wo+1, 8 channels) is
+// converted once into the form the arithmetic uses and then serves the three
+// output rows that read it (rows ho-1, ho, ho+1 use it with filter rows 2, 1,
+// 0; lincklin.cn section 18 on adjacent outputs sharing inputs):
+//   - taps kw=0 and kw=1 of channel c become one bf16 pair (x[wo-1][c],
+//     x[wo][c]) built with v_perm_b32, multiplied by the matching weight pair
+//     with v_dot2c_f32_bf16 (two products and the running sum in one op);
+//   - tap kw=2 is kept as fp32 for a plain FMA.
+// The bias is the accumulator's starting value.  Two input rows of loads are
+// in flight ahead of the arithmetic (the loop is unrolled by two so that no
+// register with a pending load is ever moved).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+struct RowX {
+    uint32_t p01[8];  // per channel: (x[wo-1][c], x[wo][c]) as a bf16 pair
+    float x2[8];      // per channel: x[wo+1][c]
+};
+
+__device__ __forceinline__ void prep_row(const V8& a, const V8& b, const V8& c, RowX& r) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        // v_perm_b32: bytes 0-3 select from the second operand, 4-7 from the first
+        r.p01[2 * i] = __builtin_amdgcn_perm(b.u[i], a.u[i], 0x05040100u);      // low halves
+        r.p01[2 * i + 1] = __builtin_amdgcn_perm(b.u[i], a.u[i], 0x07060302u);  // high halves
+        r.x2[2 * i] = lo(c.u[i]);
+        r.x2[2 * i + 1] = hi(c.u[i]);
+    }
+}
+
+__device__ __forceinline__ void row_fma(float acc[8], const RowX& r, const uint32_t wp[8], const float w2[8]) {
+#pragma unroll
+    for (int ch = 0; ch < 8; ++ch) {
+        acc[ch] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, r.p01[ch]),
+                                                  __builtin_bit_cast(bf16x2_t, wp[ch]), acc[ch], false);
+        acc[ch] = fmaf(r.x2[ch], w2[ch], acc[ch]);
+    }
+}
+
 template <int TH, bool BIAS, bool RELU>
 __global__ __launch_bounds__(kThreads) void dw3x3s1_kernel(const bf16_t* __restrict__ x,
                                                            const bf16_t* __restrict__ w,   // [3][3][C]
                                                            const float* __restrict__ bias,
                                                            bf16_t* __restrict__ y, Shape s) {
+    static_assert(TH % 2 == 0, "rows per thread come in pairs");
     const int CV = s.Cin >> 3;                       // 16-byte vectors per pixel
     const int v = blockIdx.x * kThreads + threadIdx.x;
     if (v >= s.Wo * CV) return;
@@ -90,16 +128,25 @@ __global__ __launch_bounds__(kThreads) void dw3x3s1_kernel(const bf16_t* __restr
     const int ho0 = blockIdx.y * TH;
     const int ho1 = min(ho0 + TH, s.Ho);
 
-    float wr[9][8];
+    // weights: per filter row, the (kw0, kw1) pair of each channel and kw2 in fp32
+    uint32_t wp[3][8];
+    float w2[3][8];
 #pragma unroll
-    for (int t = 0; t < 9; ++t) {
-        const V8 wv = load_v8(w + t * s.Cin + c0);
+    for (int kh = 0; kh < 3; ++kh) {
+        const V8 a = load_v8(w + (kh * 3 + 0) * s.Cin + c0);
+        const V8 b = load_v8(w + (kh * 3 + 1) * s.Cin + c0);
+        const V8 c = load_v8(w + (kh * 3 + 2) * s.Cin + c0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) { wr[t][2 * i] = lo(wv.u[i]); wr[t][2 * i + 1] = hi(wv.u[i]); }
+        for (int i = 0; i < 4; ++i) {
+            wp[kh][2 * i] = __builtin_amdgcn_perm(b.u[i], a.u[i], 0x05040100u);
+            wp[kh][2 * i + 1] = __builtin_amdgcn_perm(b.u[i], a.u[i], 0x07060302u);
+            w2[kh][2 * i] = lo(c.u[i]);
+            w2[kh][2 * i + 1] = hi(c.u[i]);
+        }
     }
-    float br[8];
+    float b0[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) br[i] = BIAS ? bias[c0 + i] : 0.0f;
+    for (int i = 0; i < 8; ++i) b0[i] = BIAS ? bias[c0 + i] : 0.0f;
 
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)s.N * s.H * s.W * s.Cin * 2u);
     // byte offsets of the window's three input columns in row 0 of image n;
@@ -111,33 +158,56 @@ __global__ __launch_bounds__(kThreads) void dw3x3s1_kernel(const bf16_t* __restr
     for (int k = 0; k < 3; ++k)
         coff[k] = ((unsigned)(wi0 + k) < (unsigned)s.W) ? (img + (wi0 + k) * s.Cin) * 2 : kOOB;
     const int rstride = s.W * s.Cin * 2;
-
     auto row_off = [&](int hi_, int k) {
         return ((unsigned)hi_ < (unsigned)s.H && coff[k] != kOOB) ? coff[k] + hi_ * rstride : kOOB;
     };
+#define DW_LOAD(RAW, HI)                                                                     \
+    do {                                                                                     \
+        _Pragma("unroll") for (int k = 0; k < 3; ++k) RAW[k] = load_v8(xr, row_off((HI), k)); \
+    } while (0)
 
-    V8 r0[3], r1[3], r2[3], rn[3];
-#pragma unroll
-    for (int k = 0; k < 3; ++k) {
-        r0[k] = load_v8(xr, row_off(ho0 - s.pad, k));
-        r1[k] = load_v8(xr, row_off(ho0 - s.pad + 1, k));
-        r2[k] = load_v8(xr, row_off(ho0 - s.pad + 2, k));
-    }
     bf16_t* yrow = y + ((size_t)n * s.Ho * s.Wo + wo) * s.Cout + c0;
-    for (int ho = ho0; ho < ho1; ++ho) {
+    auto emit = [&](int ho, const RowX& r0, const RowX& r1, const RowX& r2) {
+        float acc[8];
 #pragma unroll
-        for (int k = 0; k < 3; ++k) rn[k] = load_v8(xr, row_off(ho - s.pad + 3, k));
-        float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        for (int i = 0; i < 8; ++i) acc[i] = b0[i];
+        row_fma(acc, r0, wp[0], w2[0]);
+        row_fma(acc, r1, wp[1], w2[1]);
+        row_fma(acc, r2, wp[2], w2[2]);
+        V8 o;
 #pragma unroll
-        for (int k = 0; k < 3; ++k) {
-            fma_v8(acc, r0[k], wr[k]);
-            fma_v8(acc, r1[k], wr[3 + k]);
-            fma_v8(acc, r2[k], wr[6 + k]);
+        for (int i = 0; i < 4; ++i) {
+            float a0 = acc[2 * i], a1 = acc[2 * i + 1];
+            if (RELU) { a0 = fmaxf(a0, 0.0f); a1 = fmaxf(a1, 0.0f); }
+            o.u[i] = pack_bf16x2(a0, a1);
         }
-        *reinterpret_cast<V8*>(yrow + (size_t)ho * s.Wo * s.Cout) = finish<BIAS, RELU>(acc, br);
+        if (ho < ho1) *reinterpret_cast<V8*>(yrow + (size_t)ho * s.Wo * s.Cout) = o;
+    };
+
+    const int hb = ho0 - s.pad;  // input row of filter row 0 for output row ho0
+    V8 rawA[3], rawB[3];
+    RowX R0, R1, R2;
+    DW_LOAD(rawA, hb);
+    DW_LOAD(rawB, hb + 1);
+    prep_row(rawA[0], rawA[1], rawA[2], R0);
+    DW_LOAD(rawA, hb + 2);
+    prep_row(rawB[0], rawB[1], rawB[2], R1);
+    DW_LOAD(rawB, hb + 3);
+    prep_row(rawA[0], rawA[1], rawA[2], R2);
+    // invariant at the top of each half-iteration: R0..R2 hold input rows
+    // ho-pad .. ho-pad+2; rawB holds row ho-pad+3 (arriving)
 #pragma unroll
-        for (int k = 0; k < 3; ++k) { r0[k] = r1[k]; r1[k] = r2[k]; r2[k] = rn[k]; }
+    for (int ho = ho0; ho < ho0 + TH; ho += 2) {
+        DW_LOAD(rawA, hb + (ho - ho0) + 4);
+        emit(ho, R0, R1, R2);
+        prep_row(rawB[0], rawB[1], rawB[2], R0);  // R0 <- row ho-pad+3
+        DW_LOAD(rawB, hb + (ho - ho0) + 5);
+        emit(ho + 1, R1, R2, R0);
+        prep_row(rawA[0], rawA[1], rawA[2], R1);  // R1 <- row ho-pad+4
+        // rotate names for the next pair: rows now R2, R0, R1
+        RowX t = R0; R0 = R2; R2 = R1; R1 = t;
     }
+#undef DW_LOAD
 }
 
 // Any Kh, Kw, stride, padding, dilation.
@@ -180,8 +250,9 @@ __global__ __launch_bounds__(kThreads) void dw_generic_kernel(const bf16_t* __re
 }
 
 #ifndef DW_ROWS_PER_THREAD
-#define DW_ROWS_PER_THREAD 8
+#define DW_ROWS_PER_THREAD 14
 #endif
+static_assert(DW_ROWS_PER_THREAD % 2 == 0, "rows per thread come in pairs");
 constexpr int kTH = DW_ROWS_PER_THREAD;  // output rows per thread
 
 template <bool BIAS, bool RELU>

@@ -72,6 +72,7 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(const bf16_t* __restric
     constexpr int ERS = BM * 2 + 16;                       // epilogue LDS row stride (bytes)
     constexpr int LDS_UNITS = (2 * STAGE > BN * ERS / 16) ? 2 * STAGE : BN * ERS / 16;
     __shared__ uint4 lds_raw[LDS_UNITS];
+    __shared__ __align__(16) float sbias[BM];  // this tile's bias, read by the epilogue
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WGN, wn = wave % WGN;
@@ -214,6 +215,11 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(const bf16_t* __restric
     uint4 ra0[AV], rb0[BV], ra1[AV], rb1[BV];
     IGEMM_LOAD_STEP(ra0, rb0);
     IGEMM_LOAD_STEP(ra1, rb1);
+    if (BIAS) {
+        // stage the tile's bias once (visible after the barrier below)
+        for (int i = tid; i < BM; i += kThreads)
+            sbias[i] = co_tile + i < s.cout_g ? bias[g * s.cout_g + co_tile + i] : 0.0f;
+    }
     IGEMM_STORE_STEP(ra0, rb0, 0);
     __syncthreads();
     // Loads and stores are unconditional (past the last step they read zeros)
@@ -250,18 +256,16 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(const bf16_t* __restric
         for (int q = 0; q < 4; ++q) {
             const int col = wm * WTM + i * 32 + 8 * q + 4 * (lane >> 5);  // channel within the tile
             const int co = co_tile + col;
-            float b4[4] = {0.f, 0.f, 0.f, 0.f};
-            if (BIAS && co < s.cout_g) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) b4[r] = bias[g * s.cout_g + co + r];
-            }
+            float4 b4 = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (BIAS) b4 = *reinterpret_cast<const float4*>(&sbias[col]);
+            (void)co;
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
                 const int row = wn * WTN + j * 32 + (lane & 31);      // pixel within the tile
                 float v[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    v[r] = acc[i][j][4 * q + r] + b4[r];
+                    v[r] = acc[i][j][4 * q + r] + (&b4.x)[r];
                     if (RELU) v[r] = fmaxf(v[r], 0.0f);
                 }
                 *reinterpret_cast<uint2*>(ep + row * ERS + col * 2) =

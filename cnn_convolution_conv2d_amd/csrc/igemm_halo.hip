@@ -31,6 +31,19 @@ namespace conv2d {
 
 namespace {
 
+// Tile configurations per range of output channels per group: threads,
+// BM output channels, WGM x WGN waves, two equal-size pixel-block shapes
+// (rows x columns).  Overridable at build time for tuning sweeps.
+#ifndef HALO_CFG_M256
+#define HALO_CFG_M256 512, 256, 2, 4, 16, 16, 8, 32
+#endif
+#ifndef HALO_CFG_M128
+#define HALO_CFG_M128 256, 128, 2, 2, 16, 16, 8, 32
+#endif
+#ifndef HALO_CFG_M64
+#define HALO_CFG_M64 256, 64, 1, 4, 16, 16, 8, 32
+#endif
+
 constexpr int kBK = 32;    // input channels per chunk: one 64-byte LDS row per pixel
 constexpr int kKEmax = 5;  // largest effective filter extent (Kh-1)*D+1 the halo buffer holds
 
@@ -72,6 +85,7 @@ __global__ __launch_bounds__(NT) void halo_kernel(const bf16_t* __restrict__ x,
     static_assert(EPW >= 1 && WGN % EPW == 0, "epilogue pass fits LDS");
     constexpr int NPASS = WGN / EPW;
     __shared__ uint4 lds[PIPE_UNITS];
+    __shared__ __align__(16) float sbias[BM];  // this tile's bias, read by the epilogue
     uint4* const abuf = lds;                // [2][A_UNITS]
     uint4* const hbuf = lds + 2 * A_UNITS;  // [2][H_UNITS]
 
@@ -184,6 +198,11 @@ __global__ __launch_bounds__(NT) void halo_kernel(const bf16_t* __restrict__ x,
 
     HALO_LOAD(0);
     A_LOAD(0, 0);
+    if (BIAS) {
+        // stage the tile's bias once (visible after the barrier below)
+        for (int i = tid; i < BM; i += NT)
+            sbias[i] = co_tile + i < s.cout_g ? bias[g * s.cout_g + co_tile + i] : 0.0f;
+    }
     HALO_STORE(0);
     A_STORE(0);
     __syncthreads();
@@ -208,21 +227,27 @@ __global__ __launch_bounds__(NT) void halo_kernel(const bf16_t* __restrict__ x,
                 __builtin_amdgcn_sched_barrier(0);
                 const char* acur = reinterpret_cast<const char*>(abuf + (st & 1) * A_UNITS);
                 const char* hb = hcur + (kh * s.dil * HWd + kw * s.dil) * (kHP * 16);
+                // Both K slices' operands are requested before any matrix
+                // op, so the second slice's LDS reads overlap the first
+                // slice's MFMAs.
+                bf16x8 af[2][TM], bfr[2][TN];
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
-                    bf16x8 af[TM], bfr[TN];
 #pragma unroll
                     for (int i = 0; i < TM; ++i)
-                        af[i] = *reinterpret_cast<const bf16x8*>(acur + a_rd[ks][i]);
+                        af[ks][i] = *reinterpret_cast<const bf16x8*>(acur + a_rd[ks][i]);
 #pragma unroll
                     for (int j = 0; j < TN; ++j)
-                        bfr[j] = *reinterpret_cast<const bf16x8*>(hb + b_rd[j] + ks * 32);
+                        bfr[ks][j] = *reinterpret_cast<const bf16x8*>(hb + b_rd[j] + ks * 32);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
                     for (int i = 0; i < TM; ++i)
 #pragma unroll
                         for (int j = 0; j < TN; ++j)
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-                }
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks][i], bfr[ks][j], acc[i][j], 0, 0, 0);
                 A_STORE((st + 1) & 1);
                 if (last_tap && c + 1 < nchunk) HALO_STORE((c + 1) & 1);
                 __syncthreads();
@@ -252,18 +277,16 @@ __global__ __launch_bounds__(NT) void halo_kernel(const bf16_t* __restrict__ x,
                 for (int q = 0; q < 4; ++q) {
                     const int col = wm * WTM + i * 32 + 8 * q + 4 * (lane >> 5);
                     const int co = co_tile + col;
-                    float b4[4] = {0.f, 0.f, 0.f, 0.f};
-                    if (BIAS && co < s.cout_g) {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) b4[r] = bias[g * s.cout_g + co + r];
-                    }
+                    float4 b4 = make_float4(0.f, 0.f, 0.f, 0.f);
+                    if (BIAS) b4 = *reinterpret_cast<const float4*>(&sbias[col]);
+                    (void)co;
 #pragma unroll
                     for (int j = 0; j < TN; ++j) {
                         const int row = (wn % EPW) * WTN + j * 32 + (lane & 31);
                         float v[4];
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
-                            v[r] = acc[i][j][4 * q + r] + b4[r];
+                            v[r] = acc[i][j][4 * q + r] + (&b4.x)[r];
                             if (RELU) v[r] = fmaxf(v[r], 0.0f);
                         }
                         *reinterpret_cast<uint2*>(ep + row * ERS + col * 2) =
@@ -313,23 +336,19 @@ hipError_t launch_tile(const Shape& s, const bf16_t* x, const bf16_t* w, const f
     return hipGetLastError();
 }
 
-// Pixel block shape: 16x16 or 8x32, whichever pads the output least.
-bool prefer_wide(const Shape& s) {
-    const long long sq = (long long)((s.Ho + 15) / 16 * 16) * ((s.Wo + 15) / 16 * 16);
-    const long long wide = (long long)((s.Ho + 7) / 8 * 8) * ((s.Wo + 31) / 32 * 32);
-    return wide < sq;
-}
-
-template <int NT, int BM, int WGM, int WGN>
+template <int NT, int BM, int WGM, int WGN, int THA, int TWA, int THB, int TWB>
 hipError_t launch_shape(const Shape& s, const bf16_t* x, const bf16_t* w, const float* b, bf16_t* y,
                         hipStream_t st) {
+    static_assert(THA * TWA == THB * TWB, "equal pixel blocks");
     const bool full = s.cin_g % kBK == 0;
-    if (prefer_wide(s)) {
-        if (full) return launch_tile<NT, BM, 8, 32, WGM, WGN, true>(s, x, w, b, y, st);
-        return launch_tile<NT, BM, 8, 32, WGM, WGN, false>(s, x, w, b, y, st);
+    const long long pa = (long long)((s.Ho + THA - 1) / THA * THA) * ((s.Wo + TWA - 1) / TWA * TWA);
+    const long long pb = (long long)((s.Ho + THB - 1) / THB * THB) * ((s.Wo + TWB - 1) / TWB * TWB);
+    if (pb < pa) {
+        if (full) return launch_tile<NT, BM, THB, TWB, WGM, WGN, true>(s, x, w, b, y, st);
+        return launch_tile<NT, BM, THB, TWB, WGM, WGN, false>(s, x, w, b, y, st);
     }
-    if (full) return launch_tile<NT, BM, 16, 16, WGM, WGN, true>(s, x, w, b, y, st);
-    return launch_tile<NT, BM, 16, 16, WGM, WGN, false>(s, x, w, b, y, st);
+    if (full) return launch_tile<NT, BM, THA, TWA, WGM, WGN, true>(s, x, w, b, y, st);
+    return launch_tile<NT, BM, THA, TWA, WGM, WGN, false>(s, x, w, b, y, st);
 }
 
 }  // namespace
@@ -346,9 +365,9 @@ hipError_t launch_igemm_halo(const Shape& s, const void* x, const void* w_packed
     const bf16_t* xt = static_cast<const bf16_t*>(x);
     const bf16_t* wt = static_cast<const bf16_t*>(w_packed);
     bf16_t* yt = static_cast<bf16_t*>(y);
-    if (s.cout_g > 128) return launch_shape<512, 256, 2, 4>(s, xt, wt, bias, yt, st);
-    if (s.cout_g > 64) return launch_shape<256, 128, 2, 2>(s, xt, wt, bias, yt, st);
-    return launch_shape<256, 64, 1, 4>(s, xt, wt, bias, yt, st);
+    if (s.cout_g > 128) return launch_shape<HALO_CFG_M256>(s, xt, wt, bias, yt, st);
+    if (s.cout_g > 64) return launch_shape<HALO_CFG_M128>(s, xt, wt, bias, yt, st);
+    return launch_shape<HALO_CFG_M64>(s, xt, wt, bias, yt, st);
 }
 
 }  // namespace conv2d
