@@ -3,27 +3,43 @@
 //
 // Same GEMM as the gather kernel (lincklin.cn lesson 9, sections 7, 11, 19):
 // per group, D[co][p] = sum_k W[co][k] * X_col[k][p] with k = (ci, kh, kw).
-// What changes is where X_col comes from.  A workgroup owns BM output
-// channels x a TH x TW block of output pixels of one image.  For stride 1
-// every tap of that block reads inside one (TH + (Kh-1)D) x (TW + (Kw-1)D)
-// input window -- the block plus its halo (lincklin.cn section 12: a 16x16
-// output tile of a 3x3 filter needs an 18x18 input tile).  The window is
-// loaded from HBM/L2 once per 32-channel chunk into LDS (section 13: load
-// the tile cooperatively, synchronise, let every thread read its windows),
-// and each of the Kh*Kw taps then reads its B operand from that tile at a
-// fixed offset (kh*D rows, kw*D columns): input reuse across taps happens in
-// LDS instead of through the vector-memory path.  Dilation is only a larger
+// What changes is where X_col comes from.  A tile is BM output channels x a
+// TH x TW block of output pixels of one image.  For stride 1 every tap of
+// that block reads inside one (TH + (Kh-1)D) x (TW + (Kw-1)D) input window --
+// the block plus its halo (lincklin.cn section 12: a 16x16 output tile of a
+// 3x3 filter needs an 18x18 input tile).  The window is loaded from HBM/L2
+// once per 32-channel chunk into LDS (section 13: load the tile
+// cooperatively, synchronise, let every thread read its windows), and each
+// of the Kh*Kw taps then reads its B operand from that tile at a fixed
+// offset (kh*D rows, kw*D columns): input reuse across taps happens in LDS
+// instead of through the vector-memory path.  Dilation is only a larger
 // offset, so exactly the Kh*Kw real taps are gathered (lpnh.cn section 4.2).
 // Zero padding: window pixels outside the image are loaded as 0
 // (lincklin.cn section 26).
 //
-// K loop: chunk (32 input channels) outer, tap inner.  Per step the BM x 32
-// weight slice of (tap, chunk) is staged in LDS (double-buffered, loaded one
-// step ahead); the next chunk's halo tile is requested at the chunk's first
-// tap and written to the other halo buffer a few taps later.  Matrix cores:
-// v_mfma_f32_32x32x16_bf16, fp32 accumulators in registers for the whole K
-// loop (output stationary), fused bias + ReLU + bf16 rounding, results
-// staged through LDS so each pixel's channels are stored contiguously.
+// Schedule.  The kernel is persistent: workgroup b walks tiles b, b+G, ...
+// as one continuous stream of K-steps (one step = one tap of one 32-channel
+// chunk), so the loads of the next tile's first steps overlap the current
+// tile's last ones and there is no per-tile prologue.  Per step:
+//  * the BM x 32 weight slice is staged in a 3-slot LDS ring; its global
+//    loads are issued two steps ahead of their LDS store (two register sets),
+//  * one 16-byte piece per thread of the NEXT chunk's halo tile is loaded at
+//    each of the chunk's first taps (a load that returns zero at the others,
+//    so every step issues the same number of loads) and stored one step
+//    later into the other halo buffer,
+//  * v_mfma_f32_32x32x16_bf16 runs on two 16-wide K slices; the operands of
+//    the second slice are read from LDS while the first slice's matrix ops
+//    run, and the operands of the NEXT step's first slice while the second
+//    slice's run -- the 3-slot ring makes that step's weights visible one
+//    barrier earlier, so a wave leaves each barrier with its operands
+//    already in registers,
+//  * one barrier.
+// fp32 accumulators stay in registers for the whole K loop of a tile
+// (output stationary).  At a tile's last step the epilogue adds the bias,
+// applies ReLU, rounds to bf16 and stores straight from registers
+// (lincklin.cn section 31): a lane-half swap (v_permlane32_swap) turns the
+// 32x32 result layout into 8 consecutive channels of one pixel per lane, one
+// 16-byte store each.
 #include "mfma.hpp"
 #include "../../include/conv2d.h"
 
@@ -32,20 +48,21 @@ namespace conv2d {
 namespace {
 
 // Tile configurations per range of output channels per group: threads,
-// BM output channels, WGM x WGN waves, two equal-size pixel-block shapes
-// (rows x columns).  Overridable at build time for tuning sweeps.
-#ifndef HALO_CFG_M256
-#define HALO_CFG_M256 512, 256, 2, 4, 16, 16, 8, 32
-#endif
+// workgroups per CU the kernel is compiled for, BM output channels, WGM x WGN
+// waves, two equal-size pixel-block shapes (rows x columns).  Two
+// independent workgroups per CU (one wave per SIMD each) let one workgroup's
+// epilogue, barrier and load waits overlap the other's matrix work.
+// Overridable at build time for tuning sweeps.
 #ifndef HALO_CFG_M128
-#define HALO_CFG_M128 256, 128, 2, 2, 16, 16, 8, 32
+#define HALO_CFG_M128 256, 2, 128, 1, 4, 16, 16, 8, 32
 #endif
 #ifndef HALO_CFG_M64
-#define HALO_CFG_M64 256, 64, 1, 4, 16, 16, 8, 32
+#define HALO_CFG_M64 256, 2, 64, 1, 4, 16, 16, 8, 32
 #endif
 
-constexpr int kBK = 32;    // input channels per chunk: one 64-byte LDS row per pixel
-constexpr int kKEmax = 5;  // largest effective filter extent (Kh-1)*D+1 the halo buffer holds
+constexpr int kBK = 32;      // input channels per chunk: one 64-byte LDS row per pixel
+constexpr int kKEmax = 5;    // largest effective filter extent (Kh-1)*D+1 the halo buffer holds
+constexpr int kRing = 3;     // weight slices staged in LDS
 
 // Halo tile layout in LDS: one window pixel = 5 16-byte units (80 bytes:
 // its 4 chunks of 8 channels plus one unit of padding).  Because 5 is odd,
@@ -54,90 +71,103 @@ constexpr int kKEmax = 5;  // largest effective filter extent (Kh-1)*D+1 the hal
 // is a plain additive offset of (kh*D*width + kw*D) * 80 bytes.
 constexpr int kHP = 5;
 
-// Largest divisor of n that is <= cap (0 if none).
-constexpr int largest_divisor_upto(int n, int cap) {
-    for (int d = cap < n ? cap : n; d >= 1; --d)
-        if (n % d == 0) return d;
-    return 0;
+struct HaloGrid {
+    int tiles_h, tiles_w, n_ctiles, ntiles;
+    int hwd_magic;  // ceil(2^16 / window width): row = (pixel * magic) >> 16 inside the window
+    int nparts;     // 16-byte halo loads per thread per chunk (one per tap)
+};
+
+// LDS bytes of one workgroup: weight ring, two halo buffers, two bias buffers.
+constexpr int halo_lds_bytes(int bm, int th, int tw, int ke, bool bias) {
+    return kRing * bm * kBK * 2 + 2 * (th + ke - 1) * (tw + ke - 1) * kHP * 16 + (bias ? 2 * bm * 4 : 0);
 }
 
-template <int NT, int BM, int TH, int TW, int WGM, int WGN, bool CFULL, bool BIAS, bool RELU>
-__global__ __launch_bounds__(NT) void halo_kernel(const bf16_t* __restrict__ x,
-                                                  const bf16_t* __restrict__ wp,
-                                                  const float* __restrict__ bias,
-                                                  bf16_t* __restrict__ y, Shape s,
-                                                  int tiles_h, int tiles_w, int n_ctiles) {
+// Minimum waves per SIMD the registers are budgeted for: the requested
+// workgroups per CU, or fewer where their LDS does not fit (160 KB per CU).
+constexpr int waves_per_simd(int nt, int minb, int lds_bytes) {
+    const int fit = 163840 / lds_bytes;
+    const int b = minb < fit ? minb : fit;
+    return b * nt / 256 < 1 ? 1 : b * nt / 256;
+}
+
+// Tile t -> (output-channel tile, group, image, pixel-block origin); the
+// channel tile varies fastest, then the group, then pixel blocks in row-major
+// order over each image.
+struct TileXY {
+    int ct, g, n, ho0, wo0;
+};
+
+template <int TH, int TW>
+__device__ __forceinline__ TileXY tile_xy(int tile, const HaloGrid& hg, int groups) {
+    TileXY t;
+    t.ct = tile % hg.n_ctiles;
+    tile /= hg.n_ctiles;
+    t.g = tile % groups;
+    tile /= groups;
+    const int tw = tile % hg.tiles_w;
+    tile /= hg.tiles_w;
+    const int th = tile % hg.tiles_h;
+    t.n = tile / hg.tiles_h;
+    t.ho0 = th * TH;
+    t.wo0 = tw * TW;
+    return t;
+}
+
+// KE: largest effective filter extent the halo buffers hold (3 or 5).
+template <int NT, int MINB, int BM, int TH, int TW, int WGM, int WGN, int KE, bool CFULL, bool BIAS, bool RELU>
+__global__ __launch_bounds__(NT, waves_per_simd(NT, MINB, halo_lds_bytes(BM, TH, TW, KE, BIAS))) void halo_kernel(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ wp, const float* __restrict__ bias,
+    bf16_t* __restrict__ y, Shape s, HaloGrid hg) {
     constexpr int BN = TH * TW;
     static_assert(WGM * WGN * 64 == NT, "one wave per sub-tile");
     constexpr int WTM = BM / WGM, WTN = BN / WGN;
     constexpr int TM = WTM / 32, TN = WTN / 32;
     static_assert(TM * 32 == WTM && TN * 32 == WTN, "32x32 MFMA tiles");
-    constexpr int HCAP = (TH + kKEmax - 1) * (TW + kKEmax - 1);  // halo pixels per buffer
-    constexpr int A_UNITS = BM * 4;                              // 16-byte units per weight stage
-    constexpr int H_UNITS = HCAP * kHP;                          // 16-byte units per halo buffer
-    constexpr int AV = A_UNITS / NT;
-    static_assert(AV * NT == A_UNITS, "weight stage splits evenly");
-    constexpr int HV = (HCAP * 4 + NT - 1) / NT;
-    constexpr int PIPE_UNITS = 2 * A_UNITS + 2 * H_UNITS;
-    constexpr int ERS = BM * 2 + 16;  // epilogue LDS row stride in bytes (one pixel)
-    constexpr int EPW0 = (PIPE_UNITS * 16 / ERS) / WTN;  // wave columns that fit one pass
-    constexpr int EPW = largest_divisor_upto(WGN, EPW0);
-    static_assert(EPW >= 1 && WGN % EPW == 0, "epilogue pass fits LDS");
-    constexpr int NPASS = WGN / EPW;
-    __shared__ uint4 lds[PIPE_UNITS];
-    __shared__ __align__(16) float sbias[BM];  // this tile's bias, read by the epilogue
-    uint4* const abuf = lds;                // [2][A_UNITS]
-    uint4* const hbuf = lds + 2 * A_UNITS;  // [2][H_UNITS]
+    constexpr int HCAP = (TH + KE - 1) * (TW + KE - 1);          // halo pixels per buffer
+    constexpr int A_BYTES = BM * kBK * 2;                        // one weight slot
+    constexpr int H_BYTES = HCAP * kHP * 16;                     // one halo buffer
+    constexpr int AV = BM * 4 / NT;                              // weight loads per thread per step
+    static_assert(AV * NT == BM * 4 && AV >= 1, "weight slice splits evenly");
+    constexpr int NPMAX = (HCAP * 4 + NT - 1) / NT;              // halo parts per chunk, at most
+    constexpr int B_BYTES = BIAS ? BM * 4 : 0;                   // one tile's bias
+    // LDS: weight ring | two halo buffers | two bias buffers (current tile,
+    // next tile)
+    __shared__ uint4 lds[(kRing * A_BYTES + 2 * H_BYTES + 2 * B_BYTES) / 16];
+    char* const ring = reinterpret_cast<char*>(lds);
+    char* const halo = ring + kRing * A_BYTES;
+    char* const sbias = halo + 2 * H_BYTES;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WGN, wn = wave % WGN;
 
-    int tile = xcd_tile_index();
-    const int ct = tile % n_ctiles;  // output-channel tile (fastest)
-    tile /= n_ctiles;
-    const int g = tile % s.groups;
-    tile /= s.groups;
-    const int tw = tile % tiles_w;   // pixel blocks in row-major order over each image
-    tile /= tiles_w;
-    const int th = tile % tiles_h;
-    const int n = tile / tiles_h;
-    const int ho0 = th * TH, wo0 = tw * TW;
-    const int HH = TH + (s.Kh - 1) * s.dil;   // halo window extent (stride 1)
-    const int HWd = TW + (s.Kw - 1) * s.dil;
+    // This workgroup's tiles: first, first + G, ... (the first index is
+    // XCD-aware, so each XCD's L2 sees one run of neighbouring tiles).
+    const int G = gridDim.x;
+    const int first = xcd_tile_index();
+    if (first >= hg.ntiles) return;
+    const int nmine = (hg.ntiles - 1 - first) / G + 1;
     const int KK = s.Kh * s.Kw;
     const int nchunk = (s.cin_g + kBK - 1) / kBK;
-    const int co_tile = ct * BM;
+    const int total = nmine * nchunk * KK;  // K-steps of this workgroup
+    const int HWd = TW + (s.Kw - 1) * s.dil;  // halo window width
+    const int hunits = (TH + (s.Kh - 1) * s.dil) * HWd * 4;
+    const int tap_row = s.dil * HWd * (kHP * 16);  // LDS bytes between taps kh and kh+1
+    const int tap_col = s.dil * (kHP * 16);
+    const int wrow = KK * s.cin_g * 2;               // bytes of one packed weight row
 
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)s.N * s.H * s.W * s.Cin * 2u);
-    const __amdgpu_buffer_rsrc_t wr = make_rsrc(wp, (uint32_t)s.Cout * KK * s.cin_g * 2u);
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(wp, (uint32_t)s.Cout * (uint32_t)wrow);
+    const __amdgpu_buffer_rsrc_t yr = make_rsrc(y, (uint32_t)s.N * s.Ho * s.Wo * s.Cout * 2u);
+    const __amdgpu_buffer_rsrc_t br = make_rsrc(bias, BIAS ? (uint32_t)s.Cout * 4u : 0u);
 
-    // ---- weight (A) slots: row = output channel, 4 chunks of 8 channels;
-    // byte offset of (tap 0, chunk 0), or past the end for a missing channel
-    int a_off[AV], a_c[AV], a_lds[AV];
+    // ---- weight slots: row = output channel within the tile, 4 chunks of 8
+    int a_row[AV], a_c[AV], a_lds[AV];
 #pragma unroll
     for (int i = 0; i < AV; ++i) {
         const int q = tid + i * NT;
-        const int row = q >> 2, ch = q & 3;
-        const int co = co_tile + row;
-        const bool ok = co < s.cout_g;
-        a_off[i] = ok ? ((g * s.cout_g + co) * KK * s.cin_g + ch * 8) * 2 : kOOB;
-        a_c[i] = ch * 8;
-        a_lds[i] = swz<kBK>(row, ch);
-    }
-    // ---- halo (B) slots: window pixel hp, chunk ch; byte offset of the
-    // pixel's channel block of chunk 0, or past the end outside the image
-    int h_off[HV], h_c[HV], h_lds[HV];
-    const int hunits = HH * HWd * 4;
-#pragma unroll
-    for (int k = 0; k < HV; ++k) {
-        const int v = tid + k * NT;
-        const int hp = v >> 2, ch = v & 3;
-        const int hr = hp / HWd, hc = hp - hr * HWd;
-        const int hi = ho0 - s.pad + hr, wi = wo0 - s.pad + hc;
-        const bool in = v < hunits && (unsigned)hi < (unsigned)s.H && (unsigned)wi < (unsigned)s.W;
-        h_off[k] = in ? (((n * s.H + hi) * s.W + wi) * s.Cin + g * s.cin_g + ch * 8) * 2 : kOOB;
-        h_c[k] = ch * 8;
-        h_lds[k] = v < hunits ? hp * kHP + ch : -1;
+        a_row[i] = q >> 2;
+        a_c[i] = (q & 3) * 8;
+        a_lds[i] = swz<kBK>(q >> 2, q & 3) * 16;
     }
     // ---- MFMA operand reads: lane supplies row (lane % 32), K values
     // 8*(lane/32).. of each 16-wide K slice (chunks 2*ks, 2*ks+1 of a row)
@@ -151,9 +181,100 @@ __global__ __launch_bounds__(NT) void halo_kernel(const bf16_t* __restrict__ x,
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
         const int p = wn * WTN + j * 32 + frow;
-        const int r = p / TW, cc = p - r * TW;
-        b_rd[j] = ((r * HWd + cc) * kHP + fch) * 16;
+        b_rd[j] = (((p / TW) * HWd + p % TW) * kHP + fch) * 16;
     }
+
+    // Weight loads of K-step (tile coordinates T, chunk C, tap TP): the
+    // per-lane offset holds the row (or lies past the end for a row beyond
+    // this group's channels); tap and chunk ride in the scalar offset.
+#define A_LOAD(RA, RB, CT0, C, TP)                                                           \
+    do {                                                                                     \
+        _Pragma("unroll") for (int i = 0; i < AV; ++i) {                                     \
+            const bool ok_ = (CT0) + a_row[i] < s.cout_g &&                                  \
+                             (CFULL || (C) * kBK + a_c[i] < s.cin_g);                        \
+            (RA)[i] = load16(wr, ok_ ? (RB) + a_row[i] * wrow + a_c[i] * 2 : kOOB,           \
+                             __builtin_amdgcn_readfirstlane(((TP) * s.cin_g + (C) * kBK) * 2)); \
+        }                                                                                    \
+    } while (0)
+#define A_STORE(RA, SLOT)                                                                    \
+    do {                                                                                     \
+        _Pragma("unroll") for (int i = 0; i < AV; ++i)                                       \
+            *reinterpret_cast<uint4*>(ring + (SLOT) * A_BYTES + a_lds[i]) = (RA)[i];         \
+    } while (0)
+    // Halo part U of chunk C of the tile at image N, origin (HO0, WO0), group
+    // GG (VALID false: a load that returns 0): window unit v = tid + U*NT is
+    // (pixel v/4, channel block v%4).  HL: LDS byte offset of the destination
+    // in halo buffer HB (-1: nothing to store).
+#define H_LOAD(RH, HL, N, GG, HO0, WO0, C, U, VALID, HB)                                     \
+    do {                                                                                     \
+        const int v_ = tid + (U) * NT;                                                       \
+        const int hp_ = v_ >> 2, hch_ = v_ & 3;                                              \
+        const int hr_ = (hp_ * hg.hwd_magic) >> 16;                                          \
+        const int hi_ = (HO0) - s.pad + hr_, wi_ = (WO0) - s.pad + hp_ - hr_ * HWd;          \
+        const bool in_ = (VALID) && v_ < hunits;                                             \
+        const bool ok_ = in_ && (unsigned)hi_ < (unsigned)s.H && (unsigned)wi_ < (unsigned)s.W && \
+                         (CFULL || (C) * kBK + hch_ * 8 < s.cin_g);                          \
+        (RH) = load16(xr, ok_ ? (((N) * s.H + hi_) * s.W + wi_) * s.Cin * 2 +                \
+                                    ((GG) * s.cin_g + hch_ * 8) * 2 : kOOB,                  \
+                      __builtin_amdgcn_readfirstlane((C) * kBK * 2));                        \
+        (HL) = in_ ? kRing * A_BYTES + (HB) * H_BYTES + (hp_ * kHP + hch_) * 16 : -1;        \
+    } while (0)
+    // The bias of the tile at (group GG, channel tile CT) into bias buffer BB:
+    // four channels per thread.
+#define B_LOAD(RH, HL, GG, CT, VALID, BB)                                                    \
+    do {                                                                                     \
+        const bool in_ = (VALID) && tid * 4 < BM;                                            \
+        (RH) = load16(br, in_ ? ((GG) * s.cout_g + (CT) * BM + tid * 4) * 4 : kOOB);         \
+        (HL) = in_ ? kRing * A_BYTES + 2 * H_BYTES + (BB) * B_BYTES + tid * 16 : -1;         \
+    } while (0)
+    // The piece loaded at tap t of a chunk: halo part t of the next chunk for
+    // t < nparts; at t == nparts of a tile's last chunk, the next tile's bias;
+    // else a load that returns 0 and is not stored.  Every step issues the
+    // same number of loads.
+#define PIECE_LOAD(RH, HL)                                                                   \
+    do {                                                                                     \
+        if (BIAS && t == hg.nparts && c + 1 == nchunk)                                       \
+            B_LOAD(RH, HL, tn.g, tn.ct, k + 1 < nmine, (k + 1) & 1);                         \
+        else                                                                                 \
+            H_LOAD(RH, HL, h_n, h_g, h_ho0, h_wo0, h_c, t, h_ok && t < hg.nparts, hsel ^ 1); \
+    } while (0)
+
+    // ---- cursors (all wave-uniform; updated with scalar selects only, so
+    // the load section of a step has no branch)
+    int k = 0;                                       // tile iteration of the current step
+    TileXY tc = tile_xy<TH, TW>(first, hg, s.groups);  // current tile
+    TileXY tn = tile_xy<TH, TW>(nmine > 1 ? first + G : first, hg, s.groups);  // next tile
+    int c = 0, t = 0, kh = 0, kw = 0;                // chunk and tap of the current step
+    int hsel = 0;                                    // halo buffer of the current chunk
+    int r0 = 0;                                      // ring slot of the current step
+    // weight-load cursor: step + 3 (chunk, tap, row base and first channel of its tile)
+    int ac = 0, at = 0;
+    int a_rb = (tc.g * s.cout_g + tc.ct * BM) * wrow, a_ct = tc.ct * BM;
+    for (int adv = 0; adv < 3; ++adv) {
+        if (++at == KK) {
+            at = 0;
+            if (++ac == nchunk) {
+                ac = 0;
+                a_rb = (tn.g * s.cout_g + tn.ct * BM) * wrow;
+                a_ct = tn.ct * BM;
+            }
+        }
+    }
+    // halo-load cursor: the chunk after the current one (its tile's image,
+    // group, origin; false past the last tile)
+    int h_n, h_g, h_ho0, h_wo0, h_c;
+    bool h_ok;
+#define HALO_NEXT_CHUNK()                                                                    \
+    do {                                                                                     \
+        const bool same_ = c + 1 < nchunk;                                                   \
+        h_n = same_ ? tc.n : tn.n;                                                           \
+        h_g = same_ ? tc.g : tn.g;                                                           \
+        h_ho0 = same_ ? tc.ho0 : tn.ho0;                                                     \
+        h_wo0 = same_ ? tc.wo0 : tn.wo0;                                                     \
+        h_c = same_ ? c + 1 : 0;                                                             \
+        h_ok = same_ || k + 1 < nmine;                                                       \
+    } while (0)
+    HALO_NEXT_CHUNK();
 
     f32x16 acc[TM][TN];
 #pragma unroll
@@ -161,213 +282,691 @@ __global__ __launch_bounds__(NT) void halo_kernel(const bf16_t* __restrict__ x,
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
 
-    uint4 ra[AV], rh[HV];
-    // With Cin/G a multiple of 32 every chunk is full: the offsets need no
-    // per-lane check and the step's offset rides in the scalar field.
-#define HALO_LOAD(CH)                                                                        \
-    do {                                                                                     \
-        _Pragma("unroll") for (int k = 0; k < HV; ++k) {                                     \
-            if (CFULL) {                                                                     \
-                rh[k] = load16(xr, h_off[k], (CH) * kBK * 2);                                \
-            } else {                                                                         \
-                const bool ok = (CH) * kBK + h_c[k] < s.cin_g;                               \
-                rh[k] = load16(xr, ok ? h_off[k] : kOOB, (CH) * kBK * 2);                    \
-            }                                                                                \
-        }                                                                                    \
-    } while (0)
-#define HALO_STORE(BUF)                                                                      \
-    do {                                                                                     \
-        _Pragma("unroll") for (int k = 0; k < HV; ++k)                                       \
-            if (h_lds[k] >= 0) hbuf[(BUF) * H_UNITS + h_lds[k]] = rh[k];                     \
-    } while (0)
-#define A_LOAD(CH, TAP)                                                                      \
-    do {                                                                                     \
-        _Pragma("unroll") for (int i = 0; i < AV; ++i) {                                     \
-            if (CFULL) {                                                                     \
-                ra[i] = load16(wr, a_off[i], ((TAP) * s.cin_g + (CH) * kBK) * 2);            \
-            } else {                                                                         \
-                const bool ok = (CH) * kBK + a_c[i] < s.cin_g;                               \
-                ra[i] = load16(wr, ok ? a_off[i] : kOOB, ((TAP) * s.cin_g + (CH) * kBK) * 2); \
-            }                                                                                \
-        }                                                                                    \
-    } while (0)
-#define A_STORE(BUF)                                                                         \
-    do {                                                                                     \
-        _Pragma("unroll") for (int i = 0; i < AV; ++i) abuf[(BUF) * A_UNITS + a_lds[i]] = ra[i]; \
-    } while (0)
+    uint4 ra0[AV], ra1[AV], rh0, rh1;
+    int hl0 = -1, hl1 = -1;
+    bf16x8 af0[TM], bf0[TN], af1[TM], bf1[TN];
 
-    HALO_LOAD(0);
-    A_LOAD(0, 0);
-    if (BIAS) {
-        // stage the tile's bias once (visible after the barrier below)
-        for (int i = tid; i < BM; i += NT)
-            sbias[i] = co_tile + i < s.cout_g ? bias[g * s.cout_g + co_tile + i] : 0.0f;
+    // ---- prologue: weight steps 0 and 1 and the first chunk's halo in LDS,
+    // step 2's weights in flight (ra0), the first slice's operands read.
+    // Steps 0..2 lie in the first tile: the host admits only Kh*Kw >= 3.
+    {
+        const int c1 = 1 / KK, t1 = 1 - c1 * KK;
+        const int c2 = 2 / KK, t2 = 2 - c2 * KK;
+        uint4 p0[AV], p1[AV], ph[NPMAX];
+        int pl[NPMAX];
+        const int rb0 = (tc.g * s.cout_g + tc.ct * BM) * wrow;
+        A_LOAD(p0, rb0, tc.ct * BM, 0, 0);
+        A_LOAD(p1, rb0, tc.ct * BM, c1, t1);
+#pragma unroll
+        for (int u = 0; u < NPMAX; ++u)
+            H_LOAD(ph[u], pl[u], tc.n, tc.g, tc.ho0, tc.wo0, 0, u, u < hg.nparts, 0);
+        uint4 pb;
+        int pbl = -1;
+        if (BIAS) B_LOAD(pb, pbl, tc.g, tc.ct, true, 0);
+        A_LOAD(ra0, rb0, tc.ct * BM, c2, t2);
+        A_STORE(p0, 0);
+        A_STORE(p1, 1);
+#pragma unroll
+        for (int u = 0; u < NPMAX; ++u)
+            if (pl[u] >= 0) *reinterpret_cast<uint4*>(ring + pl[u]) = ph[u];
+        if (BIAS && pbl >= 0) *reinterpret_cast<uint4*>(ring + pbl) = pb;
     }
-    HALO_STORE(0);
-    A_STORE(0);
     __syncthreads();
+#pragma unroll
+    for (int i = 0; i < TM; ++i) af0[i] = *reinterpret_cast<const bf16x8*>(ring + a_rd[0][i]);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) bf0[j] = *reinterpret_cast<const bf16x8*>(halo + b_rd[j]);
 
-    // K loop: chunk outer, tap (kh, kw) inner.  Past the last step the weight
-    // prefetch reads harmless in-range or zero data that is never used.
-    int st = 0;
-    for (int c = 0; c < nchunk; ++c) {
-        const char* hcur = reinterpret_cast<const char*>(hbuf + (c & 1) * H_UNITS);
-        int t = 0;
-        for (int kh = 0; kh < s.Kh; ++kh) {
-            for (int kw = 0; kw < s.Kw; ++kw, ++t, ++st) {
-                const bool last_tap = t + 1 == KK;
-                // Halo loads go out before the weight loads of the same step:
-                // loads complete in order, so the wait for the weights also
-                // covers them.  The next chunk's halo has the whole chunk to
-                // arrive and is stored at its last tap.
-                if (t == 0 && c + 1 < nchunk) HALO_LOAD(c + 1);
-                if (last_tap) A_LOAD(c + 1, 0);
-                else A_LOAD(c, t + 1);
-                // keep the loads a full step ahead of their LDS stores
-                __builtin_amdgcn_sched_barrier(0);
-                const char* acur = reinterpret_cast<const char*>(abuf + (st & 1) * A_UNITS);
-                const char* hb = hcur + (kh * s.dil * HWd + kw * s.dil) * (kHP * 16);
-                // Both K slices' operands are requested before any matrix
-                // op, so the second slice's LDS reads overlap the first
-                // slice's MFMAs.
-                bf16x8 af[2][TM], bfr[2][TN];
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-                    for (int i = 0; i < TM; ++i)
-                        af[ks][i] = *reinterpret_cast<const bf16x8*>(acur + a_rd[ks][i]);
-#pragma unroll
-                    for (int j = 0; j < TN; ++j)
-                        bfr[ks][j] = *reinterpret_cast<const bf16x8*>(hb + b_rd[j] + ks * 32);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-                    for (int i = 0; i < TM; ++i)
-#pragma unroll
-                        for (int j = 0; j < TN; ++j)
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks][i], bfr[ks][j], acc[i][j], 0, 0, 0);
-                A_STORE((st + 1) & 1);
-                if (last_tap && c + 1 < nchunk) HALO_STORE((c + 1) & 1);
-                __syncthreads();
-            }
-        }
+    // Epilogue of the current tile (tc): bias, ReLU, bf16; lane l < 32 of a
+    // 32x32 block holds channels 8q+r (q = 0..3, r = 0..3) of pixel l, lane
+    // l + 32 channels 8q+4+r; one v_permlane32_swap per pair of q gives each
+    // lane 8 consecutive channels (16 bytes) of one pixel.
+    const int half = lane >> 5;
+    const bool vec16 = (s.Cout % 8 == 0) && (s.cout_g % 8 == 0);
+#define HALO_EPILOGUE()                                                                      \
+    do {                                                                                     \
+        int pix_[TN];                                                                        \
+        _Pragma("unroll") for (int j = 0; j < TN; ++j) {                                     \
+            const int p_ = wn * WTN + j * 32 + (lane & 31);                                  \
+            const int ho_ = tc.ho0 + p_ / TW, wo_ = tc.wo0 + p_ % TW;                        \
+            pix_[j] = (ho_ < s.Ho && wo_ < s.Wo) ? ((tc.n * s.Ho + ho_) * s.Wo + wo_) * s.Cout : -1; \
+        }                                                                                    \
+        const int cw_ = tc.ct * BM + wm * WTM;  /* first channel (within the group) of the wave */ \
+        _Pragma("unroll") for (int i = 0; i < TM; ++i) {                                     \
+            float4 b4_[4];                                                                   \
+            _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                  \
+                b4_[q] = make_float4(0.f, 0.f, 0.f, 0.f);                                    \
+                if (BIAS)                                                                    \
+                    b4_[q] = *reinterpret_cast<const float4*>(                               \
+                        sbias + (k & 1) * B_BYTES + (wm * WTM + i * 32 + 8 * q + 4 * half) * 4); \
+            }                                                                                \
+            _Pragma("unroll") for (int j = 0; j < TN; ++j) {                                 \
+                uint32_t pk_[4][2];                                                          \
+                _Pragma("unroll") for (int q = 0; q < 4; ++q) {                              \
+                    float v_[4];                                                             \
+                    _Pragma("unroll") for (int r = 0; r < 4; ++r) {                          \
+                        v_[r] = acc[i][j][4 * q + r] + (&b4_[q].x)[r];                       \
+                        if (RELU) v_[r] = fmaxf(v_[r], 0.0f);                                \
+                    }                                                                        \
+                    pk_[q][0] = pack_bf16x2(v_[0], v_[1]);                                   \
+                    pk_[q][1] = pack_bf16x2(v_[2], v_[3]);                                   \
+                }                                                                            \
+                _Pragma("unroll") for (int pr = 0; pr < 2; ++pr) {                           \
+                    uint32_t lo_[2], hi_[2];                                                 \
+                    _Pragma("unroll") for (int w = 0; w < 2; ++w) {                          \
+                        const auto sw_ = __builtin_amdgcn_permlane32_swap(                   \
+                            pk_[2 * pr][w], pk_[2 * pr + 1][w], false, false);               \
+                        lo_[w] = sw_[0];                                                     \
+                        hi_[w] = sw_[1];                                                     \
+                    }                                                                        \
+                    /* out-of-range pixels and channels get an offset past  \
+                       the end: the buffer store drops them */               \
+                    const int co_ = cw_ + i * 32 + 16 * pr + 8 * half;                       \
+                    const int off_ = (pix_[j] + tc.g * s.cout_g + co_) * 2;                  \
+                    if (vec16) {                                                             \
+                        store16(yr, pix_[j] >= 0 && co_ < s.cout_g ? off_ : kOOB,            \
+                                make_uint4(lo_[0], lo_[1], hi_[0], hi_[1]));                 \
+                    } else {                                                                 \
+                        store8(yr, pix_[j] >= 0 && co_ < s.cout_g ? off_ : kOOB,             \
+                               make_uint2(lo_[0], lo_[1]));                                  \
+                        store8(yr, pix_[j] >= 0 && co_ + 4 < s.cout_g ? off_ + 8 : kOOB,     \
+                               make_uint2(hi_[0], hi_[1]));                                  \
+                    }                                                                        \
+                }                                                                            \
+            }                                                                                \
+        }                                                                                    \
+    } while (0)
+
+    // One K-step.  RA_LD/RA_ST: weight registers loaded now (for step + 3) /
+    // stored now (step + 2, loaded one step ago); RH_LD/HL_LD, RH_ST/HL_ST:
+    // the same for the halo piece.
+#define HALO_STEP(RA_LD, RA_ST, RH_LD, HL_LD, RH_ST, HL_ST)                                  \
+    do {                                                                                     \
+        /* (1) loads: weights of step + 3, halo part t of the next chunk */                  \
+        A_LOAD(RA_LD, a_rb, a_ct, ac, at);                                                   \
+        PIECE_LOAD(RH_LD, HL_LD);                                                            \
+        __builtin_amdgcn_sched_barrier(0);                                                   \
+        /* (2) second slice's operands; first slice's matrix ops */                          \
+        const char* acur_ = ring + r0 * A_BYTES;                                             \
+        const char* hcur_ = halo + hsel * H_BYTES + kh * tap_row + kw * tap_col;             \
+        _Pragma("unroll") for (int i = 0; i < TM; ++i)                                       \
+            af1[i] = *reinterpret_cast<const bf16x8*>(acur_ + a_rd[1][i]);                   \
+        _Pragma("unroll") for (int j = 0; j < TN; ++j)                                       \
+            bf1[j] = *reinterpret_cast<const bf16x8*>(hcur_ + b_rd[j] + 32);                 \
+        __builtin_amdgcn_sched_barrier(0);                                                   \
+        _Pragma("unroll") for (int i = 0; i < TM; ++i)                                       \
+            _Pragma("unroll") for (int j = 0; j < TN; ++j)                                   \
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af0[i], bf0[j], acc[i][j], 0, 0, 0); \
+        /* (3) next step's first-slice operands; second slice's matrix ops */                \
+        const int r1_ = r0 == kRing - 1 ? 0 : r0 + 1;                                        \
+        const char* anext_ = ring + r1_ * A_BYTES;                                           \
+        const char* hnext_;                                                                  \
+        if (t + 1 < KK) {                                                                    \
+            const int nkw_ = kw + 1 == s.Kw ? 0 : kw + 1;                                    \
+            const int nkh_ = kw + 1 == s.Kw ? kh + 1 : kh;                                   \
+            hnext_ = halo + hsel * H_BYTES + nkh_ * tap_row + nkw_ * tap_col;                \
+        } else {                                                                             \
+            hnext_ = halo + (hsel ^ 1) * H_BYTES;                                            \
+        }                                                                                    \
+        _Pragma("unroll") for (int i = 0; i < TM; ++i)                                       \
+            af0[i] = *reinterpret_cast<const bf16x8*>(anext_ + a_rd[0][i]);                  \
+        _Pragma("unroll") for (int j = 0; j < TN; ++j)                                       \
+            bf0[j] = *reinterpret_cast<const bf16x8*>(hnext_ + b_rd[j]);                     \
+        _Pragma("unroll") for (int i = 0; i < TM; ++i)                                       \
+            _Pragma("unroll") for (int j = 0; j < TN; ++j)                                   \
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af1[i], bf1[j], acc[i][j], 0, 0, 0); \
+        __builtin_amdgcn_sched_barrier(0);                                                   \
+        /* (4) LDS stores: weights of step + 2; the piece loaded last step (none  \
+           at a chunk's first tap: the last tap loads nothing) */                            \
+        A_STORE(RA_ST, r1_ == kRing - 1 ? 0 : r1_ + 1);                                      \
+        if ((HL_ST) >= 0) *reinterpret_cast<uint4*>(ring + (HL_ST)) = (RH_ST);               \
+        /* (5) a tile's last step: epilogue, then the next tile */                           \
+        if (t + 1 == KK && c + 1 == nchunk) {                                                \
+            HALO_EPILOGUE();                                                                 \
+            _Pragma("unroll") for (int i = 0; i < TM; ++i)                                   \
+                _Pragma("unroll") for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};         \
+            ++k;                                                                             \
+            tc = tn;                                                                         \
+            tn = tile_xy<TH, TW>(k + 1 < nmine ? first + (k + 1) * G : first, hg, s.groups); \
+        }                                                                                    \
+        __syncthreads();                                                                     \
+        /* (6) advance the cursors */                                                        \
+        r0 = r1_;                                                                            \
+        if (++kw == s.Kw) { kw = 0; ++kh; }                                                  \
+        if (++t == KK) {                                                                     \
+            t = 0; kh = 0; kw = 0; hsel ^= 1;                                                \
+            if (++c == nchunk) c = 0;                                                        \
+            HALO_NEXT_CHUNK();                                                               \
+        }                                                                                    \
+        if (++at == KK) {                                                                    \
+            at = 0;                                                                          \
+            if (++ac == nchunk) {                                                            \
+                /* the weight cursor enters the tile after the current one */                \
+                ac = 0;                                                                      \
+                a_rb = (tn.g * s.cout_g + tn.ct * BM) * wrow;                                \
+                a_ct = tn.ct * BM;                                                           \
+            }                                                                                \
+        }                                                                                    \
+    } while (0)
+
+    // Two steps per iteration so the two register sets alternate statically.
+    // An odd step count runs one extra step past the end: its loads read
+    // zeros or in-range weights, its results are never stored.
+    for (int st = 0; st < total; st += 2) {
+        HALO_STEP(ra1, ra0, rh0, hl0, rh1, hl1);
+        HALO_STEP(ra0, ra1, rh1, hl1, rh0, hl0);
     }
-#undef HALO_LOAD
-#undef HALO_STORE
+#undef HALO_STEP
+#undef HALO_EPILOGUE
 #undef A_LOAD
 #undef A_STORE
+#undef H_LOAD
+#undef B_LOAD
+#undef PIECE_LOAD
+#undef HALO_NEXT_CHUNK
+}
 
-    // ---- epilogue: bias, ReLU, bf16 in registers; staged through LDS as
-    // [pixel][channel] rows in NPASS passes over the wave columns, then each
-    // pixel's channels leave as contiguous 16-byte stores.
-    // 32x32 result layout: lane l holds D[8*q + 4*(l/32) + r][l % 32] in
-    // acc[4*q + r]: four runs of four consecutive channels of one pixel.
-    char* ep = reinterpret_cast<char*>(lds);
+// Epilogue of one tile from registers: bias, ReLU, bf16; lane l < 32 of a
+// 32x32 block holds channels 8q+r (q = 0..3, r = 0..3) of pixel l, lane
+// l + 32 channels 8q+4+r; one v_permlane32_swap per pair of q gives each
+// lane 8 consecutive channels (16 bytes) of one pixel, stored with one
+// buffer store (offset past the end for pixels and channels outside the
+// output: the store is dropped).
+template <int TM, int TN, int WTM, int WTN, int TH, int TW, bool BIAS, bool RELU>
+__device__ __forceinline__ void tile_epilogue(f32x16 (&acc)[TM][TN], const char* sb,
+                                              __amdgpu_buffer_rsrc_t yr, const Shape& s,
+                                              const TileXY& tc, int co0, int wm, int wn, int lane) {
+    const int half = lane >> 5;
     const bool vec16 = (s.Cout % 8 == 0) && (s.cout_g % 8 == 0);
-    constexpr int RCH = BM / 8;
-    constexpr int PPX = EPW * WTN;  // pixels per pass
-#pragma unroll 1
-    for (int pass = 0; pass < NPASS; ++pass) {
-        if (wn / EPW == pass) {
+    int pix[TN];
 #pragma unroll
-            for (int i = 0; i < TM; ++i) {
+    for (int j = 0; j < TN; ++j) {
+        const int p = wn * WTN + j * 32 + (lane & 31);
+        const int ho = tc.ho0 + p / TW, wo = tc.wo0 + p % TW;
+        pix[j] = (ho < s.Ho && wo < s.Wo) ? ((tc.n * s.Ho + ho) * s.Wo + wo) * s.Cout : -1;
+    }
+    const int cw = co0 + wm * WTM;  // first channel (within the group) of the wave's rows
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int col = wm * WTM + i * 32 + 8 * q + 4 * (lane >> 5);
-                    const int co = co_tile + col;
-                    float4 b4 = make_float4(0.f, 0.f, 0.f, 0.f);
-                    if (BIAS) b4 = *reinterpret_cast<const float4*>(&sbias[col]);
-                    (void)co;
+    for (int i = 0; i < TM; ++i) {
+        float4 b4[4];
 #pragma unroll
-                    for (int j = 0; j < TN; ++j) {
-                        const int row = (wn % EPW) * WTN + j * 32 + (lane & 31);
-                        float v[4];
+        for (int q = 0; q < 4; ++q) {
+            b4[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (BIAS) b4[q] = *reinterpret_cast<const float4*>(sb + (wm * WTM + i * 32 + 8 * q + 4 * half) * 4);
+        }
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            v[r] = acc[i][j][4 * q + r] + (&b4.x)[r];
-                            if (RELU) v[r] = fmaxf(v[r], 0.0f);
-                        }
-                        *reinterpret_cast<uint2*>(ep + row * ERS + col * 2) =
-                            make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-                    }
+        for (int j = 0; j < TN; ++j) {
+            uint32_t pk[4][2];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float v[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    v[r] = acc[i][j][4 * q + r] + (&b4[q].x)[r];
+                    if (RELU) v[r] = fmaxf(v[r], 0.0f);
+                }
+                pk[q][0] = pack_bf16x2(v[0], v[1]);
+                pk[q][1] = pack_bf16x2(v[2], v[3]);
+            }
+#pragma unroll
+            for (int pr = 0; pr < 2; ++pr) {
+                uint32_t lo[2], hi[2];
+#pragma unroll
+                for (int w = 0; w < 2; ++w) {
+                    const auto sw = __builtin_amdgcn_permlane32_swap(pk[2 * pr][w], pk[2 * pr + 1][w], false, false);
+                    lo[w] = sw[0];
+                    hi[w] = sw[1];
+                }
+                const int co = cw + i * 32 + 16 * pr + 8 * half;
+                const int off = (pix[j] + tc.g * s.cout_g + co) * 2;
+                if (vec16) {
+                    store16(yr, pix[j] >= 0 && co < s.cout_g ? off : kOOB, make_uint4(lo[0], lo[1], hi[0], hi[1]));
+                } else {
+                    store8(yr, pix[j] >= 0 && co < s.cout_g ? off : kOOB, make_uint2(lo[0], lo[1]));
+                    store8(yr, pix[j] >= 0 && co + 4 < s.cout_g ? off + 8 : kOOB, make_uint2(hi[0], hi[1]));
                 }
             }
         }
-        __syncthreads();
-        for (int q = tid; q < PPX * RCH; q += NT) {
-            const int row = q / RCH, cch = q - row * RCH;
-            const int p = pass * PPX + row;
-            const int r = p / TW, cc = p - r * TW;
-            const int ho = ho0 + r, wo = wo0 + cc;
-            const int co = co_tile + cch * 8;
-            if (ho >= s.Ho || wo >= s.Wo || co >= s.cout_g) continue;
-            const uint4 v = *reinterpret_cast<const uint4*>(ep + row * ERS + cch * 16);
-            bf16_t* dst = y + ((size_t)(n * s.Ho + ho) * s.Wo + wo) * s.Cout + g * s.cout_g + co;
-            if (vec16 && co + 8 <= s.cout_g) {
-                *reinterpret_cast<uint4*>(dst) = v;
-            } else {
-                *reinterpret_cast<uint2*>(dst) = make_uint2(v.x, v.y);
-                if (co + 8 <= s.cout_g) *reinterpret_cast<uint2*>(dst + 4) = make_uint2(v.z, v.w);
-            }
-        }
-        __syncthreads();
     }
 }
 
-template <int NT, int BM, int TH, int TW, int WGM, int WGN, bool CFULL>
-hipError_t launch_tile(const Shape& s, const bf16_t* x, const bf16_t* w, const float* b, bf16_t* y,
-                       hipStream_t st) {
-    const int tiles_h = (s.Ho + TH - 1) / TH, tiles_w = (s.Wo + TW - 1) / TW;
-    const int n_ctiles = (s.cout_g + BM - 1) / BM;
-    const long long blocks = (long long)s.N * tiles_h * tiles_w * s.groups * n_ctiles;
-    if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    dim3 grid((unsigned)blocks);
-    const bool bias = s.epilogue & CONV2D_EPI_BIAS, relu = s.epilogue & CONV2D_EPI_RELU;
-    if (bias && relu)
-        hipLaunchKernelGGL((halo_kernel<NT, BM, TH, TW, WGM, WGN, CFULL, true, true>), grid, dim3(NT), 0, st, x, w, b, y, s, tiles_h, tiles_w, n_ctiles);
-    else if (bias)
-        hipLaunchKernelGGL((halo_kernel<NT, BM, TH, TW, WGM, WGN, CFULL, true, false>), grid, dim3(NT), 0, st, x, w, b, y, s, tiles_h, tiles_w, n_ctiles);
-    else if (relu)
-        hipLaunchKernelGGL((halo_kernel<NT, BM, TH, TW, WGM, WGN, CFULL, false, true>), grid, dim3(NT), 0, st, x, w, b, y, s, tiles_h, tiles_w, n_ctiles);
-    else
-        hipLaunchKernelGGL((halo_kernel<NT, BM, TH, TW, WGM, WGN, CFULL, false, false>), grid, dim3(NT), 0, st, x, w, b, y, s, tiles_h, tiles_w, n_ctiles);
+// 3x3 filters with dilation DIL (1 or 2): the same schedule as halo_kernel,
+// with the nine taps of a chunk unrolled at compile time.  Ring slots, tap
+// offsets and every LDS operand address are immediates; load offsets are
+// computed once per chunk; a K-step issues little besides its global loads,
+// LDS reads, matrix ops and LDS stores.  Per step (tap t of a chunk):
+//  * weights of step + 3 are loaded into register set t % 3 and stored one
+//    step later into ring slot (t + 2) % 3 (the slot read three steps later),
+//  * at taps 0 .. NPS-1 two 16-byte pieces per thread of the next chunk's
+//    halo window are loaded (stored one step later); at tap NPS of a tile's
+//    last chunk, the next tile's bias,
+//  * the second slice's operands are read, the first slice's matrix ops
+//    issue, the next step's first-slice operands are read, the second
+//    slice's matrix ops issue,
+//  * one barrier.
+template <int NT, int MINB, int BM, int TH, int TW, int WGM, int WGN, int DIL, bool CFULL, bool BIAS, bool RELU>
+__global__ __launch_bounds__(NT, waves_per_simd(NT, MINB, halo_lds_bytes(BM, TH, TW, 2 * DIL + 1, BIAS)))
+void halo3_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ wp, const float* __restrict__ bias,
+                  bf16_t* __restrict__ y, Shape s, HaloGrid hg) {
+    constexpr int BN = TH * TW;
+    static_assert(WGM * WGN * 64 == NT, "one wave per sub-tile");
+    constexpr int WTM = BM / WGM, WTN = BN / WGN;
+    constexpr int TM = WTM / 32, TN = WTN / 32;
+    static_assert(TM * 32 == WTM && TN * 32 == WTN, "32x32 MFMA tiles");
+    static_assert(32 % TW == 0 || TW % 32 == 0, "32-pixel MFMA tiles cover whole block rows");
+    constexpr int HWd = TW + 2 * DIL, HH = TH + 2 * DIL;  // halo window
+    constexpr int HUNITS = HH * HWd * 4;                   // its 16-byte units per chunk
+    constexpr int A_BYTES = BM * kBK * 2;
+    constexpr int H_BYTES = HH * HWd * kHP * 16;
+    constexpr int B_BYTES = BIAS ? BM * 4 : 0;
+    constexpr int AV = BM * 4 / NT;
+    static_assert(AV * NT == BM * 4 && AV >= 1, "weight slice splits evenly");
+    constexpr int PPS = 2;                                 // halo pieces per loading step
+    constexpr int NPS = ((HUNITS + NT - 1) / NT + PPS - 1) / PPS;  // steps that load halo pieces
+    static_assert(NPS + 1 <= 7, "halo pieces land two taps before the chunk's last");
+    // LDS distance between MFMA column blocks j and j + 1 (32 pixels)
+    constexpr int JSTRIDE = TW <= 32 ? (32 / TW) * HWd * kHP * 16 : 32 * kHP * 16;
+    __shared__ uint4 lds[(kRing * A_BYTES + 2 * H_BYTES + 2 * B_BYTES) / 16];
+    char* const ring = reinterpret_cast<char*>(lds);
+    char* const halo = ring + kRing * A_BYTES;
+    char* const sbias = halo + 2 * H_BYTES;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WGN, wn = wave % WGN;
+    const int G = gridDim.x;
+    const int first = xcd_tile_index();
+    if (first >= hg.ntiles) return;
+    const int nmine = (hg.ntiles - 1 - first) / G + 1;
+    const int nchunk = (s.cin_g + kBK - 1) / kBK;
+    const int wrow = 9 * s.cin_g * 2;  // bytes of one packed weight row
+
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)s.N * s.H * s.W * s.Cin * 2u);
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(wp, (uint32_t)s.Cout * (uint32_t)wrow);
+    const __amdgpu_buffer_rsrc_t yr = make_rsrc(y, (uint32_t)s.N * s.Ho * s.Wo * s.Cout * 2u);
+    const __amdgpu_buffer_rsrc_t br = make_rsrc(bias, BIAS ? (uint32_t)s.Cout * 4u : 0u);
+
+    // ---- per-lane constants
+    int a_row[AV], a_c[AV], a_lds[AV];
+#pragma unroll
+    for (int i = 0; i < AV; ++i) {
+        const int q = tid + i * NT;
+        a_row[i] = q >> 2;
+        a_c[i] = (q & 3) * 8;
+        a_lds[i] = swz<kBK>(q >> 2, q & 3) * 16;
+    }
+    const int frow = lane & 31, fch = lane >> 5;
+    // first-slice and second-slice weight operand offsets of MFMA row block 0
+    // (row blocks i are i * 32 rows = i * 2048 bytes further)
+    const int a_rd0 = swz<kBK>(wm * WTM + frow, fch) * 16;
+    const int a_rd1 = swz<kBK>(wm * WTM + frow, 2 + fch) * 16;
+    // pixel operand offset at tap (0, 0) of MFMA column block 0 (block j is
+    // j * JSTRIDE bytes further)
+    const int p0 = wn * WTN + frow;
+    const int b_lane = ((p0 / TW) * HWd + p0 % TW) * (kHP * 16) + fch * 16;
+
+    // weight-load offsets of a tile (row within this group's channels, else past the end)
+    auto a_offsets = [&](const TileXY& T, int* vo) {
+#pragma unroll
+        for (int i = 0; i < AV; ++i) {
+            const int co = T.ct * BM + a_row[i];
+            vo[i] = co < s.cout_g ? ((T.g * s.cout_g + co) * wrow + a_c[i] * 2) : kOOB;
+        }
+    };
+
+    TileXY tc = tile_xy<TH, TW>(first, hg, s.groups);
+    TileXY tn = tile_xy<TH, TW>(nmine > 1 ? first + G : first, hg, s.groups);
+    int k = 0, c = 0, hsel = 0;
+
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
+
+    uint4 ra[3][AV];           // weight register sets (step % 3)
+    uint4 hv[2][PPS];          // halo / bias pieces (tap % 2)
+    int hl[2][PPS];            // their LDS destinations (-1: none)
+    bf16x8 af0[TM], bf0[TN], af1[TM], bf1[TN];
+
+#define A3_LOAD(RA, VO, C, TAP)                                                              \
+    do {                                                                                     \
+        const int so_ = __builtin_amdgcn_readfirstlane(((TAP) * s.cin_g + (C) * kBK) * 2);  \
+        _Pragma("unroll") for (int i = 0; i < AV; ++i) {                                     \
+            const bool ok_ = CFULL || (C) * kBK + a_c[i] < s.cin_g;                          \
+            (RA)[i] = load16(wr, ok_ ? (VO)[i] : kOOB, so_);                                 \
+        }                                                                                    \
+    } while (0)
+#define A3_STORE(RA, SLOT)                                                                   \
+    do {                                                                                     \
+        _Pragma("unroll") for (int i = 0; i < AV; ++i)                                       \
+            *reinterpret_cast<uint4*>(ring + (SLOT) * A_BYTES + a_lds[i]) = (RA)[i];         \
+    } while (0)
+    // halo piece U (window unit tid + U*NT) of chunk C of the tile (N, GG,
+    // HO0, WO0) into halo buffer HB; VALID false or a unit past the window:
+    // a load that returns 0, not stored
+#define H3_LOAD(RH, HL, N, GG, HO0, WO0, C, U, VALID, HB)                                    \
+    do {                                                                                     \
+        const int v_ = tid + (U) * NT;                                                       \
+        const int hp_ = v_ >> 2, hch_ = v_ & 3;                                              \
+        const int hr_ = hp_ / HWd;                                                           \
+        const int hi_ = (HO0) - s.pad + hr_, wi_ = (WO0) - s.pad + hp_ - hr_ * HWd;          \
+        const bool in_ = (VALID) && v_ < HUNITS;                                             \
+        const bool ok_ = in_ && (unsigned)hi_ < (unsigned)s.H && (unsigned)wi_ < (unsigned)s.W && \
+                         (CFULL || (C) * kBK + hch_ * 8 < s.cin_g);                          \
+        (RH) = load16(xr, ok_ ? (((N) * s.H + hi_) * s.W + wi_) * s.Cin * 2 +                \
+                                    ((GG) * s.cin_g + hch_ * 8) * 2 : kOOB,                  \
+                      __builtin_amdgcn_readfirstlane((C) * kBK * 2));                        \
+        (HL) = in_ ? kRing * A_BYTES + (HB) * H_BYTES + (hp_ * kHP + hch_) * 16 : -1;        \
+    } while (0)
+
+    // ---- prologue: weight steps 0, 1 in ring slots 0, 1; step 2's weights in
+    // flight (set 2); the first chunk's halo window and the first tile's bias
+    // in LDS; the first slice's operands of step 0 read
+    int a_vo_c[AV], a_vo_n[AV];  // weight offsets of the current and the next chunk's tile
+    a_offsets(tc, a_vo_c);
+    {
+        uint4 p0r[AV], p1r[AV];
+        A3_LOAD(p0r, a_vo_c, 0, 0);
+        A3_LOAD(p1r, a_vo_c, 0, 1);
+        constexpr int NP = (HUNITS + NT - 1) / NT;
+        uint4 ph[NP];
+        int pl[NP];
+#pragma unroll
+        for (int u = 0; u < NP; ++u) H3_LOAD(ph[u], pl[u], tc.n, tc.g, tc.ho0, tc.wo0, 0, u, true, 0);
+        uint4 pb = make_uint4(0, 0, 0, 0);
+        const bool bin = BIAS && tid * 4 < BM;
+        if (BIAS) pb = load16(br, bin ? ((tc.g * s.cout_g + tc.ct * BM + tid * 4) * 4) : kOOB);
+        A3_LOAD(ra[2], a_vo_c, 0, 2);
+        A3_STORE(p0r, 0);
+        A3_STORE(p1r, 1);
+#pragma unroll
+        for (int u = 0; u < NP; ++u)
+            if (pl[u] >= 0) *reinterpret_cast<uint4*>(ring + pl[u]) = ph[u];
+        if (bin) *reinterpret_cast<uint4*>(sbias + tid * 16) = pb;
+    }
+    __syncthreads();
+    {
+        const char* ab = ring + a_rd0;
+        const char* bb = halo + b_lane;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) af0[i] = *reinterpret_cast<const bf16x8*>(ab + i * 2048);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) bf0[j] = *reinterpret_cast<const bf16x8*>(bb + j * JSTRIDE);
+    }
+
+    // One tap T (a literal 0..8) of the current chunk.
+#define TAPOFF(T) ((((T) / 3) * DIL * HWd + ((T) % 3) * DIL) * (kHP * 16))
+#define HALO3_STEP(T)                                                                        \
+    do {                                                                                     \
+        /* (1) loads: weights of step + 3; halo pieces / the next tile's bias */             \
+        if ((T) + 3 < 9) A3_LOAD(ra[(T) % 3], a_vo_c, c, (T) + 3);                           \
+        else A3_LOAD(ra[(T) % 3], a_vo_n, cn, (T) + 3 - 9);                                  \
+        if ((T) < NPS) {                                                                     \
+            _Pragma("unroll") for (int p = 0; p < PPS; ++p)                                  \
+                H3_LOAD(hv[(T) & 1][p], hl[(T) & 1][p], hn.n, hn.g, hn.ho0, hn.wo0, cn,      \
+                        (T) * PPS + p, h_ok, hsel ^ 1);                                      \
+        } else if ((T) == NPS) {                                                             \
+            const bool bin_ = BIAS && last_chunk && k + 1 < nmine && tid * 4 < BM;           \
+            hv[(T) & 1][0] = load16(br, bin_ ? ((tn.g * s.cout_g + tn.ct * BM + tid * 4) * 4) : kOOB); \
+            hl[(T) & 1][0] = bin_ ? kRing * A_BYTES + 2 * H_BYTES + ((k + 1) & 1) * B_BYTES + tid * 16 : -1; \
+        }                                                                                    \
+        __builtin_amdgcn_sched_barrier(0);                                                   \
+        /* (2) second slice's operands of this step */                                       \
+        {                                                                                    \
+            const char* ab_ = ring + ((T) % 3) * A_BYTES + a_rd1;                            \
+            const char* bb_ = b_cur + TAPOFF(T) + 32;                                        \
+            _Pragma("unroll") for (int i = 0; i < TM; ++i)                                   \
+                af1[i] = *reinterpret_cast<const bf16x8*>(ab_ + i * 2048);                   \
+            _Pragma("unroll") for (int j = 0; j < TN; ++j)                                   \
+                bf1[j] = *reinterpret_cast<const bf16x8*>(bb_ + j * JSTRIDE);                \
+        }                                                                                    \
+        __builtin_amdgcn_sched_barrier(0);                                                   \
+        /* (3) first slice's matrix ops */                                                   \
+        _Pragma("unroll") for (int i = 0; i < TM; ++i)                                       \
+            _Pragma("unroll") for (int j = 0; j < TN; ++j)                                   \
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af0[i], bf0[j], acc[i][j], 0, 0, 0); \
+        /* (4) next step's first-slice operands; second slice's matrix ops */                \
+        {                                                                                    \
+            const char* ab_ = ring + (((T) + 1) % 3) * A_BYTES + a_rd0;                      \
+            const char* bb_ = (T) + 1 < 9 ? b_cur + TAPOFF((T) + 1 < 9 ? (T) + 1 : 0) : b_nxt; \
+            _Pragma("unroll") for (int i = 0; i < TM; ++i)                                   \
+                af0[i] = *reinterpret_cast<const bf16x8*>(ab_ + i * 2048);                   \
+            _Pragma("unroll") for (int j = 0; j < TN; ++j)                                   \
+                bf0[j] = *reinterpret_cast<const bf16x8*>(bb_ + j * JSTRIDE);                \
+        }                                                                                    \
+        _Pragma("unroll") for (int i = 0; i < TM; ++i)                                       \
+            _Pragma("unroll") for (int j = 0; j < TN; ++j)                                   \
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af1[i], bf1[j], acc[i][j], 0, 0, 0); \
+        __builtin_amdgcn_sched_barrier(0);                                                   \
+        /* (5) LDS stores: weights of step + 2; pieces loaded last step */                   \
+        A3_STORE(ra[((T) + 2) % 3], ((T) + 2) % 3);                                          \
+        if ((T) >= 1 && (T) <= NPS + 1) {                                                    \
+            _Pragma("unroll") for (int p = 0; p < ((T) - 1 < NPS ? PPS : 1); ++p)            \
+                if (hl[((T) + 1) & 1][p] >= 0)                                               \
+                    *reinterpret_cast<uint4*>(ring + hl[((T) + 1) & 1][p]) = hv[((T) + 1) & 1][p]; \
+        }                                                                                    \
+        /* (6) a tile's last step: epilogue, then the next tile */                           \
+        if ((T) == 8 && last_chunk) {                                                        \
+            tile_epilogue<TM, TN, WTM, WTN, TH, TW, BIAS, RELU>(acc, sbias + (k & 1) * B_BYTES, yr, s, \
+                                                              tc, tc.ct * BM, wm, wn, lane); \
+            _Pragma("unroll") for (int i = 0; i < TM; ++i)                                   \
+                _Pragma("unroll") for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};         \
+        }                                                                                    \
+        __syncthreads();                                                                     \
+    } while (0)
+
+    const int total = nmine * nchunk;  // chunks of this workgroup
+    for (int q = 0; q < total; ++q) {
+        // chunk state: the next chunk (its tile, channel chunk, validity)
+        const bool last_chunk = c + 1 == nchunk;
+        const int cn = last_chunk ? 0 : c + 1;
+        const TileXY hn = last_chunk ? tn : tc;
+        const bool h_ok = !last_chunk || k + 1 < nmine;
+        if (last_chunk) a_offsets(tn, a_vo_n);
+        else {
+            _Pragma("unroll") for (int i = 0; i < AV; ++i) a_vo_n[i] = a_vo_c[i];
+        }
+        const char* const b_cur = halo + hsel * H_BYTES + b_lane;
+        const char* const b_nxt = halo + (hsel ^ 1) * H_BYTES + b_lane;
+        HALO3_STEP(0);
+        HALO3_STEP(1);
+        HALO3_STEP(2);
+        HALO3_STEP(3);
+        HALO3_STEP(4);
+        HALO3_STEP(5);
+        HALO3_STEP(6);
+        HALO3_STEP(7);
+        HALO3_STEP(8);
+        // advance to the next chunk (and tile)
+        hsel ^= 1;
+        if (last_chunk) {
+            c = 0;
+            ++k;
+            tc = tn;
+            tn = tile_xy<TH, TW>(k + 1 < nmine ? first + (k + 1) * G : first, hg, s.groups);
+            _Pragma("unroll") for (int i = 0; i < AV; ++i) a_vo_c[i] = a_vo_n[i];
+        } else {
+            ++c;
+        }
+    }
+#undef A3_LOAD
+#undef A3_STORE
+#undef H3_LOAD
+#undef TAPOFF
+#undef HALO3_STEP
+}
+
+// Tile choice and launch parameters of one call; `ok` false when this
+// kernel does not take the shape.
+struct HaloPlan {
+    bool ok;
+    int cfg;        // 0: M128, 1: M64
+    bool shape_b;   // second pixel-block shape of the configuration
+    bool ke5;       // effective filter extent above 3: the larger halo buffers
+    HaloGrid hg;
+};
+
+template <int NT, int MINB, int BM, int WGM, int WGN, int THA, int TWA, int THB, int TWB>
+HaloPlan plan_cfg(const Shape& s, int cfg) {
+    static_assert(THA * TWA == THB * TWB, "equal pixel blocks");
+    HaloPlan p{};
+    p.cfg = cfg;
+    const long long pa = (long long)((s.Ho + THA - 1) / THA * THA) * ((s.Wo + TWA - 1) / TWA * TWA);
+    const long long pb = (long long)((s.Ho + THB - 1) / THB * THB) * ((s.Wo + TWB - 1) / TWB * TWB);
+    p.shape_b = pb < pa;
+    p.ke5 = (s.Kh - 1) * s.dil + 1 > 3 || (s.Kw - 1) * s.dil + 1 > 3;
+    const int TH = p.shape_b ? THB : THA, TW = p.shape_b ? TWB : TWA;
+    const int HWd = TW + (s.Kw - 1) * s.dil, HH = TH + (s.Kh - 1) * s.dil;
+    const int hunits = HH * HWd * 4;
+    p.hg.nparts = (hunits + NT - 1) / NT;
+    p.hg.hwd_magic = (65536 + HWd - 1) / HWd;
+    p.hg.tiles_h = (s.Ho + TH - 1) / TH;
+    p.hg.tiles_w = (s.Wo + TW - 1) / TW;
+    p.hg.n_ctiles = (s.cout_g + BM - 1) / BM;
+    const long long tiles = (long long)s.N * p.hg.tiles_h * p.hg.tiles_w * s.groups * p.hg.n_ctiles;
+    p.hg.ntiles = (int)(tiles > 0x7fffffffLL ? 0 : tiles);
+    // row = (pixel * magic) >> 16 must be exact over the window
+    bool magic_ok = true;
+    for (int hp = 0; hp < HH * HWd && magic_ok; ++hp) magic_ok = ((hp * p.hg.hwd_magic) >> 16) == hp / HWd;
+    // halo pieces are loaded at taps 0..nparts-1 (the bias at tap nparts),
+    // stored one tap later, and read by the operand prefetch of the chunk's
+    // last tap
+    p.ok = tiles > 0 && tiles <= 0x7fffffffLL && magic_ok && s.Kh * s.Kw >= p.hg.nparts + 2;
+    return p;
+}
+
+HaloPlan make_plan(const Shape& s) {
+    HaloPlan p{};
+    const long long xbytes = (long long)s.N * s.H * s.W * s.Cin * 2;
+    const long long ybytes = (long long)s.N * s.Ho * s.Wo * s.Cout * 2;
+    if (!(s.stride == 1 && (s.Kh - 1) * s.dil + 1 <= kKEmax && (s.Kw - 1) * s.dil + 1 <= kKEmax &&
+          s.cin_g % 8 == 0 && s.cout_g % 4 == 0 && s.cout_g > 32 &&
+          xbytes < 0x7fff0000LL && ybytes < 0x7fff0000LL))
+        return p;
+    if (s.cout_g > 64) return plan_cfg<HALO_CFG_M128>(s, 0);
+    return plan_cfg<HALO_CFG_M64>(s, 1);
+}
+
+// Resident workgroups per CU of one kernel instance on a device (cached).
+template <typename K>
+int blocks_per_cu(K kernel, int nt, int dev) {
+    static int cache[64] = {};
+    if (dev < 0 || dev >= 64) dev = 0;
+    int v = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
+    if (v > 0) return v;
+    int b = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, kernel, nt, 0) != hipSuccess || b < 1) b = 1;
+    __atomic_store_n(&cache[dev], b, __ATOMIC_RELAXED);
+    return b;
+}
+
+int cu_count(int dev) {
+    static int cache[64] = {};
+    if (dev < 0 || dev >= 64) return 256;
+    int v = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
+    if (v > 0) return v;
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
+    __atomic_store_n(&cache[dev], n, __ATOMIC_RELAXED);
+    return n;
+}
+
+template <int NT, int MINB, int BM, int TH, int TW, int WGM, int WGN, int KE, bool CFULL, bool BIAS, bool RELU>
+hipError_t launch_k(const Shape& s, const HaloGrid& hg, const bf16_t* x, const bf16_t* w,
+                    const float* b, bf16_t* y, hipStream_t st) {
+    auto kern = halo_kernel<NT, MINB, BM, TH, TW, WGM, WGN, KE, CFULL, BIAS, RELU>;
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    const long long resident = (long long)cu_count(dev) * blocks_per_cu(kern, NT, dev);
+    const int grid = (int)(hg.ntiles < resident ? hg.ntiles : resident);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(NT), 0, st, x, w, b, y, s, hg);
     return hipGetLastError();
 }
 
-template <int NT, int BM, int WGM, int WGN, int THA, int TWA, int THB, int TWB>
-hipError_t launch_shape(const Shape& s, const bf16_t* x, const bf16_t* w, const float* b, bf16_t* y,
-                        hipStream_t st) {
-    static_assert(THA * TWA == THB * TWB, "equal pixel blocks");
+template <int NT, int MINB, int BM, int TH, int TW, int WGM, int WGN, int KE, bool CFULL>
+hipError_t launch_epi(const Shape& s, const HaloGrid& hg, const bf16_t* x, const bf16_t* w,
+                      const float* b, bf16_t* y, hipStream_t st) {
+    const bool bias = s.epilogue & CONV2D_EPI_BIAS, relu = s.epilogue & CONV2D_EPI_RELU;
+    if (bias && relu) return launch_k<NT, MINB, BM, TH, TW, WGM, WGN, KE, CFULL, true, true>(s, hg, x, w, b, y, st);
+    if (bias) return launch_k<NT, MINB, BM, TH, TW, WGM, WGN, KE, CFULL, true, false>(s, hg, x, w, b, y, st);
+    if (relu) return launch_k<NT, MINB, BM, TH, TW, WGM, WGN, KE, CFULL, false, true>(s, hg, x, w, b, y, st);
+    return launch_k<NT, MINB, BM, TH, TW, WGM, WGN, KE, CFULL, false, false>(s, hg, x, w, b, y, st);
+}
+
+template <int NT, int MINB, int BM, int WGM, int WGN, int TH, int TW>
+hipError_t launch_shape(const Shape& s, const HaloPlan& p, const bf16_t* x, const bf16_t* w,
+                        const float* b, bf16_t* y, hipStream_t st) {
     const bool full = s.cin_g % kBK == 0;
-    const long long pa = (long long)((s.Ho + THA - 1) / THA * THA) * ((s.Wo + TWA - 1) / TWA * TWA);
-    const long long pb = (long long)((s.Ho + THB - 1) / THB * THB) * ((s.Wo + TWB - 1) / TWB * TWB);
-    if (pb < pa) {
-        if (full) return launch_tile<NT, BM, THB, TWB, WGM, WGN, true>(s, x, w, b, y, st);
-        return launch_tile<NT, BM, THB, TWB, WGM, WGN, false>(s, x, w, b, y, st);
+    if (p.ke5) {
+        if (full) return launch_epi<NT, MINB, BM, TH, TW, WGM, WGN, 5, true>(s, p.hg, x, w, b, y, st);
+        return launch_epi<NT, MINB, BM, TH, TW, WGM, WGN, 5, false>(s, p.hg, x, w, b, y, st);
     }
-    if (full) return launch_tile<NT, BM, THA, TWA, WGM, WGN, true>(s, x, w, b, y, st);
-    return launch_tile<NT, BM, THA, TWA, WGM, WGN, false>(s, x, w, b, y, st);
+    if (full) return launch_epi<NT, MINB, BM, TH, TW, WGM, WGN, 3, true>(s, p.hg, x, w, b, y, st);
+    return launch_epi<NT, MINB, BM, TH, TW, WGM, WGN, 3, false>(s, p.hg, x, w, b, y, st);
+}
+
+template <int NT, int MINB, int BM, int TH, int TW, int WGM, int WGN, int DIL, bool CFULL, bool BIAS, bool RELU>
+hipError_t launch3_k(const Shape& s, const HaloGrid& hg, const bf16_t* x, const bf16_t* w,
+                     const float* b, bf16_t* y, hipStream_t st) {
+    auto kern = halo3_kernel<NT, MINB, BM, TH, TW, WGM, WGN, DIL, CFULL, BIAS, RELU>;
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    const long long resident = (long long)cu_count(dev) * blocks_per_cu(kern, NT, dev);
+    const int grid = (int)(hg.ntiles < resident ? hg.ntiles : resident);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(NT), 0, st, x, w, b, y, s, hg);
+    return hipGetLastError();
+}
+
+template <int NT, int MINB, int BM, int TH, int TW, int WGM, int WGN, int DIL, bool CFULL>
+hipError_t launch3_epi(const Shape& s, const HaloGrid& hg, const bf16_t* x, const bf16_t* w,
+                       const float* b, bf16_t* y, hipStream_t st) {
+    const bool bias = s.epilogue & CONV2D_EPI_BIAS, relu = s.epilogue & CONV2D_EPI_RELU;
+    if (bias && relu) return launch3_k<NT, MINB, BM, TH, TW, WGM, WGN, DIL, CFULL, true, true>(s, hg, x, w, b, y, st);
+    if (bias) return launch3_k<NT, MINB, BM, TH, TW, WGM, WGN, DIL, CFULL, true, false>(s, hg, x, w, b, y, st);
+    if (relu) return launch3_k<NT, MINB, BM, TH, TW, WGM, WGN, DIL, CFULL, false, true>(s, hg, x, w, b, y, st);
+    return launch3_k<NT, MINB, BM, TH, TW, WGM, WGN, DIL, CFULL, false, false>(s, hg, x, w, b, y, st);
+}
+
+template <int NT, int MINB, int BM, int WGM, int WGN, int TH, int TW>
+hipError_t launch3_shape(const Shape& s, const HaloPlan& p, const bf16_t* x, const bf16_t* w,
+                         const float* b, bf16_t* y, hipStream_t st) {
+    const bool full = s.cin_g % kBK == 0;
+    if (s.dil == 2) {
+        if (full) return launch3_epi<NT, MINB, BM, TH, TW, WGM, WGN, 2, true>(s, p.hg, x, w, b, y, st);
+        return launch3_epi<NT, MINB, BM, TH, TW, WGM, WGN, 2, false>(s, p.hg, x, w, b, y, st);
+    }
+    if (full) return launch3_epi<NT, MINB, BM, TH, TW, WGM, WGN, 1, true>(s, p.hg, x, w, b, y, st);
+    return launch3_epi<NT, MINB, BM, TH, TW, WGM, WGN, 1, false>(s, p.hg, x, w, b, y, st);
+}
+
+// 3x3 with dilation 1 or 2: the kernel with the taps unrolled.
+bool is_3x3(const Shape& s) { return s.Kh == 3 && s.Kw == 3 && (s.dil == 1 || s.dil == 2); }
+
+template <int NT, int MINB, int BM, int WGM, int WGN, int THA, int TWA, int THB, int TWB>
+hipError_t launch_cfg(const Shape& s, const HaloPlan& p, const bf16_t* x, const bf16_t* w,
+                      const float* b, bf16_t* y, hipStream_t st) {
+    if (is_3x3(s)) {
+        if (p.shape_b) return launch3_shape<NT, MINB, BM, WGM, WGN, THB, TWB>(s, p, x, w, b, y, st);
+        return launch3_shape<NT, MINB, BM, WGM, WGN, THA, TWA>(s, p, x, w, b, y, st);
+    }
+    if (p.shape_b) return launch_shape<NT, MINB, BM, WGM, WGN, THB, TWB>(s, p, x, w, b, y, st);
+    return launch_shape<NT, MINB, BM, WGM, WGN, THA, TWA>(s, p, x, w, b, y, st);
 }
 
 }  // namespace
 
-bool igemm_halo_supports(const Shape& s) {
-    const long long xbytes = (long long)s.N * s.H * s.W * s.Cin * 2;
-    return s.stride == 1 && (s.Kh - 1) * s.dil + 1 <= kKEmax && (s.Kw - 1) * s.dil + 1 <= kKEmax &&
-           s.cin_g % 8 == 0 && s.cout_g % 4 == 0 && s.cout_g > 32 && xbytes < 0x7fff0000LL;
-}
+bool igemm_halo_supports(const Shape& s) { return make_plan(s).ok; }
 
 hipError_t launch_igemm_halo(const Shape& s, const void* x, const void* w_packed, const float* bias,
                              void* y, hipStream_t st) {
     (void)hipGetLastError();  // report only this launch's error
+    const HaloPlan p = make_plan(s);
+    if (!p.ok) return hipErrorInvalidValue;
     const bf16_t* xt = static_cast<const bf16_t*>(x);
     const bf16_t* wt = static_cast<const bf16_t*>(w_packed);
     bf16_t* yt = static_cast<bf16_t*>(y);
-    if (s.cout_g > 128) return launch_shape<HALO_CFG_M256>(s, xt, wt, bias, yt, st);
-    if (s.cout_g > 64) return launch_shape<HALO_CFG_M128>(s, xt, wt, bias, yt, st);
-    return launch_shape<HALO_CFG_M64>(s, xt, wt, bias, yt, st);
+    if (p.cfg == 0) return launch_cfg<HALO_CFG_M128>(s, p, xt, wt, bias, yt, st);
+    return launch_cfg<HALO_CFG_M64>(s, p, xt, wt, bias, yt, st);
 }
 
 }  // namespace conv2d

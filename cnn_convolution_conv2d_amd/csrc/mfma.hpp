@@ -29,6 +29,18 @@ __device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, int byte_off, 
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, uniform_off, 0));
 }
 
+// Buffer stores: an offset past the descriptor's size drops the store, so
+// out-of-range pixels and channels need no branch.
+__device__ __forceinline__ void store16(__amdgpu_buffer_rsrc_t r, int byte_off, uint4 v) {
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, byte_off, 0, 0);
+}
+
+__device__ __forceinline__ void store8(__amdgpu_buffer_rsrc_t r, int byte_off, uint2 v) {
+    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, byte_off, 0, 0);
+}
+
 // An LDS row holds the BK channels of one K-step for one output channel (A)
 // or one pixel (B): BK*2 bytes = BK/8 16-byte chunks.  The chunk index is
 // XOR-swizzled with the row so that any 16 consecutive rows read at the same
