@@ -75,6 +75,7 @@ struct HaloGrid {
     int tiles_h, tiles_w, n_ctiles, ntiles;
     int hwd_magic;  // ceil(2^16 / window width): row = (pixel * magic) >> 16 inside the window
     int nparts;     // 16-byte halo loads per thread per chunk (one per tap)
+    int spread;     // last-round tiles go to every spread-th first-round workgroup of an XCD
 };
 
 // LDS bytes of one workgroup: weight ring, two halo buffers, two bias buffers.
@@ -574,9 +575,21 @@ void halo3_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ wp, c
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WGN, wn = wave % WGN;
     const int G = gridDim.x;
+    // This workgroup's tiles: first + k*G for the full rounds (first is
+    // XCD-aware, so each XCD's L2 sees one run of neighbouring tiles), then at
+    // most one of the last round's tiles, spread so that no two of them share
+    // a CU.
     const int first = xcd_tile_index();
     if (first >= hg.ntiles) return;
-    const int nmine = (hg.ntiles - 1 - first) / G + 1;
+    const int nfull = hg.ntiles / G, nextra = hg.ntiles - nfull * G;
+    int e_extra;
+    if (G % 8 == 0) {
+        const int m = blockIdx.x >> 3;
+        e_extra = m % hg.spread == 0 ? (blockIdx.x & 7) + 8 * (m / hg.spread) : nextra;
+    } else {
+        e_extra = blockIdx.x;
+    }
+    const int nmine = nfull + (e_extra < nextra ? 1 : 0);
     const int nchunk = (s.cin_g + kBK - 1) / kBK;
     const int wrow = 9 * s.cin_g * 2;  // bytes of one packed weight row
 
@@ -613,9 +626,10 @@ void halo3_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ wp, c
         }
     };
 
-    TileXY tc = tile_xy<TH, TW>(first, hg, s.groups);
-    TileXY tn = tile_xy<TH, TW>(nmine > 1 ? first + G : first, hg, s.groups);
-    int k = 0, c = 0, hsel = 0;
+#define TILE_OF(KK) ((KK) < nfull ? first + (KK) * G : nfull * G + e_extra)
+    TileXY tc = tile_xy<TH, TW>(TILE_OF(0), hg, s.groups);
+    TileXY tn = tile_xy<TH, TW>(TILE_OF(nmine > 1 ? 1 : 0), hg, s.groups);
+    int hsel = 0;
 
     f32x16 acc[TM][TN];
 #pragma unroll
@@ -745,50 +759,61 @@ void halo3_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ wp, c
                 if (hl[((T) + 1) & 1][p] >= 0)                                               \
                     *reinterpret_cast<uint4*>(ring + hl[((T) + 1) & 1][p]) = hv[((T) + 1) & 1][p]; \
         }                                                                                    \
-        /* (6) a tile's last step: epilogue, then the next tile */                           \
-        if ((T) == 8 && last_chunk) {                                                        \
-            tile_epilogue<TM, TN, WTM, WTN, TH, TW, BIAS, RELU>(acc, sbias + (k & 1) * B_BYTES, yr, s, \
-                                                              tc, tc.ct * BM, wm, wn, lane); \
-            _Pragma("unroll") for (int i = 0; i < TM; ++i)                                   \
-                _Pragma("unroll") for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};         \
-        }                                                                                    \
         __syncthreads();                                                                     \
     } while (0)
 
-    const int total = nmine * nchunk;  // chunks of this workgroup
-    for (int q = 0; q < total; ++q) {
-        // chunk state: the next chunk (its tile, channel chunk, validity)
-        const bool last_chunk = c + 1 == nchunk;
-        const int cn = last_chunk ? 0 : c + 1;
-        const TileXY hn = last_chunk ? tn : tc;
-        const bool h_ok = !last_chunk || k + 1 < nmine;
-        if (last_chunk) a_offsets(tn, a_vo_n);
-        else {
-            _Pragma("unroll") for (int i = 0; i < AV; ++i) a_vo_n[i] = a_vo_c[i];
+    const int half = lane >> 5;
+    for (int k = 0; k < nmine; ++k) {
+        // accumulators start at the tile's bias (its rows of the current bias
+        // buffer), so the epilogue only applies ReLU and rounds
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float4 b4 = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (BIAS)
+                    b4 = *reinterpret_cast<const float4*>(sbias + (k & 1) * B_BYTES +
+                                                          (wm * WTM + i * 32 + 8 * q + 4 * half) * 4);
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    acc[i][j][4 * q + 0] = b4.x;
+                    acc[i][j][4 * q + 1] = b4.y;
+                    acc[i][j][4 * q + 2] = b4.z;
+                    acc[i][j][4 * q + 3] = b4.w;
+                }
+            }
         }
-        const char* const b_cur = halo + hsel * H_BYTES + b_lane;
-        const char* const b_nxt = halo + (hsel ^ 1) * H_BYTES + b_lane;
-        HALO3_STEP(0);
-        HALO3_STEP(1);
-        HALO3_STEP(2);
-        HALO3_STEP(3);
-        HALO3_STEP(4);
-        HALO3_STEP(5);
-        HALO3_STEP(6);
-        HALO3_STEP(7);
-        HALO3_STEP(8);
-        // advance to the next chunk (and tile)
-        hsel ^= 1;
-        if (last_chunk) {
-            c = 0;
-            ++k;
-            tc = tn;
-            tn = tile_xy<TH, TW>(k + 1 < nmine ? first + (k + 1) * G : first, hg, s.groups);
-            _Pragma("unroll") for (int i = 0; i < AV; ++i) a_vo_c[i] = a_vo_n[i];
-        } else {
-            ++c;
+        for (int c = 0; c < nchunk; ++c) {
+            // chunk state: the next chunk (its tile, channel chunk, validity)
+            const bool last_chunk = c + 1 == nchunk;
+            const int cn = last_chunk ? 0 : c + 1;
+            const TileXY hn = last_chunk ? tn : tc;
+            const bool h_ok = !last_chunk || k + 1 < nmine;
+            if (last_chunk) a_offsets(tn, a_vo_n);
+            else {
+                _Pragma("unroll") for (int i = 0; i < AV; ++i) a_vo_n[i] = a_vo_c[i];
+            }
+            const char* const b_cur = halo + hsel * H_BYTES + b_lane;
+            const char* const b_nxt = halo + (hsel ^ 1) * H_BYTES + b_lane;
+            HALO3_STEP(0);
+            HALO3_STEP(1);
+            HALO3_STEP(2);
+            HALO3_STEP(3);
+            HALO3_STEP(4);
+            HALO3_STEP(5);
+            HALO3_STEP(6);
+            HALO3_STEP(7);
+            HALO3_STEP(8);
+            hsel ^= 1;
         }
+        // the tile is done: ReLU, bf16, store; then the next tile
+        tile_epilogue<TM, TN, WTM, WTN, TH, TW, false, RELU>(acc, sbias, yr, s, tc, tc.ct * BM, wm, wn, lane);
+        tc = tn;
+        tn = tile_xy<TH, TW>(TILE_OF(k + 2 < nmine ? k + 2 : 0), hg, s.groups);
+#pragma unroll
+        for (int i = 0; i < AV; ++i) a_vo_c[i] = a_vo_n[i];
     }
+#undef TILE_OF
 #undef A3_LOAD
 #undef A3_STORE
 #undef H3_LOAD
@@ -825,6 +850,7 @@ HaloPlan plan_cfg(const Shape& s, int cfg) {
     p.hg.n_ctiles = (s.cout_g + BM - 1) / BM;
     const long long tiles = (long long)s.N * p.hg.tiles_h * p.hg.tiles_w * s.groups * p.hg.n_ctiles;
     p.hg.ntiles = (int)(tiles > 0x7fffffffLL ? 0 : tiles);
+    p.hg.spread = 1;
     // row = (pixel * magic) >> 16 must be exact over the window
     bool magic_ok = true;
     for (int hp = 0; hp < HH * HWd && magic_ok; ++hp) magic_ok = ((hp * p.hg.hwd_magic) >> 16) == hp / HWd;
@@ -911,9 +937,17 @@ hipError_t launch3_k(const Shape& s, const HaloGrid& hg, const bf16_t* x, const 
     auto kern = halo3_kernel<NT, MINB, BM, TH, TW, WGM, WGN, DIL, CFULL, BIAS, RELU>;
     int dev = 0;
     (void)hipGetDevice(&dev);
-    const long long resident = (long long)cu_count(dev) * blocks_per_cu(kern, NT, dev);
+    const int bpc = blocks_per_cu(kern, NT, dev);
+    const long long resident = (long long)cu_count(dev) * bpc;
     const int grid = (int)(hg.ntiles < resident ? hg.ntiles : resident);
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(NT), 0, st, x, w, b, y, s, hg);
+    // Workgroups go round-robin over the 8 XCDs and, within one, fill every
+    // CU once before any CU takes a second: the last round's tiles go to
+    // every spread-th first-round workgroup of each XCD.
+    HaloGrid h = hg;
+    const int per_xcd = grid / 8, extra = hg.ntiles % grid;
+    const int slots = per_xcd / (bpc > 0 ? bpc : 1), want = (extra + 7) / 8;
+    h.spread = (grid % 8 == 0 && want > 0 && slots / want > 1) ? slots / want : 1;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(NT), 0, st, x, w, b, y, s, h);
     return hipGetLastError();
 }
 
