@@ -467,25 +467,31 @@ __global__ __launch_bounds__(NT, waves_per_simd(NT, MINB, halo_lds_bytes(BM, TH,
 #undef HALO_NEXT_CHUNK
 }
 
-// Epilogue of one tile from registers: bias, ReLU, bf16; lane l < 32 of a
-// 32x32 block holds channels 8q+r (q = 0..3, r = 0..3) of pixel l, lane
-// l + 32 channels 8q+4+r; one v_permlane32_swap per pair of q gives each
-// lane 8 consecutive channels (16 bytes) of one pixel, stored with one
-// buffer store (offset past the end for pixels and channels outside the
-// output: the store is dropped).
+// Epilogue of one tile from registers: bias, ReLU, bf16.  In the 32x32
+// result layout lane l < 32 of a block holds channels 8q+r (q = 0..3,
+// r = 0..3) of pixel l and lane l + 32 channels 8q+4+r.  A lane-half swap
+// (v_permlane32_swap) gives each lane 8 consecutive channels; a row swap
+// (v_permlane16_swap) then gathers 32 consecutive channels of 16 pixels into
+// one store instruction: lanes l, l+16, l+32, l+48 write the four 16-byte
+// pieces of one pixel's 64 contiguous bytes.  Pixels and channels outside the
+// output get an offset past the end: the buffer store drops them.
 template <int TM, int TN, int WTM, int WTN, int TH, int TW, bool BIAS, bool RELU>
 __device__ __forceinline__ void tile_epilogue(f32x16 (&acc)[TM][TN], const char* sb,
                                               __amdgpu_buffer_rsrc_t yr, const Shape& s,
                                               const TileXY& tc, int co0, int wm, int wn, int lane) {
     const int half = lane >> 5;
     const bool vec16 = (s.Cout % 8 == 0) && (s.cout_g % 8 == 0);
-    int pix[TN];
+    int pix[TN][2];
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-        const int p = wn * WTN + j * 32 + (lane & 31);
-        const int ho = tc.ho0 + p / TW, wo = tc.wo0 + p % TW;
-        pix[j] = (ho < s.Ho && wo < s.Wo) ? ((tc.n * s.Ho + ho) * s.Wo + wo) * s.Cout : -1;
-    }
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int p = wn * WTN + j * 32 + 16 * h + (lane & 15);
+            const int ho = tc.ho0 + p / TW, wo = tc.wo0 + p % TW;
+            pix[j][h] = (ho < s.Ho && wo < s.Wo) ? ((tc.n * s.Ho + ho) * s.Wo + wo) * s.Cout : -1;
+        }
+    // channel of this lane's 16-byte piece within a 32-channel block
+    const int cl = ((lane >> 4) & 1) * 16 + half * 8;
     const int cw = co0 + wm * WTM;  // first channel (within the group) of the wave's rows
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
@@ -495,6 +501,7 @@ __device__ __forceinline__ void tile_epilogue(f32x16 (&acc)[TM][TN], const char*
             b4[q] = make_float4(0.f, 0.f, 0.f, 0.f);
             if (BIAS) b4[q] = *reinterpret_cast<const float4*>(sb + (wm * WTM + i * 32 + 8 * q + 4 * half) * 4);
         }
+        const int co = cw + i * 32 + cl;
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             uint32_t pk[4][2];
@@ -509,22 +516,33 @@ __device__ __forceinline__ void tile_epilogue(f32x16 (&acc)[TM][TN], const char*
                 pk[q][0] = pack_bf16x2(v[0], v[1]);
                 pk[q][1] = pack_bf16x2(v[2], v[3]);
             }
+            // r8[pr]: 8 channels 16*pr + 8*half .. +7 of pixel lane % 32
+            uint32_t r8[2][4];
 #pragma unroll
-            for (int pr = 0; pr < 2; ++pr) {
-                uint32_t lo[2], hi[2];
+            for (int pr = 0; pr < 2; ++pr)
 #pragma unroll
                 for (int w = 0; w < 2; ++w) {
                     const auto sw = __builtin_amdgcn_permlane32_swap(pk[2 * pr][w], pk[2 * pr + 1][w], false, false);
-                    lo[w] = sw[0];
-                    hi[w] = sw[1];
+                    r8[pr][w] = sw[0];
+                    r8[pr][2 + w] = sw[1];
                 }
-                const int co = cw + i * 32 + 16 * pr + 8 * half;
-                const int off = (pix[j] + tc.g * s.cout_g + co) * 2;
+            // out[h]: channels cl .. cl+7 of pixel 16*h + lane % 16
+            uint32_t out[2][4];
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const auto sw = __builtin_amdgcn_permlane16_swap(r8[0][d], r8[1][d], false, false);
+                out[0][d] = sw[0];
+                out[1][d] = sw[1];
+            }
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int off = (pix[j][h] + tc.g * s.cout_g + co) * 2;
                 if (vec16) {
-                    store16(yr, pix[j] >= 0 && co < s.cout_g ? off : kOOB, make_uint4(lo[0], lo[1], hi[0], hi[1]));
+                    store16(yr, pix[j][h] >= 0 && co < s.cout_g ? off : kOOB,
+                            make_uint4(out[h][0], out[h][1], out[h][2], out[h][3]));
                 } else {
-                    store8(yr, pix[j] >= 0 && co < s.cout_g ? off : kOOB, make_uint2(lo[0], lo[1]));
-                    store8(yr, pix[j] >= 0 && co + 4 < s.cout_g ? off + 8 : kOOB, make_uint2(hi[0], hi[1]));
+                    store8(yr, pix[j][h] >= 0 && co < s.cout_g ? off : kOOB, make_uint2(out[h][0], out[h][1]));
+                    store8(yr, pix[j][h] >= 0 && co + 4 < s.cout_g ? off + 8 : kOOB, make_uint2(out[h][2], out[h][3]));
                 }
             }
         }
