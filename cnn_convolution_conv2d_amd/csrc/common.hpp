@@ -57,6 +57,32 @@ __device__ __forceinline__ float epilogue(float acc, const float* bias, int co) 
     return v;
 }
 
+// Compute units of a device (cached per device id).
+inline int cu_count(int dev) {
+    static int cache[64] = {};
+    if (dev < 0 || dev >= 64) return 256;
+    int v = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
+    if (v > 0) return v;
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
+    __atomic_store_n(&cache[dev], n, __ATOMIC_RELAXED);
+    return n;
+}
+
+// Resident workgroups per CU of one kernel on a device (cached per kernel
+// and device id; at least 1).
+template <typename K>
+int blocks_per_cu(K kernel, int nt, int dev) {
+    static int cache[64] = {};
+    if (dev < 0 || dev >= 64) dev = 0;
+    int v = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
+    if (v > 0) return v;
+    int b = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, kernel, nt, 0) != hipSuccess || b < 1) b = 1;
+    __atomic_store_n(&cache[dev], b, __ATOMIC_RELAXED);
+    return b;
+}
+
 // Host-side launchers (each defined in its kernel's source file).  They
 // return hipSuccess or the launch error.
 hipError_t launch_direct(const Shape& s, const void* x, int xl, const void* w, int wl,
@@ -73,6 +99,9 @@ bool igemm_supports(const Shape& s);
 bool igemm_halo_supports(const Shape& s);
 bool gemm1x1_supports(const Shape& s);
 bool depthwise_supports(const Shape& s);
+hipError_t launch_pointwise(const Shape& s, const void* x, const void* w_packed, const float* bias,
+                            void* y, hipStream_t st);
+bool pointwise_supports(const Shape& s);
 
 hipError_t launch_transpose(const void* src, void* dst, int batch, int rows, int cols,
                             int elem_bytes, hipStream_t st);

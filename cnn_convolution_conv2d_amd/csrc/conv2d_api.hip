@@ -130,7 +130,11 @@ int run_nhwc(int path, const Shape& s, const void* x, const void* wp, const floa
         e = launch_direct(s, x, NHWC, wp, is_depthwise(s) ? W_DW : W_PACKED, bias, y, NHWC, st);
         break;
     case CONV2D_PATH_DEPTHWISE: e = launch_depthwise(s, x, wp, bias, y, st); break;
-    case CONV2D_PATH_GEMM1X1: e = launch_gemm1x1(s, x, wp, bias, y, st); break;
+    case CONV2D_PATH_GEMM1X1:
+        // the streaming kernel where the weights fit in LDS, else the tiled GEMM
+        e = pointwise_supports(s) ? launch_pointwise(s, x, wp, bias, y, st)
+                                  : launch_gemm1x1(s, x, wp, bias, y, st);
+        break;
     case CONV2D_PATH_IGEMM_GATHER: e = launch_igemm(s, x, wp, bias, y, st); break;
     case CONV2D_PATH_IGEMM_HALO: e = launch_igemm_halo(s, x, wp, bias, y, st); break;
     default: return set_error(CONV2D_ERR_UNSUPPORTED, "unknown path %d", path);

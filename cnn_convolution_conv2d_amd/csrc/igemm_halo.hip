@@ -891,30 +891,6 @@ HaloPlan make_plan(const Shape& s) {
     return plan_cfg<HALO_CFG_M64>(s, 1);
 }
 
-// Resident workgroups per CU of one kernel instance on a device (cached).
-template <typename K>
-int blocks_per_cu(K kernel, int nt, int dev) {
-    static int cache[64] = {};
-    if (dev < 0 || dev >= 64) dev = 0;
-    int v = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
-    if (v > 0) return v;
-    int b = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, kernel, nt, 0) != hipSuccess || b < 1) b = 1;
-    __atomic_store_n(&cache[dev], b, __ATOMIC_RELAXED);
-    return b;
-}
-
-int cu_count(int dev) {
-    static int cache[64] = {};
-    if (dev < 0 || dev >= 64) return 256;
-    int v = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
-    if (v > 0) return v;
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
-    __atomic_store_n(&cache[dev], n, __ATOMIC_RELAXED);
-    return n;
-}
-
 template <int NT, int MINB, int BM, int TH, int TW, int WGM, int WGN, int KE, bool CFULL, bool BIAS, bool RELU>
 hipError_t launch_k(const Shape& s, const HaloGrid& hg, const bf16_t* x, const bf16_t* w,
                     const float* b, bf16_t* y, hipStream_t st) {

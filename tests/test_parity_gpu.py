@@ -179,6 +179,14 @@ def _sweep():
         (1, 64, 11, 13, 128, 5, 5, 1, 2, 1, 1), (2, 96, 10, 10, 192, 3, 3, 1, 1, 1, 2),
         (1, 16, 20, 18, 300, 3, 1, 1, 0, 1, 1), (1, 24, 7, 33, 72, 1, 3, 1, 1, 2, 1),
         (1, 8, 2, 3, 40, 3, 3, 1, 1, 1, 1), (1, 136, 6, 5, 64, 3, 3, 1, 0, 1, 1),
+        # 1x1 shapes for the streaming pointwise kernel (Cin up to 256 in
+        # 16-channel slices, Cout split into 128-channel work items, Cout not a
+        # multiple of 8, more 32-pixel tiles than waves) and for the tiled GEMM
+        # (Cin or Cout above 256)
+        (2, 256, 9, 11, 64, 1, 1, 1, 0, 1, 1), (1, 64, 13, 17, 256, 1, 1, 1, 0, 1, 1),
+        (1, 144, 7, 9, 24, 1, 1, 1, 0, 1, 1), (1, 32, 5, 5, 20, 1, 1, 1, 0, 1, 1),
+        (16, 16, 64, 70, 16, 1, 1, 1, 0, 1, 1), (1, 264, 3, 5, 16, 1, 1, 1, 0, 1, 1),
+        (1, 16, 4, 6, 272, 1, 1, 1, 0, 1, 1),
     ]
     return cases
 
