@@ -52,8 +52,9 @@ PEAK_FP32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 ROTATE_BYTES = 512 << 20
 METRIC = "conv2d fwd TFLOP/s (GB/s for depthwise) and % of MI355X roofline, 1 GPU"
-KERNEL_SOURCES = {"direct": "direct.hip", "depthwise": "depthwise.hip", "gemm1x1": "igemm.hip",
-                  "igemm_gather": "igemm.hip", "igemm_halo": "igemm_halo.hip"}
+KERNEL_SOURCES = {"direct": ["direct.hip"], "depthwise": ["depthwise.hip"],
+                  "gemm1x1": ["pointwise.hip", "igemm.hip"], "igemm_gather": ["igemm.hip"],
+                  "igemm_halo": ["igemm_halo.hip"]}
 
 
 def out_hw(ly):
@@ -83,10 +84,10 @@ def bound_of(ly):
 
 
 def source_digest(path_name):
-    src = os.path.join(ROOT, "cnn_convolution_conv2d_amd", "csrc", KERNEL_SOURCES[path_name])
+    csrc = os.path.join(ROOT, "cnn_convolution_conv2d_amd", "csrc")
     h = hashlib.sha256()
-    for p in (src, os.path.join(ROOT, "cnn_convolution_conv2d_amd", "csrc", "common.hpp")):
-        h.update(open(p, "rb").read())
+    for name in KERNEL_SOURCES[path_name] + ["common.hpp", "mfma.hpp"]:
+        h.update(open(os.path.join(csrc, name), "rb").read())
     return h.hexdigest()[:16]
 
 
