@@ -10,10 +10,11 @@
 //  * the whole weight matrix is staged in LDS once per workgroup (rows at an
 //    odd pitch of 16-byte units, so the 16 rows read together by a quarter
 //    wave land in 16 distinct bank slots);
-//  * every wave walks its own 32-pixel tiles with no barrier; a tile's
-//    activations are loaded straight into MFMA operand registers (lane l
-//    holds 8 channels of pixel l % 32), one tile ahead of the one being
-//    computed;
+//  * every wave walks its own 32-pixel tiles with no barrier.  A tile's
+//    activations are one contiguous run of 32*Cin channels, fetched one tile
+//    ahead with fully coalesced 1 KB loads, written to the wave's own LDS
+//    region at an odd pixel pitch, and read back in MFMA operand layout
+//    (lane l: 8 channels of pixel l % 32);
 //  * v_mfma_f32_32x32x16_bf16 per 32 output channels and 16 input channels,
 //    fp32 accumulators initialised with the bias;
 //  * the same register epilogue as the halo kernel: ReLU, bf16, two lane
@@ -26,27 +27,33 @@ namespace conv2d {
 namespace {
 
 constexpr int kPwThreads = 256;
+constexpr int kPwWaves = kPwThreads / 64;
 constexpr int kPwMaxLds = 64 * 1024;  // bytes of staged weights
 constexpr int kPwMaxCout = 256;
 
-// Row pitch of the staged weights in 16-byte units: odd.
-__host__ __device__ constexpr int pw_pitch(int cin) { return ((cin + 7) / 8) | 1; }
+// Row pitch of the staged weights and activations in 16-byte units: odd (no
+// bank conflicts), and at least two units per 16-channel slice, so the last
+// slice's second half is a zero pad unit inside the row when Cin % 16 == 8.
+__host__ __device__ constexpr int pw_pitch(int cin) { return (2 * ((cin + 15) / 16)) | 1; }
 
 // MB: 32-row blocks of output channels per work item; KS: 16-channel slices
 // of the input (Cin <= 16*KS).  A work item is one 32-pixel tile and one
 // group of MB*32 output channels (nmh groups cover Cout); the items of one
 // tile are consecutive, so the later ones find its activations in cache.
-template <int MB, int KS>
+template <int MB, int KS, bool STAGED>
 __global__ __launch_bounds__(kPwThreads, 2) void pw_kernel(const bf16_t* __restrict__ x,
                                                        const bf16_t* __restrict__ wp,
                                                        const float* __restrict__ bias,
                                                        bf16_t* __restrict__ y, int npix, int cin,
                                                        int cout, int ntiles, int nmh, int has_bias,
-                                                       int relu) {
-    __shared__ uint4 wl[kPwMaxLds / 16];
+                                                       int relu, int cin8_magic) {
+    // dynamic LDS: weights [rows][P units], then one activation tile
+    // [32 pixels][P units] per wave
+    extern __shared__ uint4 pw_lds[];
     __shared__ __align__(16) float sb[kPwMaxCout];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int P = pw_pitch(cin);
+    uint4* const wl = pw_lds;
 
     // stage the weights (rows past Cout and channels past Cin are zero) and
     // the bias
@@ -54,7 +61,7 @@ __global__ __launch_bounds__(kPwThreads, 2) void pw_kernel(const bf16_t* __restr
     {
         // all loads first (zero for padding units), then the LDS stores, so
         // the staging costs one memory latency
-        constexpr int kUnits = kPwMaxLds / 16 / kPwThreads;
+        constexpr int kUnits = (kPwMaxLds / 16 + kPwThreads - 1) / kPwThreads;
         const __amdgpu_buffer_rsrc_t wr = make_rsrc(wp, (uint32_t)cout * (uint32_t)cin * 2u);
         uint4 v[kUnits];
 #pragma unroll
@@ -70,6 +77,11 @@ __global__ __launch_bounds__(kPwThreads, 2) void pw_kernel(const bf16_t* __restr
         }
     }
     for (int i = tid; i < rows; i += kPwThreads) sb[i] = (has_bias && i < cout) ? bias[i] : 0.0f;
+    // pad units of every pixel row of the activation tiles (never written
+    // by the staging) are zero
+    if (STAGED)
+        for (int u = tid; u < kPwWaves * 32 * P; u += kPwThreads)
+            if ((u % P) * 8 >= cin) wl[rows * P + u] = make_uint4(0, 0, 0, 0);
     __syncthreads();
 
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)npix * (uint32_t)cin * 2u);
@@ -77,6 +89,10 @@ __global__ __launch_bounds__(kPwThreads, 2) void pw_kernel(const bf16_t* __restr
     const int frow = lane & 31, h = lane >> 5;
     // weight operand: row frow of block mb, 16-byte chunk 2s + h
     const char* const a_base = reinterpret_cast<const char*>(wl) + (frow * P + h) * 16;
+    // this wave's activation tile; operand of slice s: pixel frow, chunk 2s + h
+    char* const xt = reinterpret_cast<char*>(wl + rows * P + wave * 32 * P);
+    const char* const b_base = xt + (frow * P + h) * 16;
+    const int cin8 = cin / 8, tunits = 32 * cin8;  // 16-byte units of one tile
     // epilogue: this lane's 16-byte piece holds channels cl .. cl+7 of a
     // 32-channel block, of pixel 16*e + lane % 16 (e = 0, 1) of the tile
     const int cl = ((lane >> 4) & 1) * 16 + h * 8;
@@ -89,15 +105,37 @@ __global__ __launch_bounds__(kPwThreads, 2) void pw_kernel(const bf16_t* __restr
     uint4 b0[KS], b1[KS];
     f32x16 acc[MB];
 
-    // activations of tile T: lane supplies pixel T*32 + lane % 32, channels
-    // 16 s + 8 (lane / 32) .. +7 (zero past the image or past Cin)
+    // STAGED: activations of item I's tile as units u = 64 k + lane of the
+    // tile's contiguous run (coalesced), later written to the wave's tile in
+    // LDS.  Otherwise: straight into operand layout, k = slice, lane l holding
+    // channels 16k + 8 (l / 32) .. +7 of pixel l % 32.  Zero past the image or
+    // past Cin.
 #define PW_LOAD(B, I)                                                                        \
     do {                                                                                     \
-        const int p_ = ((I) / nmh) * 32 + frow;                                              \
-        const bool pin_ = (I) < nitems && p_ < npix;                                         \
-        _Pragma("unroll") for (int s = 0; s < KS; ++s) {                                     \
-            const bool ok_ = pin_ && s * 16 + 8 * h < cin;                                   \
-            (B)[s] = load16(xr, ok_ ? (p_ * cin + s * 16 + 8 * h) * 2 : kOOB);               \
+        const int p0_ = ((I) / nmh) * 32;                                                    \
+        const bool tin_ = (I) < nitems;                                                      \
+        _Pragma("unroll") for (int k = 0; k < KS; ++k) {                                     \
+            if (STAGED) {                                                                    \
+                const int u_ = k * 64 + lane;                                                \
+                const int pl_ = (u_ * cin8_magic) >> 16;                                     \
+                const bool ok_ = tin_ && u_ < tunits && p0_ + pl_ < npix;                    \
+                (B)[k] = load16(xr, ok_ ? (p0_ * cin + u_ * 8) * 2 : kOOB);                  \
+            } else {                                                                         \
+                const bool ok_ = tin_ && p0_ + frow < npix && k * 16 + 8 * h < cin;          \
+                (B)[k] = load16(xr, ok_ ? ((p0_ + frow) * cin + k * 16 + 8 * h) * 2 : kOOB); \
+            }                                                                                \
+        }                                                                                    \
+    } while (0)
+    // STAGED: the loaded units into the wave's tile at the odd pixel pitch
+#define PW_STAGE(B)                                                                          \
+    do {                                                                                     \
+        if (STAGED) {                                                                        \
+            _Pragma("unroll") for (int k = 0; k < KS; ++k) {                                 \
+                const int u_ = k * 64 + lane;                                                \
+                const int pl_ = (u_ * cin8_magic) >> 16;                                     \
+                if (u_ < tunits)                                                             \
+                    *reinterpret_cast<uint4*>(xt + (pl_ * P + u_ - pl_ * cin8) * 16) = (B)[k]; \
+            }                                                                                \
         }                                                                                    \
     } while (0)
 
@@ -105,6 +143,7 @@ __global__ __launch_bounds__(kPwThreads, 2) void pw_kernel(const bf16_t* __restr
 #define PW_TILE(B, I)                                                                        \
     do {                                                                                     \
         const int T = (I) / nmh, c0_ = ((I) - T * nmh) * (MB * 32);                          \
+        PW_STAGE(B);                                                                         \
         _Pragma("unroll") for (int mb = 0; mb < MB; ++mb)                                    \
             _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                  \
                 const float4 b4_ = *reinterpret_cast<const float4*>(&sb[c0_ + mb * 32 + 8 * q + 4 * h]); \
@@ -113,12 +152,17 @@ __global__ __launch_bounds__(kPwThreads, 2) void pw_kernel(const bf16_t* __restr
                 acc[mb][4 * q + 2] = b4_.z;                                                  \
                 acc[mb][4 * q + 3] = b4_.w;                                                  \
             }                                                                                \
-        _Pragma("unroll") for (int s = 0; s < KS; ++s)                                       \
-            _Pragma("unroll") for (int mb = 0; mb < MB; ++mb) {                              \
-                const bf16x8 a_ = *reinterpret_cast<const bf16x8*>(a_base + ((c0_ + mb * 32) * P + 2 * s) * 16); \
-                acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_, __builtin_bit_cast(bf16x8, (B)[s]), \
-                                                                 acc[mb], 0, 0, 0);          \
+        /* slices past Cin are skipped: their weight reads would run past a row */          \
+        _Pragma("unroll") for (int s = 0; s < KS; ++s) {                                     \
+            if (s * 16 < cin) {                                                              \
+                const bf16x8 b_ = STAGED ? *reinterpret_cast<const bf16x8*>(b_base + 2 * s * 16) \
+                                         : __builtin_bit_cast(bf16x8, (B)[s]);               \
+                _Pragma("unroll") for (int mb = 0; mb < MB; ++mb) {                          \
+                    const bf16x8 a_ = *reinterpret_cast<const bf16x8*>(a_base + ((c0_ + mb * 32) * P + 2 * s) * 16); \
+                    acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_, b_, acc[mb], 0, 0, 0); \
+                }                                                                            \
             }                                                                                \
+        }                                                                                    \
         int pix_[2];                                                                         \
         _Pragma("unroll") for (int e = 0; e < 2; ++e) {                                      \
             const int p_ = (T) * 32 + 16 * e + (lane & 15);                                  \
@@ -177,51 +221,84 @@ __global__ __launch_bounds__(kPwThreads, 2) void pw_kernel(const bf16_t* __restr
         PW_TILE(b1, it + nw);
     }
 #undef PW_LOAD
+#undef PW_STAGE
 #undef PW_TILE
 }
 
-template <int MB, int KS>
+// LDS bytes of one workgroup: weights plus one activation tile per wave.
+long long pw_lds_bytes(int cin, int rows, bool staged) {
+    return (long long)(rows + (staged ? kPwWaves * 32 : 0)) * pw_pitch(cin) * 16;
+}
+
+// Activations through LDS (coalesced 1 KB loads) for narrow inputs and wide
+// outputs, where it was measured faster; straight into operand registers
+// otherwise (wide inputs keep two workgroups per CU that way).
+bool pw_staged(int cin, int cout) { return cin <= 128 && cout >= 128; }
+
+template <int MB, int KS, bool STAGED>
 hipError_t launch_pw(const Shape& s, const bf16_t* x, const bf16_t* w, const float* b, bf16_t* y,
                      hipStream_t st) {
-    auto kern = pw_kernel<MB, KS>;
+    auto kern = pw_kernel<MB, KS, STAGED>;
     const int npix = s.N * s.Ho * s.Wo;
     const int ntiles = (npix + 31) / 32;
     const int nmh = (s.Cout + MB * 32 - 1) / (MB * 32);
+    const long long lds = pw_lds_bytes(s.Cin, nmh * MB * 32, STAGED);
+    // unit -> pixel of a tile: (u * magic) >> 16 == u / (Cin/8) for u < 32*Cin/8
+    const int cin8 = s.Cin / 8, magic = (65536 + cin8 - 1) / cin8;
     int dev = 0;
     (void)hipGetDevice(&dev);
-    const long long resident = (long long)cu_count(dev) * blocks_per_cu(kern, kPwThreads, dev);
-    const long long want = ((long long)ntiles * nmh + 3) / 4;
+    const int by_regs = blocks_per_cu(kern, kPwThreads, dev);
+    const int by_lds = (int)(163840 / (lds + kPwMaxCout * 4));
+    const int bpc = by_lds < by_regs ? (by_lds < 1 ? 1 : by_lds) : by_regs;
+    // at most two workgroups per CU: with more, the waves' activation streams
+    // evict each other's lines from L1 between the slices that share them
+    // (measured slower)
+    const long long resident = (long long)cu_count(dev) * (bpc < 2 ? bpc : 2);
+    const long long want = ((long long)ntiles * nmh + kPwWaves - 1) / kPwWaves;
     const int grid = (int)(want < resident ? want : resident);
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(kPwThreads), 0, st, x, w, b, y, npix, s.Cin, s.Cout, ntiles, nmh,
-                       (s.epilogue & CONV2D_EPI_BIAS) ? 1 : 0, (s.epilogue & CONV2D_EPI_RELU) ? 1 : 0);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kPwThreads), (unsigned)lds, st, x, w, b, y, npix, s.Cin, s.Cout,
+                       ntiles, nmh, (s.epilogue & CONV2D_EPI_BIAS) ? 1 : 0, (s.epilogue & CONV2D_EPI_RELU) ? 1 : 0,
+                       magic);
     return hipGetLastError();
 }
 
-template <int MB>
+template <int MB, bool STAGED>
 hipError_t launch_pw_ks(const Shape& s, const bf16_t* x, const bf16_t* w, const float* b, bf16_t* y,
                         hipStream_t st) {
     const int ks = (s.Cin + 15) / 16;
-    if (ks <= 4) return launch_pw<MB, 4>(s, x, w, b, y, st);
-    if (ks <= 8) return launch_pw<MB, 8>(s, x, w, b, y, st);
-    if (ks <= 12) return launch_pw<MB, 12>(s, x, w, b, y, st);
-    return launch_pw<MB, 16>(s, x, w, b, y, st);
+    if (ks <= 4) return launch_pw<MB, 4, STAGED>(s, x, w, b, y, st);
+    if (ks <= 8) return launch_pw<MB, 8, STAGED>(s, x, w, b, y, st);
+    if (ks <= 12) return launch_pw<MB, 12, STAGED>(s, x, w, b, y, st);
+    if constexpr (MB <= 2 && !STAGED) return launch_pw<MB, 16, STAGED>(s, x, w, b, y, st);
+    return hipErrorInvalidValue;  // more than 192 input channels: at most two blocks, not staged
+}
+
+template <int MB>
+hipError_t launch_pw_mb(const Shape& s, const bf16_t* x, const bf16_t* w, const float* b, bf16_t* y,
+                        hipStream_t st) {
+    if (pw_staged(s.Cin, s.Cout)) return launch_pw_ks<MB, true>(s, x, w, b, y, st);
+    return launch_pw_ks<MB, false>(s, x, w, b, y, st);
 }
 
 }  // namespace
 
-// 32-row output-channel blocks per work item (the launcher's choice).
-int pw_blocks(int cout) {
+// 32-row output-channel blocks per work item (the launcher's choice): up to
+// four, up to two with more than 192 input channels (register budget).
+int pw_blocks(int cin, int cout) {
     const int mb = (cout + 31) / 32;
-    return mb <= 1 ? 1 : mb <= 2 ? 2 : 4;
+    const int cap = cin > 192 ? 2 : 4;
+    const int b = mb <= 1 ? 1 : mb <= 2 ? 2 : 4;
+    return b < cap ? b : cap;
 }
 
 bool pointwise_supports(const Shape& s) {
     const long long npix = (long long)s.N * s.Ho * s.Wo;
-    const int mb = pw_blocks(s.Cout);
+    const int mb = pw_blocks(s.Cin, s.Cout);
     const long long rows = (long long)(s.Cout + mb * 32 - 1) / (mb * 32) * (mb * 32);
     return s.Kh == 1 && s.Kw == 1 && s.stride == 1 && s.pad == 0 && s.groups == 1 && s.dtype == CONV2D_BF16 &&
            s.Cin % 8 == 0 && s.Cin <= 256 && s.Cout % 4 == 0 && s.Cout <= kPwMaxCout &&
            rows * pw_pitch(s.Cin) * 16 <= kPwMaxLds &&
+           pw_lds_bytes(s.Cin, (int)rows, pw_staged(s.Cin, s.Cout)) + kPwMaxCout * 4 <= 163840 &&
            npix * s.Cin * 2 < 0x7fff0000LL && npix * s.Cout * 2 < 0x7fff0000LL;
 }
 
@@ -232,10 +309,10 @@ hipError_t launch_pointwise(const Shape& s, const void* x, const void* w_packed,
     const bf16_t* xt = static_cast<const bf16_t*>(x);
     const bf16_t* wt = static_cast<const bf16_t*>(w_packed);
     bf16_t* yt = static_cast<bf16_t*>(y);
-    const int mb = pw_blocks(s.Cout);
-    if (mb == 1) return launch_pw_ks<1>(s, xt, wt, bias, yt, st);
-    if (mb == 2) return launch_pw_ks<2>(s, xt, wt, bias, yt, st);
-    return launch_pw_ks<4>(s, xt, wt, bias, yt, st);
+    const int mb = pw_blocks(s.Cin, s.Cout);
+    if (mb == 1) return launch_pw_mb<1>(s, xt, wt, bias, yt, st);
+    if (mb == 2) return launch_pw_mb<2>(s, xt, wt, bias, yt, st);
+    return launch_pw_mb<4>(s, xt, wt, bias, yt, st);
 }
 
 }  // namespace conv2d

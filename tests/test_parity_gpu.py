@@ -186,7 +186,7 @@ def _sweep():
         (2, 256, 9, 11, 64, 1, 1, 1, 0, 1, 1), (1, 64, 13, 17, 256, 1, 1, 1, 0, 1, 1),
         (1, 144, 7, 9, 24, 1, 1, 1, 0, 1, 1), (1, 32, 5, 5, 20, 1, 1, 1, 0, 1, 1),
         (16, 16, 64, 70, 16, 1, 1, 1, 0, 1, 1), (1, 264, 3, 5, 16, 1, 1, 1, 0, 1, 1),
-        (1, 16, 4, 6, 272, 1, 1, 1, 0, 1, 1),
+        (1, 16, 4, 6, 272, 1, 1, 1, 0, 1, 1), (2, 40, 9, 7, 136, 1, 1, 1, 0, 1, 1),
     ]
     return cases
 
