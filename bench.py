@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """conv2d forward throughput on one MI355X, against the kernel's roofline.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--layer CID:LI | --all]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--layer CID:LI | --separable | --all]
 
 A step is one forward pass of the workload layer through the timed C entry
 ``conv2d_fwd_nhwc_packed`` (channels-last activations already resident in
@@ -9,7 +9,10 @@ HBM, weights packed once beforehand): host plan -> kernel with the fused
 bias+ReLU epilogue.  The default workload is the 3x3 bf16 layer
 N=32, 128x112x112 -> 256, stride 1, pad 1, bias+ReLU (implicit GEMM with
 M=256, K=1152, N*Ho*Wo=401408).  ``--layer`` / ``--all`` time the other
-workload layers (one JSON line each).
+workload layers (one JSON line each); ``--separable`` times the
+depthwise-separable pair of config 3 as one fused pass
+(``conv2d_fwd_separable_nhwc``: 3x3 depthwise + bias + ReLU, then the 1x1
+144 -> 24, the intermediate kept on chip).
 
 Timing: W untimed warm-up steps, then exactly K steps between two
 torch.cuda.synchronize() calls (wall clock -> ms_per_step and value).  Input
@@ -52,9 +55,9 @@ PEAK_FP32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 ROTATE_BYTES = 512 << 20
 METRIC = "conv2d fwd TFLOP/s (GB/s for depthwise) and % of MI355X roofline, 1 GPU"
-KERNEL_SOURCES = {"direct": ["direct.hip"], "depthwise": ["depthwise.hip"],
+KERNEL_SOURCES = {"direct": ["direct.hip"], "depthwise": ["depthwise.hip", "dwrow.hpp"],
                   "gemm1x1": ["pointwise.hip", "igemm.hip"], "igemm_gather": ["igemm.hip"],
-                  "igemm_halo": ["igemm_halo.hip"]}
+                  "igemm_halo": ["igemm_halo.hip"], "separable": ["separable.hip", "dwrow.hpp"]}
 
 
 def out_hw(ly):
@@ -100,6 +103,17 @@ def measured_traffic(key, path_name):
     if not entry or entry.get("source_digest") != source_digest(path_name):
         return None
     return entry.get("hbm_bytes_per_launch")
+
+
+def _builder():
+    """The library's build module, loaded by path: importing it through the
+    package would first load the (possibly stale or missing) library."""
+    import importlib.util
+    path = os.path.join(ROOT, "cnn_convolution_conv2d_amd", "build.py")
+    spec = importlib.util.spec_from_file_location("conv2d_build", path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
 
 
 def host_cpu():
@@ -235,13 +249,133 @@ def bench_layer(cid, li, steps, warmup, cpu_seconds, with_cpu):
     return line
 
 
+def separable_algorithmic():
+    """Nominal FLOPs (depthwise + 1x1) and bytes (x, both weights, both
+    biases and y, each once; the intermediate never reaches memory) of the
+    fused depthwise-separable pass."""
+    dw, pw = ci.layer(3, 0), ci.layer(3, 1)
+    fd, _ = algorithmic(dw)
+    fp, _ = algorithmic(pw)
+    ho, wo = out_hw(dw)
+    nbytes = 2 * (dw.N * dw.Cin * dw.H * dw.W + dw.Cin * 9 + pw.Cout * pw.Cin + dw.N * pw.Cout * ho * wo)
+    nbytes += 4 * (dw.Cin if dw.epilogue & ci.EPI_BIAS else 0)
+    nbytes += 4 * (pw.Cout if pw.epilogue & ci.EPI_BIAS else 0)
+    return fd + fp, nbytes
+
+
+def separable_cpu_baseline(x, wdw, bdw, wpw, bpw, target_s):
+    """The oracle's block (depthwise, bf16 intermediate, 1x1) on whole images
+    of the workload until target_s elapses; GB/s of the fused pass."""
+    import oracle
+    dw, pw = ci.layer(3, 0), ci.layer(3, 1)
+    _, nbytes = separable_algorithmic()
+    k = 0
+    t0 = time.perf_counter()
+    while k < dw.N and (k == 0 or time.perf_counter() - t0 < target_s):
+        oracle.separable(x[k:k + 1], wdw, wpw, bdw, bpw, dw.stride, dw.pad,
+                         dw_relu=bool(dw.epilogue & ci.EPI_RELU), pw_relu=bool(pw.epilogue & ci.EPI_RELU))
+        k += 1
+    dt = time.perf_counter() - t0
+    return {"value": round(nbytes * (k / dw.N) / dt / 1e9, 6), "unit": "GB/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"first {k} of {dw.N} images, all channels, fp64 depthwise + 1x1 ({dt:.1f} s)",
+            "host_cpu": host_cpu()}
+
+
+def bench_separable(steps, warmup, cpu_seconds, with_cpu):
+    """Config 3's pair as one fused pass, timed like a layer."""
+    import torch
+    import cnn_convolution_conv2d_amd as c2
+
+    dw, pw = ci.layer(3, 0), ci.layer(3, 1)
+    ho, wo = out_hw(dw)
+    N, C, Cout = dw.N, dw.Cin, pw.Cout
+    flops, nbytes = separable_algorithmic()
+    x, wdw, bdw = ci.layer_tensors(3, 0)
+    _, wpw, bpw = ci.layer_tensors(3, 1, N=1, H=1, W=1)
+    dev = torch.device("cuda", torch.cuda.current_device())
+    stream = torch.cuda.current_stream()
+    wd = torch.from_numpy(wdw).to(dev).to(torch.bfloat16)
+    wdp = torch.empty(c2.conv2d_packed_weight_bytes(C, C, 3, 3, C, c2.BF16) // 2, dtype=torch.bfloat16,
+                      device=dev)
+    c2.conv2d_pack_weights(wd, wdp, C, C, 3, 3, C, c2.BF16)
+    wpd = torch.from_numpy(wpw.reshape(Cout, C)).to(dev).to(torch.bfloat16).contiguous()
+    bdd = torch.from_numpy(bdw).to(dev) if bdw is not None else None
+    bpd = torch.from_numpy(bpw).to(dev) if bpw is not None else None
+    set_bytes = 2 * (x.size + N * Cout * ho * wo)
+    R = max(1, min(16, math.ceil(ROTATE_BYTES / set_bytes)))
+    x_nchw = torch.from_numpy(x).to(dev).to(torch.bfloat16)
+    x0 = torch.empty((N, dw.H, dw.W, C), dtype=torch.bfloat16, device=dev)
+    c2.conv2d_nchw_to_nhwc(x_nchw, x0, N, C, dw.H, dw.W, c2.BF16)
+    xs = [x0] + [x0.clone() for _ in range(R - 1)]
+    ys = [torch.empty((N, ho, wo, Cout), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+    del x_nchw, wd
+
+    def step(i):
+        j = i % R
+        c2.conv2d_fwd_separable_nhwc(xs[j], wdp, bdd, wpd, bpd, ys[j], N, C, dw.H, dw.W, Cout,
+                                     dw.stride, dw.pad, c2.BF16, dw.epilogue, pw.epilogue, stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = np.array([a.elapsed_time(e) for a, e in ev])
+    mean_ms = float(launch_ms.mean())
+    ms_per_step = wall * 1e3 / steps
+    value = nbytes / (ms_per_step * 1e-3) / 1e9
+    achieved = nbytes / (mean_ms * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded, workload shapes and distributions; no dataset)",
+        "config": {
+            "workload": f"cfg3 fused depthwise-separable: N={N} C={C} {dw.H}x{dw.W}, 3x3 depthwise "
+                        f"s{dw.stride} p{dw.pad} bias relu -> 1x1 {C}->{Cout}",
+            "layout": "NHWC activations, packed weights", "path": "separable",
+            "gflop_per_step": round(flops / 1e9, 4), "algorithmic_mb_per_step": round(nbytes / 1e6, 3),
+            "rotating_buffer_sets": R, "device": torch.cuda.get_device_name(dev),
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 3), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": measured_traffic("cfg3:separable", "separable"),
+            "kernel_mean_us": round(mean_ms * 1e3, 3),
+            "kernel_median_us": round(float(np.median(launch_ms)) * 1e3, 3),
+        },
+    }
+    if with_cpu:
+        line["cpu_baseline"] = separable_cpu_baseline(x, wdw, bdw, wpw, bpw, cpu_seconds)
+    return line
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--layer", default="2:0", help="workload layer as CID:LAYER_INDEX")
-    ap.add_argument("--all", action="store_true", help="time every workload layer")
+    ap.add_argument("--all", action="store_true", help="time every workload layer and the fused pair")
+    ap.add_argument("--separable", action="store_true",
+                    help="time the fused depthwise-separable pair of config 3")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -269,15 +403,22 @@ def main(argv=None):
         print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
                           "dispatches": 5}))
         return 0
-    from cnn_convolution_conv2d_amd import build as b
+    b = _builder()
     if not os.path.exists(b.OUT):
         b.build()
+    if a.separable and not a.all:
+        print(json.dumps(bench_separable(a.steps, a.warmup, a.cpu_seconds,
+                                         with_cpu=not a.no_cpu_baseline)), flush=True)
+        return 0
     layers = [(c, i) for c in sorted(ci.WORKLOADS) for i in range(len(ci.WORKLOADS[c].layers))] \
         if a.all else [tuple(int(v) for v in a.layer.split(":"))]
     for cid, li in layers:
         line = bench_layer(cid, li, a.steps, a.warmup, a.cpu_seconds,
                            with_cpu=not a.no_cpu_baseline)
         print(json.dumps(line), flush=True)
+        if a.all and cid == 3 and li == len(ci.WORKLOADS[3].layers) - 1:
+            print(json.dumps(bench_separable(a.steps, a.warmup, a.cpu_seconds,
+                                             with_cpu=not a.no_cpu_baseline)), flush=True)
     return 0
 
 

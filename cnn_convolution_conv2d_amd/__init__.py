@@ -29,7 +29,8 @@ ERR_ARG, ERR_GROUPS, ERR_EMPTY_OUTPUT, ERR_UNSUPPORTED, ERR_HIP = -1, -2, -3, -4
 ERR_NULL, ERR_DTYPE, ERR_EPILOGUE, ERR_ALIGN = -6, -7, -8, -9
 
 # Every symbol include/conv2d.h declares.
-EXPORTS = ("conv2d_fwd", "conv2d_fwd_nhwc_packed", "conv2d_packed_weight_bytes",
+EXPORTS = ("conv2d_fwd", "conv2d_fwd_nhwc_packed", "conv2d_fwd_separable_nhwc",
+           "conv2d_packed_weight_bytes",
            "conv2d_pack_weights", "conv2d_nchw_to_nhwc", "conv2d_nhwc_to_nchw",
            "conv2d_out_dim", "conv2d_check_args", "conv2d_select_path",
            "conv2d_set_path_override", "conv2d_release_scratch", "conv2d_strerror",
@@ -55,6 +56,8 @@ def _load() -> ctypes.CDLL:
     for name in ("conv2d_fwd", "conv2d_fwd_nhwc_packed"):
         f = getattr(lib, name)
         f.argtypes, f.restype = conv_args, I
+    lib.conv2d_fwd_separable_nhwc.argtypes = [P] * 6 + [I] * 10 + [P]
+    lib.conv2d_fwd_separable_nhwc.restype = I
     lib.conv2d_packed_weight_bytes.argtypes = [I] * 6
     lib.conv2d_packed_weight_bytes.restype = ctypes.c_size_t
     lib.conv2d_pack_weights.argtypes = [P, P] + [I] * 6 + [P]
@@ -121,6 +124,16 @@ def conv2d_fwd_nhwc_packed(x, w_packed, bias, y, N, Cin, H, W, Cout, Kh, Kw, str
                                       Cout, Kh, Kw, stride, pad, dilation, groups, dtype, epilogue,
                                       _stream(stream)),
            "conv2d_fwd_nhwc_packed")
+
+
+def conv2d_fwd_separable_nhwc(x, w_dw, bias_dw, w_pw, bias_pw, y, N, C, H, W, Cout, stride, pad,
+                              dtype, dw_epilogue, pw_epilogue, stream=None) -> None:
+    """Fused 3x3 depthwise (+ its epilogue) then 1x1 (+ its epilogue): NHWC x,
+    packed [3][3][C] w_dw, [Cout][C] w_pw, fp32 biases or None, NHWC y."""
+    _check(lib.conv2d_fwd_separable_nhwc(_ptr(x), _ptr(w_dw), _ptr(bias_dw), _ptr(w_pw), _ptr(bias_pw),
+                                         _ptr(y), N, C, H, W, Cout, stride, pad, dtype, dw_epilogue,
+                                         pw_epilogue, _stream(stream)),
+           "conv2d_fwd_separable_nhwc")
 
 
 def conv2d_packed_weight_bytes(Cout, Cin, Kh, Kw, groups, dtype) -> int:

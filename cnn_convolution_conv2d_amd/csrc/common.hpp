@@ -17,6 +17,15 @@ struct Shape {
     int epilogue;        // CONV2D_EPI_* bits
 };
 
+// One fused depthwise-separable call (3x3 depthwise, then 1x1), validated on
+// the host.
+struct SepShape {
+    int N, C, H, W, Cout;
+    int stride, pad;
+    int Ho, Wo;
+    int dw_epilogue, pw_epilogue;  // CONV2D_EPI_* bits of each stage
+};
+
 enum Layout { NCHW = 0, NHWC = 1 };
 enum WLayout { W_OIHW = 0, W_PACKED = 1, W_DW = 2 };  // raw, [Cout][Kh][Kw][Cin/G], [Kh][Kw][C]
 
@@ -70,15 +79,16 @@ inline int cu_count(int dev) {
 }
 
 // Resident workgroups per CU of one kernel on a device (cached per kernel
-// and device id; at least 1).
-template <typename K>
-int blocks_per_cu(K kernel, int nt, int dev) {
+// and device id; at least 1).  The kernel is a template argument so that
+// every kernel, including those that share a signature, has its own cache.
+template <auto Kernel>
+int blocks_per_cu(int nt, int dev) {
     static int cache[64] = {};
     if (dev < 0 || dev >= 64) dev = 0;
     int v = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
     if (v > 0) return v;
     int b = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, kernel, nt, 0) != hipSuccess || b < 1) b = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, Kernel, nt, 0) != hipSuccess || b < 1) b = 1;
     __atomic_store_n(&cache[dev], b, __ATOMIC_RELAXED);
     return b;
 }
@@ -102,6 +112,9 @@ bool depthwise_supports(const Shape& s);
 hipError_t launch_pointwise(const Shape& s, const void* x, const void* w_packed, const float* bias,
                             void* y, hipStream_t st);
 bool pointwise_supports(const Shape& s);
+hipError_t launch_separable(const SepShape& s, const void* x, const void* w_dw, const float* b_dw,
+                            const void* w_pw, const float* b_pw, void* y, hipStream_t st);
+bool separable_supports(const SepShape& s);
 
 hipError_t launch_transpose(const void* src, void* dst, int batch, int rows, int cols,
                             int elem_bytes, hipStream_t st);

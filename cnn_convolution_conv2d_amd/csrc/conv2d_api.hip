@@ -308,6 +308,43 @@ int conv2d_fwd(const void* x, const void* w, const float* bias, void* y,
     return conv2d_nhwc_to_nchw(yn, y, N, Cout, s.Ho, s.Wo, dtype, stream);
 }
 
+int conv2d_fwd_separable_nhwc(const void* x, const void* w_dw, const float* bias_dw, const void* w_pw,
+                              const float* bias_pw, void* y, int N, int C, int H, int W, int Cout,
+                              int stride, int pad, int dtype, int dw_epilogue, int pw_epilogue,
+                              hipStream_t stream) {
+    if (dtype != CONV2D_F32 && dtype != CONV2D_BF16) return set_error(CONV2D_ERR_DTYPE, "unknown dtype %d", dtype);
+    const int known = CONV2D_EPI_BIAS | CONV2D_EPI_RELU;
+    if (dw_epilogue < 0 || (dw_epilogue & ~known) || pw_epilogue < 0 || (pw_epilogue & ~known))
+        return set_error(CONV2D_ERR_EPILOGUE, "unknown epilogue bits (depthwise 0x%x, pointwise 0x%x)",
+                         dw_epilogue, pw_epilogue);
+    if (N < 1 || C < 1 || H < 1 || W < 1 || Cout < 1)
+        return set_error(CONV2D_ERR_ARG, "sizes must be >= 1 (N=%d C=%d H=%d W=%d Cout=%d)", N, C, H, W, Cout);
+    if (stride < 1 || pad < 0) return set_error(CONV2D_ERR_ARG, "need stride>=1, pad>=0 (got %d %d)", stride, pad);
+    if (!x || !w_dw || !w_pw || !y) return set_error(CONV2D_ERR_NULL, "x, w_dw, w_pw and y must be non-NULL");
+    if ((dw_epilogue & CONV2D_EPI_BIAS) && !bias_dw)
+        return set_error(CONV2D_ERR_NULL, "bias_dw is NULL but the depthwise epilogue asks for it");
+    if ((pw_epilogue & CONV2D_EPI_BIAS) && !bias_pw)
+        return set_error(CONV2D_ERR_NULL, "bias_pw is NULL but the pointwise epilogue asks for it");
+    if ((long long)H + 2LL * pad >= INT_MAX / 2) return set_error(CONV2D_ERR_UNSUPPORTED, "padding too large");
+    const long long Ho = out_extent(H, 3, stride, pad, 1), Wo = out_extent(W, 3, stride, pad, 1);
+    if (Ho < 1 || Wo < 1) return set_error(CONV2D_ERR_EMPTY_OUTPUT, "empty output (Ho=%lld Wo=%lld)", Ho, Wo);
+    if ((long long)N * C * H * W >= INT_MAX || (long long)N * Cout * Ho * Wo >= INT_MAX)
+        return set_error(CONV2D_ERR_UNSUPPORTED, "tensor too large for 32-bit element offsets");
+    if (dtype != CONV2D_BF16)
+        return set_error(CONV2D_ERR_UNSUPPORTED, "the fused depthwise-separable kernel runs bf16 only");
+    SepShape ss;
+    ss.N = N; ss.C = C; ss.H = H; ss.W = W; ss.Cout = Cout; ss.stride = stride; ss.pad = pad;
+    ss.Ho = (int)Ho; ss.Wo = (int)Wo; ss.dw_epilogue = dw_epilogue; ss.pw_epilogue = pw_epilogue;
+    if (!separable_supports(ss))
+        return set_error(CONV2D_ERR_UNSUPPORTED,
+                         "fused depthwise-separable needs C %% 8 == 0, C <= 256, Cout %% 4 == 0, Cout <= 128, "
+                         "stride 1 or 2 and tensors below 2 GiB (got C=%d Cout=%d stride=%d)", C, Cout, stride);
+    if (!(aligned16(x) && aligned16(w_dw) && aligned16(w_pw) && aligned16(y)))
+        return set_error(CONV2D_ERR_ALIGN, "x, w_dw, w_pw and y must be 16-byte aligned");
+    const hipError_t e = launch_separable(ss, x, w_dw, bias_dw, w_pw, bias_pw, y, stream);
+    return e == hipSuccess ? CONV2D_OK : hip_fail(e, "separable launch");
+}
+
 void conv2d_release_scratch(void) {
     std::lock_guard<std::mutex> lk(g_scratch_mu);
     int cur = 0;

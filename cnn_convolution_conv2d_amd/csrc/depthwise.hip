@@ -23,24 +23,16 @@
 // Other kernel sizes, strides and dilations: the same mapping, all taps
 // loaded per output (dilated taps at kh*D, kw*D only, never a zero-filled
 // window; lpnh.cn section 4.2).
-#include "common.hpp"
+#include "dwrow.hpp"
 #include "../../include/conv2d.h"
 
 namespace conv2d {
 
 namespace {
 
+using namespace dwrow;
+
 constexpr int kThreads = 256;
-
-struct alignas(16) V8 { uint32_t u[4]; };  // 8 bf16
-
-__device__ __forceinline__ V8 load_v8(const bf16_t* p) {
-    return *reinterpret_cast<const V8*>(p);
-}
-__device__ __forceinline__ V8 zero_v8() { V8 v; v.u[0] = v.u[1] = v.u[2] = v.u[3] = 0; return v; }
-
-__device__ __forceinline__ float lo(uint32_t u) { return __uint_as_float(u << 16); }
-__device__ __forceinline__ float hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 
 __device__ __forceinline__ void fma_v8(float acc[8], const V8& x, const float w[8]) {
 #pragma unroll
@@ -63,56 +55,9 @@ __device__ __forceinline__ V8 finish(const float acc[8], const float b[8]) {
     return o;
 }
 
-// Raw buffer loads: an offset beyond the tensor returns zero, so padding taps
-// and rows outside the image cost no branch.
-constexpr int kOOB = 0x7ffffff0;
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ V8 load_v8(__amdgpu_buffer_rsrc_t r, int byte_off) {
-    return __builtin_bit_cast(V8, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
-}
-
-// 3x3, stride 1, dilation 1, any padding.
-//
-// Each input row the thread touches (its 3 columns wo-1..wo+1, 8 channels) is
-// converted once into the form the arithmetic uses and then serves the three
-// output rows that read it (rows ho-1, ho, ho+1 use it with filter rows 2, 1,
-// 0; lincklin.cn section 18 on adjacent outputs sharing inputs):
-//   - taps kw=0 and kw=1 of channel c become one bf16 pair (x[wo-1][c],
-//     x[wo][c]) built with v_perm_b32, multiplied by the matching weight pair
-//     with v_dot2c_f32_bf16 (two products and the running sum in one op);
-//   - tap kw=2 is kept as fp32 for a plain FMA.
-// The bias is the accumulator's starting value.  Two input rows of loads are
-// in flight ahead of the arithmetic (the loop is unrolled by two so that no
-// register with a pending load is ever moved).
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-struct RowX {
-    uint32_t p01[8];  // per channel: (x[wo-1][c], x[wo][c]) as a bf16 pair
-    float x2[8];      // per channel: x[wo+1][c]
-};
-
-__device__ __forceinline__ void prep_row(const V8& a, const V8& b, const V8& c, RowX& r) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        // v_perm_b32: bytes 0-3 select from the second operand, 4-7 from the first
-        r.p01[2 * i] = __builtin_amdgcn_perm(b.u[i], a.u[i], 0x05040100u);      // low halves
-        r.p01[2 * i + 1] = __builtin_amdgcn_perm(b.u[i], a.u[i], 0x07060302u);  // high halves
-        r.x2[2 * i] = lo(c.u[i]);
-        r.x2[2 * i + 1] = hi(c.u[i]);
-    }
-}
-
-__device__ __forceinline__ void row_fma(float acc[8], const RowX& r, const uint32_t wp[8], const float w2[8]) {
-#pragma unroll
-    for (int ch = 0; ch < 8; ++ch) {
-        acc[ch] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, r.p01[ch]),
-                                                  __builtin_bit_cast(bf16x2_t, wp[ch]), acc[ch], false);
-        acc[ch] = fmaf(r.x2[ch], w2[ch], acc[ch]);
-    }
-}
-
+// 3x3, stride 1, dilation 1, any padding: the row arithmetic of dwrow.hpp,
+// with two input rows of loads in flight ahead of it (the loop is unrolled by
+// two so that no register with a pending load is ever moved).
 template <int TH, bool BIAS, bool RELU>
 __global__ __launch_bounds__(kThreads) void dw3x3s1_kernel(const bf16_t* __restrict__ x,
                                                            const bf16_t* __restrict__ w,   // [3][3][C]
@@ -131,19 +76,7 @@ __global__ __launch_bounds__(kThreads) void dw3x3s1_kernel(const bf16_t* __restr
     // weights: per filter row, the (kw0, kw1) pair of each channel and kw2 in fp32
     uint32_t wp[3][8];
     float w2[3][8];
-#pragma unroll
-    for (int kh = 0; kh < 3; ++kh) {
-        const V8 a = load_v8(w + (kh * 3 + 0) * s.Cin + c0);
-        const V8 b = load_v8(w + (kh * 3 + 1) * s.Cin + c0);
-        const V8 c = load_v8(w + (kh * 3 + 2) * s.Cin + c0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            wp[kh][2 * i] = __builtin_amdgcn_perm(b.u[i], a.u[i], 0x05040100u);
-            wp[kh][2 * i + 1] = __builtin_amdgcn_perm(b.u[i], a.u[i], 0x07060302u);
-            w2[kh][2 * i] = lo(c.u[i]);
-            w2[kh][2 * i + 1] = hi(c.u[i]);
-        }
-    }
+    load_taps<4>(w, s.Cin, c0, wp, w2);
     float b0[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) b0[i] = BIAS ? bias[c0 + i] : 0.0f;

@@ -247,7 +247,7 @@ hipError_t launch_pw(const Shape& s, const bf16_t* x, const bf16_t* w, const flo
     const int cin8 = s.Cin / 8, magic = (65536 + cin8 - 1) / cin8;
     int dev = 0;
     (void)hipGetDevice(&dev);
-    const int by_regs = blocks_per_cu(kern, kPwThreads, dev);
+    const int by_regs = blocks_per_cu<pw_kernel<MB, KS, STAGED>>(kPwThreads, dev);
     const int by_lds = (int)(163840 / (lds + kPwMaxCout * 4));
     const int bpc = by_lds < by_regs ? (by_lds < 1 ? 1 : by_lds) : by_regs;
     // at most two workgroups per CU: with more, the waves' activation streams

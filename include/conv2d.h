@@ -117,6 +117,36 @@ int conv2d_fwd_nhwc_packed(const void* x, const void* w_packed, const float* bia
                            int dtype, int epilogue, hipStream_t stream);
 
 /*
+ * conv2d_fwd_separable_nhwc -- the depthwise-separable block as one fused
+ * pass (lincklin.cn lesson 9, section 25; lpnh.cn section 4.1; lnrq.cn
+ * section 3.1): a 3x3 depthwise convolution (groups == C, stride S, padding
+ * P, dilation 1) with its epilogue, then a 1x1 convolution C -> Cout with
+ * its own epilogue:
+ *   t[n,c,ho,wo]  = bf16( epi_dw( sum_{kh,kw<3} X[n,c,ho*S+kh-P,wo*S+kw-P]
+ *                                               . w_dw[c,kh,kw] ) )
+ *   Y[n,co,ho,wo] = epi_pw( sum_{c<C} t[n,c,ho,wo] . w_pw[co,c] )
+ * t is what a separate depthwise layer would store (bias, then ReLU, then
+ * rounding to nearest even); it stays on chip and is never written to
+ * memory.  Ho = floor((H + 2P - 3)/S) + 1, likewise Wo.
+ *   x       [N][H][W][C]      bf16 (NHWC)
+ *   w_dw    [3][3][C]         bf16: conv2d_pack_weights of the [C][1][3][3]
+ *                             depthwise weight (Cout = Cin = groups = C)
+ *   bias_dw fp32 [C], required iff dw_epilogue has CONV2D_EPI_BIAS
+ *   w_pw    [Cout][C]         bf16 (the [Cout][C][1][1] weight as it is)
+ *   bias_pw fp32 [Cout], required iff pw_epilogue has CONV2D_EPI_BIAS
+ *   y       [N][Ho][Wo][Cout] bf16 (NHWC), written completely
+ * Runs dtype CONV2D_BF16 with C % 8 == 0, C <= 256, Cout % 4 == 0,
+ * Cout <= 128 and stride 1 or 2; other valid calls return
+ * CONV2D_ERR_UNSUPPORTED (run the two layers through conv2d_fwd_nhwc_packed
+ * instead).  x, w_dw, w_pw and y must be 16-byte aligned.  Allocates
+ * nothing; errors as for the other entries.
+ */
+int conv2d_fwd_separable_nhwc(const void* x, const void* w_dw, const float* bias_dw,
+                              const void* w_pw, const float* bias_pw, void* y,
+                              int N, int C, int H, int W, int Cout, int stride, int pad,
+                              int dtype, int dw_epilogue, int pw_epilogue, hipStream_t stream);
+
+/*
  * Packed weight layout (the reduction order the NHWC kernels walk: tap
  * (kh, kw) outer, input channel inner; the row/column order of W_matrix,
  * lincklin.cn section 7, with K ordered to match channels-last input):

@@ -185,3 +185,32 @@ def round_to_bf16(v):
     out = r.view(np.float32).astype(np.float64)
     out[np.isnan(a)] = np.nan
     return out
+
+
+def bf16_round(v):
+    """Round fp64 values to the nearest bf16 (8 significant bits, fp32's
+    exponent range), ties to even, in one step from the fp64 value; returned
+    as fp64.  Magnitudes past the largest bf16 become infinities; below
+    2**-126 the spacing stays 2**-133 (subnormals)."""
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    out = v.copy()
+    fin = np.isfinite(v) & (v != 0)
+    _, e = np.frexp(v[fin])  # |v| = m * 2**e with 0.5 <= m < 1
+    ulp = np.ldexp(1.0, np.maximum(e, -125) - 8)
+    out[fin] = np.round(v[fin] / ulp) * ulp  # np.round: half to even; the scaling is exact
+    big = np.abs(out) > np.ldexp(255.0 / 128.0, 127)  # largest finite bf16: (2 - 2**-7) * 2**127
+    out[big] = np.copysign(np.inf, out[big])
+    return out
+
+
+def separable(x, w_dw, w_pw, bias_dw=None, bias_pw=None, stride=1, pad=1, dw_relu=True,
+              pw_relu=False, lib=None):
+    """The depthwise-separable block (page "How a GPU executes NN convolution",
+    lincklin.cn, section 25; "lnrq.cn" section 3.1): the 3x3 depthwise
+    convolution (groups = C) with its bias and ReLU, its result rounded to
+    bf16 (the value a depthwise layer stores), then the 1x1 convolution with
+    its own bias and ReLU.  Returns (y, S), S = sum over the C input channels
+    of |t * w_pw| for each output (t the rounded intermediate)."""
+    C = np.asarray(x).shape[1]
+    t, _ = conv2d(x, w_dw, bias_dw, stride, pad, 1, C, relu=dw_relu, with_scale=False, lib=lib)
+    return conv2d(bf16_round(t), w_pw, bias_pw, 1, 0, 1, 1, relu=pw_relu, lib=lib)

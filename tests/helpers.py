@@ -11,9 +11,20 @@ import conv_inputs as ci
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
+def builder():
+    """The library's build module, loaded by path: importing it through the
+    package would first load the (possibly stale or missing) library."""
+    import importlib.util
+    path = os.path.join(ROOT, "cnn_convolution_conv2d_amd", "build.py")
+    spec = importlib.util.spec_from_file_location("conv2d_build", path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
 def ensure_built():
     """Build libconv2d.so if it is missing (tests load what is built)."""
-    from cnn_convolution_conv2d_amd import build as b
+    b = builder()
     if not os.path.exists(b.OUT):
         b.build(verbose=False)
 
@@ -119,3 +130,27 @@ def run_nchw(x_nchw, w, bias, stride, pad, dil, groups, dtype, epilogue):
                   lib_dtype(dtype), epilogue)
     torch.cuda.synchronize()
     return yd.float().cpu().numpy().astype(np.float64)
+
+
+def run_separable(x_nchw, w_dw, b_dw, w_pw, b_pw, stride, pad, dw_epilogue, pw_epilogue,
+                  return_dev=False):
+    """x (NCHW float32 values), w_dw [C][1][3][3], w_pw [Cout][C][1][1] -> the
+    fused depthwise-separable entry (bf16) -> NCHW float64 result."""
+    import torch
+    import cnn_convolution_conv2d_amd as c2
+    N, C, H, W = x_nchw.shape
+    Cout = w_pw.shape[0]
+    Ho = c2.conv2d_out_dim(H, 3, stride, pad, 1)
+    Wo = c2.conv2d_out_dim(W, 3, stride, pad, 1)
+    xd = to_dev(ci.nchw_to_nhwc(x_nchw), ci.BF16)
+    wdp = pack_weights(to_dev(w_dw, ci.BF16), C, C, 3, 3, C, ci.BF16)
+    wpd = to_dev(np.asarray(w_pw).reshape(Cout, C), ci.BF16)
+    bdd = None if b_dw is None else torch.from_numpy(np.asarray(b_dw, np.float32)).cuda()
+    bpd = None if b_pw is None else torch.from_numpy(np.asarray(b_pw, np.float32)).cuda()
+    yd = torch.full((N, Ho, Wo, Cout), float("nan"), dtype=torch.bfloat16, device="cuda")
+    c2.conv2d_fwd_separable_nhwc(xd, wdp, bdd, wpd, bpd, yd, N, C, H, W, Cout, stride, pad, c2.BF16,
+                                 dw_epilogue, pw_epilogue)
+    torch.cuda.synchronize()
+    if return_dev:
+        return yd
+    return ci.nhwc_to_nchw(yd.float().cpu().numpy()).astype(np.float64)

@@ -90,6 +90,35 @@ def test_forward_entries_reject_bad_args_before_any_gpu_work():
     assert c2.lib.conv2d_nhwc_to_nchw(P, P, 1, 8, 9, 9, 5, None) == c2.ERR_DTYPE
 
 
+def _sep_call(x=P, wd=P, bd=P, wq=P, bq=P, y=P, **over):
+    a = dict(N=1, C=144, H=9, W=9, Cout=24, stride=1, pad=1, dtype=c2.BF16,
+             dw=c2.EPI_BIAS | c2.EPI_RELU, pw=c2.EPI_NONE)
+    a.update(over)
+    return c2.lib.conv2d_fwd_separable_nhwc(x, wd, bd, wq, bq, y, a["N"], a["C"], a["H"], a["W"],
+                                            a["Cout"], a["stride"], a["pad"], a["dtype"], a["dw"],
+                                            a["pw"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    ({"N": 0}, c2.ERR_ARG), ({"C": 0}, c2.ERR_ARG), ({"Cout": -2}, c2.ERR_ARG),
+    ({"stride": 0}, c2.ERR_ARG), ({"pad": -1}, c2.ERR_ARG),
+    ({"dtype": 7}, c2.ERR_DTYPE), ({"dw": 4}, c2.ERR_EPILOGUE), ({"pw": -1}, c2.ERR_EPILOGUE),
+    ({"x": None}, c2.ERR_NULL), ({"wd": None}, c2.ERR_NULL), ({"wq": None}, c2.ERR_NULL),
+    ({"y": None}, c2.ERR_NULL), ({"bd": None}, c2.ERR_NULL),
+    ({"bq": None, "pw": c2.EPI_BIAS}, c2.ERR_NULL),
+    ({"H": 1, "pad": 0}, c2.ERR_EMPTY_OUTPUT), ({"W": 2, "pad": 0, "stride": 2}, c2.ERR_EMPTY_OUTPUT),
+    ({"dtype": c2.F32}, c2.ERR_UNSUPPORTED), ({"C": 12}, c2.ERR_UNSUPPORTED),
+    ({"C": 264}, c2.ERR_UNSUPPORTED), ({"Cout": 22}, c2.ERR_UNSUPPORTED),
+    ({"Cout": 132}, c2.ERR_UNSUPPORTED), ({"stride": 3}, c2.ERR_UNSUPPORTED),
+    ({"x": P + 8}, c2.ERR_ALIGN), ({"wq": P + 4}, c2.ERR_ALIGN),
+])
+def test_separable_entry_rejects_bad_args_before_any_gpu_work(over, code):
+    """Every one of these returns its code from the host checks, so nothing
+    is enqueued (none of the addresses is ever dereferenced)."""
+    assert _sep_call(**over) == code
+    assert c2.last_error()
+
+
 def test_strerror_names_every_code():
     seen = set()
     for code in range(0, -10, -1):

@@ -234,6 +234,79 @@ def test_p8_separable_equals_factorised_standard_conv():
     np.testing.assert_array_equal(y, y2)
 
 
+# ------------------------------------------------------------- p8: the separable block
+
+@pytest.mark.parametrize("v,want", [
+    (1 + 2.0**-8, 1.0),                       # midpoint of 1 and 1 + 2**-7: ties to the even 1
+    (1 + 3 * 2.0**-8, 1 + 2.0**-6),           # midpoint of 1 + 2**-7 and 1 + 2**-6: even is 1 + 2**-6
+    (1 + 2.0**-8 + 2.0**-30, 1 + 2.0**-7),    # a hair above the midpoint rounds up (one rounding)
+    (-(1 + 2.0**-8 + 2.0**-30), -(1 + 2.0**-7)),
+    (3.0, 3.0), (0.0, 0.0), (-0.0, -0.0),
+    (2.0**-130, 2.0**-130),                   # subnormal, a multiple of the spacing 2**-133
+    (2.0**-134, 0.0), (3 * 2.0**-134, 2.0**-132),  # subnormal ties to even
+    ((2 - 2.0**-7) * 2.0**127, (2 - 2.0**-7) * 2.0**127),  # largest finite bf16
+    ((2 - 2.0**-8) * 2.0**127, math.inf),     # its upper midpoint ties to the even 2**128: overflow
+])
+def test_bf16_round_cases(v, want):
+    """bf16 keeps 8 significant bits and fp32's exponent range; rounding is to
+    nearest, ties to even, taken once from the exact value."""
+    got = float(oracle.bf16_round(np.array([v]))[0])
+    assert got == want and math.copysign(1, got) == math.copysign(1, want), (v, got, want)
+
+
+def test_bf16_round_agrees_with_bit_level_rounding_on_fp32_values():
+    """On fp32 values the fp64 rounding equals the bit-level fp32 -> bf16
+    rounding of the input generator (an independent formulation)."""
+    rng = np.random.default_rng(11)
+    a = (rng.standard_normal(200000) * 10.0 ** rng.integers(-40, 38, 200000)).astype(np.float32)
+    a = a[np.isfinite(a)]
+    want = ci.bf16_bits_to_f32(ci.f32_to_bf16_bits(a)).astype(np.float64)
+    np.testing.assert_array_equal(oracle.bf16_round(a.astype(np.float64)), want)
+
+
+@pytest.mark.parametrize("stride,pad,dw_relu,pw_relu", [(1, 1, True, False), (2, 1, True, True),
+                                                        (1, 0, False, True), (2, 2, True, False)])
+def test_p8_separable_block_matches_torch(stride, pad, dw_relu, pw_relu):
+    """The block composed from torch's own float64 convolutions: depthwise
+    (groups = C) + bias, ReLU, bf16 rounding of the intermediate, then the
+    1x1 convolution + bias (and ReLU)."""
+    rng = np.random.default_rng(20 + 4 * stride + pad)
+    N, C, H, W, Cout = 2, 16, 9, 11, 12
+    x = ci.to_storage(rng.uniform(-1, 1, (N, C, H, W)), ci.BF16)
+    wdw = ci.to_storage(rng.standard_normal((C, 1, 3, 3)) * 0.47, ci.BF16)
+    bdw = rng.standard_normal(C) * 0.01
+    wpw = ci.to_storage(rng.standard_normal((Cout, C, 1, 1)) * 0.35, ci.BF16)
+    bpw = rng.standard_normal(Cout) * 0.01
+    y, s = oracle.separable(x, wdw, wpw, bdw, bpw, stride, pad, dw_relu=dw_relu, pw_relu=pw_relu)
+    t = _torch_conv(x, wdw, bdw, stride, pad, 1, C, relu=dw_relu)
+    yt = _torch_conv(oracle.bf16_round(t), wpw, bpw, 1, 0, 1, 1, relu=pw_relu)
+    assert y.shape == (N, Cout, (H + 2 * pad - 3) // stride + 1, (W + 2 * pad - 3) // stride + 1)
+    np.testing.assert_allclose(y, yt, rtol=0, atol=1e-12 * float(s.max()))
+    # S is the sum of |t * w_pw| over the C products of each output
+    st = _torch_conv(np.abs(oracle.bf16_round(t)), np.abs(wpw), None, 1, 0, 1, 1)
+    np.testing.assert_allclose(s, st, rtol=1e-12)
+
+
+def test_p8_separable_block_without_relu_is_a_factorised_conv():
+    """On integers (the bf16 rounding is exact) and with no ReLU the block is
+    one standard convolution with W[co,c,kh,kw] = w_pw[co,c] * w_dw[c,kh,kw]
+    and bias b_pw + w_pw @ b_dw."""
+    rng = np.random.default_rng(21)
+    C, Cout = 6, 5
+    x = rng.integers(-2, 3, size=(2, C, 8, 9)).astype(np.float64)
+    wdw = rng.integers(-1, 2, size=(C, 1, 3, 3)).astype(np.float64)
+    wpw = rng.integers(-1, 2, size=(Cout, C, 1, 1)).astype(np.float64)
+    bdw = rng.integers(-4, 5, size=C).astype(np.float64)
+    bpw = rng.integers(-4, 5, size=Cout).astype(np.float64)
+    for stride in (1, 2):
+        y, _ = oracle.separable(x, wdw, wpw, bdw, bpw, stride, 1, dw_relu=False, pw_relu=False)
+        wstd = wpw[:, :, 0, 0][:, :, None, None] * wdw[:, 0][None, :, :, :]
+        # the depthwise bias is added after its sum, so it reaches every
+        # output as w_pw @ b_dw
+        yb, _ = oracle.conv2d(x, wstd, bpw + wpw[:, :, 0, 0] @ bdw, stride, 1)
+        np.testing.assert_array_equal(y, yb)
+
+
 # ------------------------------------------------------------- p9: 1x1 = GEMM
 
 def test_p9_pointwise_is_gemm():
