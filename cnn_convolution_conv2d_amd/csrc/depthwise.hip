@@ -109,11 +109,7 @@ __global__ __launch_bounds__(kThreads) void dw3x3s1_kernel(const bf16_t* __restr
         row_fma(acc, r2, wp[2], w2[2]);
         V8 o;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float a0 = acc[2 * i], a1 = acc[2 * i + 1];
-            if (RELU) { a0 = fmaxf(a0, 0.0f); a1 = fmaxf(a1, 0.0f); }
-            o.u[i] = pack_bf16x2(a0, a1);
-        }
+        for (int i = 0; i < 4; ++i) o.u[i] = pack_relu<RELU>(acc[2 * i], acc[2 * i + 1]);
         if (ho < ho1) *reinterpret_cast<V8*>(yrow + (size_t)ho * s.Wo * s.Cout) = o;
     };
 

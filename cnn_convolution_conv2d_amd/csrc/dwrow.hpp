@@ -64,16 +64,34 @@ __device__ __forceinline__ void prep_row(const Vec<NW>& a, const Vec<NW>& b, con
     }
 }
 
-// acc += one filter row applied to one prepared input row.
+// acc += one filter row applied to one prepared input row: the kw=2 tap
+// first (a three-operand FMA, so a bias held in acc's source register needs
+// no copy), then the (kw0, kw1) pair.
 template <int NW>
 __device__ __forceinline__ void row_fma(float acc[2 * NW], const RowXN<NW>& r, const uint32_t wp[2 * NW],
                                         const float w2[2 * NW]) {
 #pragma unroll
     for (int ch = 0; ch < 2 * NW; ++ch) {
+        acc[ch] = fmaf(r.x2[ch], w2[ch], acc[ch]);
         acc[ch] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, r.p01[ch]),
                                                   __builtin_bit_cast(bf16x2_t, wp[ch]), acc[ch], false);
-        acc[ch] = fmaf(r.x2[ch], w2[ch], acc[ch]);
     }
+}
+
+// Two fp32 values -> a bf16 pair (nearest even), then ReLU on the pair: a
+// bf16 is sign-magnitude, so as a 16-bit integer every negative value is
+// below zero and max(v, 0) per half zeroes exactly the negatives.  Rounding
+// keeps the sign, so this equals rounding max(v, 0) for every finite value.
+template <bool RELU>
+__device__ __forceinline__ uint32_t pack_relu(float a, float b) {
+    uint32_t p = pack_bf16x2(a, b);
+    if (!RELU) return p;
+    // keep the pair opaque: seen through, the 16-bit max splits the pair
+    // conversion into two single conversions and a permute
+    asm("" : "+v"(p));
+    typedef short s16x2 __attribute__((ext_vector_type(2)));
+    const s16x2 z = {0, 0};
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(s16x2, p), z));
 }
 
 // The 3x3 filter of channels c0..c0+2*NW-1 from the packed depthwise weights

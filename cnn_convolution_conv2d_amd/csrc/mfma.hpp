@@ -9,6 +9,7 @@ namespace conv2d {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Raw buffer access: a load whose byte offset lies beyond the descriptor's
 // size returns zero, which is how out-of-image taps (zero padding) and

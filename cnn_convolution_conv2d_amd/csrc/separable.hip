@@ -9,25 +9,31 @@
 // a workgroup computes the depthwise output of a band of RB output rows x CW
 // columns, for all C channels, into LDS, applies the 1x1 convolution to it on
 // the matrix cores and writes only the Cout final channels: the intermediate
-// never leaves the CU, and the whole block reads x once and writes y once.
+// never leaves the CU, and the block reads x once and writes y once.
 //
-// Depthwise phase.  Thread t owns 4 channels, group t % (C/4) (their 3x3
-// taps stay in its registers for the whole kernel; 4 rather than 8 channels
-// keep a thread within the register budget of four waves per SIMD), and the
-// band's output columns t / (C/4) + j * (NT / (C/4)).  For each column it
-// loads the band's input rows (consecutive threads load consecutive 8-byte
-// pieces of one row, so every wave's loads are coalesced; the neighbouring
-// columns a tap needs come through L1), runs the row arithmetic of dwrow.hpp
-// and writes the RB output pieces into the LDS tile [pixel][channel] (odd
-// pitch of 16-byte units).  The value is rounded to bf16 after the depthwise bias and ReLU:
-// the value a separate depthwise layer would store, so the fused result is
-// the two-layer chain's.
+// Input staging.  A band needs its input rows x CWI columns x C channels;
+// each input row of it is one contiguous run of the NHWC tensor, copied as
+// 16-byte units straight from memory into LDS (buffer loads to LDS, 64 units
+// per wave instruction, one row per wave, no registers); units outside the
+// image read zero, which is the zero padding.  Two staging buffers
+// alternate: the next band's rows are in flight while this band is computed.
 //
-// Pointwise phase.  Each wave takes 32-pixel tiles of the band.  The weights
-// [Cout][C] sit in LDS for the whole kernel; v_mfma_f32_32x32x16_bf16 per 32
-// output channels and 16 input channels, fp32 accumulators initialised with
-// the bias; the register epilogue (ReLU, bf16, two lane swaps) stores 16
-// bytes per lane, every pixel's channels contiguous.
+// Depthwise phase.  The threads form two halves, one per half of the band's
+// rows.  Thread t of a half owns 4 channels, group t % (C/4) (their 3x3 taps
+// stay in its registers), and column t / (C/4) of the band.  It reads its
+// window rows from the staging buffer, runs the row arithmetic of dwrow.hpp
+// (each input row prepared once and applied to the output rows that use it)
+// and writes its results into the LDS tile [pixel][channel] (odd pitch of
+// 16-byte units).  The value is rounded to bf16 after the depthwise bias and
+// ReLU: the value a separate depthwise layer would store, so the fused result
+// is the two-layer chain's.
+//
+// Pointwise phase.  The band's output is cut into blocks of 16 pixels x 16
+// output channels, spread over all waves; each is a chain of
+// v_mfma_f32_16x16x32_bf16 over the input channels, 32 at a time, with the
+// weights [Cout][C] in LDS for the whole kernel and an fp32 accumulator
+// initialised with the bias.  A lane ends with 4 consecutive output channels
+// of one pixel: ReLU, bf16, one 8-byte store.
 #include "dwrow.hpp"
 #include "../../include/conv2d.h"
 
@@ -37,242 +43,252 @@ namespace {
 
 using namespace dwrow;
 
-constexpr int kSepThreads = 512;
+constexpr int kSepThreads = 1024;
 constexpr int kSepWaves = kSepThreads / 64;
+constexpr int kSepHalf = kSepThreads / 2;          // threads of one half of a band's rows
 constexpr int kSepMaxC = 256;
 constexpr int kSepMaxCout = 128;
-constexpr int kSepKS = kSepMaxC / 16;  // 16-channel slices of the widest input
+constexpr int kSepLds = 163840 - kSepMaxCout * 4;  // dynamic LDS next to the static bias table
 
-// LDS row pitch in 16-byte units: odd (conflict-free operand reads), and at
-// least two units per 16-channel slice so that the second half of the last
-// slice is a zero unit inside the row when C % 16 == 8.
-__host__ __device__ constexpr int sep_pitch(int c) { return (2 * ((c + 15) / 16)) | 1; }
+// Row pitch of the depthwise tile and of the pointwise weights in 16-byte
+// units: odd (conflict-free operand reads) and covering whole 32-channel
+// steps of the matrix op, so the units of the last step past C are zero
+// units inside the row.
+__host__ __device__ constexpr int sep_pitch(int c) { return (4 * ((c + 31) / 32)) | 1; }
+
+// Output rows per band: seven at stride 1 (split 4 + 3 between the halves),
+// three at stride 2 (2 + 1).
+constexpr int sep_rows(int stride) { return stride == 1 ? 7 : 3; }
+
+// Input rows staged per band: those of the RB output rows, plus, when RB is
+// odd, those the second half reads for its unstored last row.
+__host__ __device__ constexpr int sep_staged_rows(int S, int RB) { return (2 * ((RB + 1) / 2) - 1) * S + 3; }
 
 struct SepGrid {
     int N, C, H, W, Ho, Wo, Cout, pad;
-    int CW;       // output columns per band
-    int nrb, ncb;  // row bands and column chunks per image
-    int nitems;   // N * nrb * ncb
-    int ptiles;   // 32-pixel tiles of one band
-    int dw_bias, dw_relu, pw_bias, pw_relu;
+    int CW;             // output columns per band
+    int nrb, ncb;       // row bands and column chunks per image
+    int nitems;         // N * nrb * ncb
+    int pblocks;        // 16-pixel blocks of one band
+    int rowp;           // 16-byte units per staged input row (a multiple of 64)
+    uint32_t cw_magic;  // ceil(2^32 / CW): p / CW == umulhi(p, cw_magic) for a band's pixels
+    int dw_bias, pw_bias, pw_relu;  // (the depthwise ReLU is a template flag)
 };
 
-// S: depthwise stride; RB: output rows per band; MB: 32-row blocks of
-// pointwise output channels (Cout <= 32 * MB).
-template <int S, int RB, int MB>
+// This wave's LDS operations complete, then the workgroup barrier.  Buffer
+// loads still in flight (the next band's staging) are not waited for.
+__device__ __forceinline__ void lds_barrier() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt at their maxima (no wait)
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Copy the input rows of band `item` into staging buffer xs, one row per
+// wave: row i of the band is the run of units [wi0 * C/8, wi0 * C/8 + rowp)
+// of image row hb + i (units outside the row, or a row outside the image,
+// read 0).
+template <int S, int RB>
+__device__ __forceinline__ void sep_stage(uint4* __restrict__ xs, const SepGrid& g, __amdgpu_buffer_rsrc_t xr,
+                                          int item, int wave, int lane) {
+    constexpr int NR = sep_staged_rows(S, RB);
+    static_assert(NR <= kSepWaves, "one staged row per wave");
+    if (wave >= NR) return;
+    const int C8 = g.C >> 3;
+    const int cb = item % g.ncb, t = item / g.ncb;
+    const int rb = t % g.nrb, n = t / g.nrb;
+    const int hi = rb * RB * S - g.pad + wave;
+    const bool rin = (unsigned)hi < (unsigned)g.H;
+    const int q0 = (cb * g.CW * S - g.pad) * C8 + lane;  // this lane's unit of the image row
+    const int rowbase = (n * g.H + hi) * g.W * C8;
+    uint4* const dst = xs + wave * g.rowp;
+    for (int ch = 0; ch < g.rowp; ch += 64) {
+        const int q = q0 + ch;
+        const bool ok = rin && (unsigned)q < (unsigned)(g.W * C8);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)(dst + ch), 16, ok ? (rowbase + q) * 16 : kOOB, 0, 0,
+                                                 0);
+    }
+}
+
+// One band: start the next band's staging (next >= 0), the depthwise phase
+// from the staged rows xc into the tile dl, then the pointwise phase from dl
+// with the weights wl and bias sb.  Every LDS buffer is a separate restrict
+// argument, so the compiler can tell the staging copies in flight apart from
+// the LDS accesses of this band and does not wait for them; the caller waits
+// for a band's staging before passing it in.
+template <int S, int RB, bool DWR>
+__device__ __forceinline__ void sep_band(const uint4* __restrict__ xc, uint4* __restrict__ xn,
+                                         uint4* __restrict__ dl, const uint4* __restrict__ wl,
+                                         const float* __restrict__ sb, const SepGrid& g,
+                                         __amdgpu_buffer_rsrc_t xr, __amdgpu_buffer_rsrc_t yr, int item, int next,
+                                         const uint32_t (&wp)[3][4], const float (&w2)[3][4], const float (&b0)[4]) {
+    constexpr int RA = (RB + 1) / 2;      // output rows of the first half (the second has RB - RA)
+    constexpr int NA = (RA - 1) * S + 3;  // input rows one half reads
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int C = g.C, P = sep_pitch(C);
+    const int cb = item % g.ncb, t = item / g.ncb;
+    const int rb = t % g.nrb, n = t / g.nrb;
+    const int ho0 = rb * RB, wo0 = cb * g.CW;
+    if (next >= 0) sep_stage<S, RB>(xn, g, xr, next, wave, lane);
+
+    // Depthwise: the two halves of the threads take output rows [0, RA) and
+    // [RA, RB) of the band (when RB is odd, the second half's last row is
+    // computed from staged rows past the band and not stored).
+    const int C4 = C >> 2;
+    const int cpp = kSepHalf / C4;  // columns per pass
+    // (a half is whole waves: r0 is uniform, which the compiler is told)
+    const int th = tid & (kSepHalf - 1), r0 = __builtin_amdgcn_readfirstlane(tid >= kSepHalf ? RA : 0);
+    const int cg = th % C4, cpos = th / C4;
+    if (cpos < cpp) {
+        // LDS byte addresses: the window origin of the thread's column and the
+        // tile pixel of its first output row, each advanced per pass; the
+        // offsets of the window rows and taps, and of the tile rows, are
+        // uniform
+        const int rowb = g.rowp * 16, tapb = C * 2, colb = S * C * 2, trow = g.CW * P * 16;
+        const char* xp = reinterpret_cast<const char*>(xc) + r0 * S * rowb + cpos * colb + cg * 8;
+        char* dp = reinterpret_cast<char*>(dl) + (r0 * g.CW + cpos) * P * 16 + cg * 8;
+        for (int c = cpos; c < g.CW; c += cpp, xp += cpp * colb, dp += cpp * P * 16) {
+            V4 raw[NA][3];
+#pragma unroll
+            for (int i = 0; i < NA; ++i)
+#pragma unroll
+                for (int kk = 0; kk < 3; ++kk) raw[i][kk] = *reinterpret_cast<const V4*>(xp + i * rowb + kk * tapb);
+            // every read of the window is issued before the first wait (left
+            // to itself the compiler waits for each read before the next)
+            __builtin_amdgcn_sched_barrier(0);
+            // input rows in order: each is prepared once, applied to the (up
+            // to three) output rows whose window covers it, and dropped; an
+            // output row is finished and written to the tile with its last
+            // filter row
+            float acc[RA][4];
+#pragma unroll
+            for (int i = 0; i < NA; ++i) {
+                RowXN<2> rx;
+                prep_row(raw[i][0], raw[i][1], raw[i][2], rx);
+#pragma unroll
+                for (int r = 0; r < RA; ++r) {
+                    const int kh = i - r * S;  // filter row of input row i for output row r0 + r
+                    if (kh < 0 || kh > 2) continue;
+                    if (kh == 0)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) acc[r][q] = b0[q];
+                    row_fma(acc[r], rx, wp[kh], w2[kh]);
+                    if (kh == 2 && (RB % 2 == 0 || r0 + r < RB))
+                        *reinterpret_cast<uint2*>(dp + r * trow) =
+                            make_uint2(pack_relu<DWR>(acc[r][0], acc[r][1]), pack_relu<DWR>(acc[r][2], acc[r][3]));
+                }
+            }
+        }
+    }
+    lds_barrier();
+
+    // Pointwise: block u is pixels 16 pb .. +15 and output channels
+    // 16 cb .. +15 of the band.  Operands of step k (input channels 32 k ..
+    // +31): weight row 16 cb + l % 16 and tile pixel 16 pb + l % 16, both at
+    // unit 4 k + l / 16; the result in lane l is output channels 16 cb +
+    // 4 (l / 16) .. +3 of pixel l % 16.
+    const int lr = lane & 15, kq = lane >> 4;
+    const int nk = (C + 31) / 32;          // 32-channel steps
+    const int nblk = (g.Cout + 15) / 16;   // 16-channel output blocks
+    for (int u = wave; u < g.pblocks * nblk; u += kSepWaves) {
+        const int pb = u / nblk, cbk = u - pb * nblk;
+        const char* ap = reinterpret_cast<const char*>(wl) + ((cbk * 16 + lr) * P + kq) * 16;
+        const char* bp = reinterpret_cast<const char*>(dl) + ((pb * 16 + lr) * P + kq) * 16;
+        const int co = cbk * 16 + 4 * kq;
+        f32x4 acc = *reinterpret_cast<const f32x4*>(&sb[co]);
+        for (int k = 0; k < nk; ++k, ap += 64, bp += 64)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(ap),
+                                                         *reinterpret_cast<const bf16x8*>(bp), acc, 0, 0, 0);
+        const int p = pb * 16 + lr;
+        const int r = __umulhi(p, g.cw_magic), c = p - r * g.CW;
+        const bool ok = r < RB && ho0 + r < g.Ho && wo0 + c < g.Wo && co < g.Cout;
+        float v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = g.pw_relu ? fmaxf(acc[q], 0.0f) : acc[q];
+        store8(yr, ok ? (((n * g.Ho + ho0 + r) * g.Wo + wo0 + c) * g.Cout + co) * 2 : kOOB,
+               make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])));
+    }
+}
+
+// S: depthwise stride; RB: output rows per band; DWR: ReLU after the
+// depthwise.
+template <int S, int RB, bool DWR>
 __global__ __launch_bounds__(kSepThreads, 4) void sep_kernel(const bf16_t* __restrict__ x,
                                                          const bf16_t* __restrict__ wdw,  // [3][3][C]
                                                          const float* __restrict__ bdw,
                                                          const bf16_t* __restrict__ wpw,  // [Cout][C]
                                                          const float* __restrict__ bpw,
                                                          bf16_t* __restrict__ y, SepGrid g) {
-    constexpr int NR = (RB - 1) * S + 3;  // input rows of a band
-    constexpr int ROWS = MB * 32;
-    // dynamic LDS: pointwise weights [ROWS][P], then the band's depthwise
-    // output [ptiles * 32 pixels][P]
+    constexpr int NR = sep_staged_rows(S, RB);
+    // dynamic LDS: pointwise weights [rows][P] (rows = Cout rounded up to
+    // 16); the band's depthwise output [pblocks * 16 pixels][P]; two staging
+    // buffers [NR][rowp] of input rows
     extern __shared__ uint4 sep_lds[];
     __shared__ __align__(16) float sbp[kSepMaxCout];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int C = g.C, C8 = C >> 3, P = sep_pitch(C);
+    const int ROWS = (g.Cout + 15) / 16 * 16;
     uint4* const wl = sep_lds;
-    uint4* const dl = sep_lds + ROWS * P;
+    uint4* const dl = wl + ROWS * P;
+    uint4* const xin = dl + g.pblocks * 16 * P;
+    const int xbuf = NR * g.rowp;  // units of one staging buffer
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)g.N * g.H * g.W * C * 2u);
+    const __amdgpu_buffer_rsrc_t yr = make_rsrc(y, (uint32_t)g.N * g.Ho * g.Wo * g.Cout * 2u);
 
-    // pointwise weights (rows past Cout and units past C are zero): all loads
-    // first, then the LDS stores
-    {
-        constexpr int kU = (ROWS * sep_pitch(kSepMaxC) + kSepThreads - 1) / kSepThreads;
-        const __amdgpu_buffer_rsrc_t wr = make_rsrc(wpw, (uint32_t)g.Cout * (uint32_t)C * 2u);
-        uint4 v[kU];
+    const int first = xcd_tile_index();
+    if (first < g.nitems) sep_stage<S, RB>(xin, g, xr, first, wave, lane);
+
+    // Set-up in one memory round trip: every load (pointwise weights with
+    // zero rows past Cout and zero units past C, the depthwise taps and bias
+    // of this thread's 4 channels, the pointwise bias) goes out before the
+    // first LDS store.
+    constexpr int kU = (kSepMaxCout * sep_pitch(kSepMaxC) + kSepThreads - 1) / kSepThreads;
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(wpw, (uint32_t)g.Cout * (uint32_t)C * 2u);
+    uint4 v[kU];
 #pragma unroll
-        for (int k = 0; k < kU; ++k) {
-            const int u = tid + k * kSepThreads;
-            const int r = u / P, c = u - r * P;
-            v[k] = load16(wr, (u < ROWS * P && r < g.Cout && c < C8) ? (r * C + c * 8) * 2 : kOOB);
-        }
-#pragma unroll
-        for (int k = 0; k < kU; ++k) {
-            const int u = tid + k * kSepThreads;
-            if (u < ROWS * P) wl[u] = v[k];
-        }
+    for (int k = 0; k < kU; ++k) {
+        const int u = tid + k * kSepThreads;
+        const int r = u / P, c = u - r * P;
+        v[k] = load16(wr, (u < ROWS * P && r < g.Cout && c < C8) ? (r * C + c * 8) * 2 : kOOB);
     }
-    for (int i = tid; i < ROWS; i += kSepThreads) sbp[i] = (g.pw_bias && i < g.Cout) ? bpw[i] : 0.0f;
-    // the pad units of every pixel of the depthwise tile are never written
-    // by the depthwise phase: zero them once
-    for (int p = tid; p < g.ptiles * 32; p += kSepThreads)
-        for (int u = C8; u < P; ++u) dl[p * P + u] = make_uint4(0, 0, 0, 0);
-
-    // depthwise taps and bias of this thread's 4 channels
-    const int C4 = C >> 2;
-    const int cpp = kSepThreads / C4;  // columns per pass
-    const int cg = tid % C4, cpos = tid / C4;
+    const int cg = (tid & (kSepHalf - 1)) % (C >> 2);
     uint32_t wp[3][4];
     float w2[3][4], b0[4];
     load_taps<2>(wdw, C, cg * 4, wp, w2);
 #pragma unroll
     for (int i = 0; i < 4; ++i) b0[i] = g.dw_bias ? bdw[cg * 4 + i] : 0.0f;
-
-    const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)g.N * g.H * g.W * C * 2u);
-    const __amdgpu_buffer_rsrc_t yr = make_rsrc(y, (uint32_t)g.N * g.Ho * g.Wo * g.Cout * 2u);
-    const int rstride = g.W * C * 2;
-
-    // pointwise operands: weight row frow of block mb, unit 2s + h; pixel
-    // frow of tile T, unit 2s + h
-    const int frow = lane & 31, h = lane >> 5;
-    const char* const a_base = reinterpret_cast<const char*>(wl) + (frow * P + h) * 16;
-    const char* const b_base = reinterpret_cast<const char*>(dl) + (frow * P + h) * 16;
-    // epilogue: this lane's 16-byte piece holds channels cl .. cl+7 of a
-    // 32-channel block, of pixel 16 e + lane % 16 (e = 0, 1) of the tile
-    const int cl = ((lane >> 4) & 1) * 16 + h * 8;
-    const bool vec16 = g.Cout % 8 == 0;
+    const float bp = (g.pw_bias && tid < g.Cout) ? bpw[tid] : 0.0f;
+#pragma unroll
+    for (int k = 0; k < kU; ++k) {
+        const int u = tid + k * kSepThreads;
+        if (u < ROWS * P) wl[u] = v[k];
+    }
+    if (tid < kSepMaxCout) sbp[tid] = bp;
+    // the pad units of every pixel of the depthwise tile are never written
+    // by the depthwise phase: zero them once
+    for (int p = tid; p < g.pblocks * 16; p += kSepThreads)
+        for (int u = C8; u < P; ++u) dl[p * P + u] = make_uint4(0, 0, 0, 0);
 
     // consecutive logical blocks (those of one XCD) take consecutive bands,
     // which share their halo rows in that XCD's L2
-    for (int item = xcd_tile_index(); item < g.nitems; item += gridDim.x) {
-        const int cb = item % g.ncb, t = item / g.ncb;
-        const int rb = t % g.nrb, n = t / g.nrb;
-        const int ho0 = rb * RB, wo0 = cb * g.CW;
-        __syncthreads();  // the previous band's pointwise reads (and the set-up stores) are done
-
-        if (cpos < cpp) {
-            const int img = n * g.H * g.W * C + cg * 4;
-            const int hb = ho0 * S - g.pad;  // input row of filter row 0 for output row ho0
-            for (int c = cpos; c < g.CW; c += cpp) {
-                const int wi0 = (wo0 + c) * S - g.pad;
-                int coff[3];
-#pragma unroll
-                for (int k = 0; k < 3; ++k)
-                    coff[k] = ((unsigned)(wi0 + k) < (unsigned)g.W) ? (img + (wi0 + k) * C) * 2 : kOOB;
-                V4 raw[NR][3];
-#pragma unroll
-                for (int i = 0; i < NR; ++i) {
-                    const bool rin = (unsigned)(hb + i) < (unsigned)g.H;
-#pragma unroll
-                    for (int k = 0; k < 3; ++k)
-                        raw[i][k] = load_v4(xr, (rin && coff[k] != kOOB) ? coff[k] + (hb + i) * rstride : kOOB);
-                }
-                RowXN<2> rx[NR];
-#pragma unroll
-                for (int i = 0; i < NR; ++i) prep_row(raw[i][0], raw[i][1], raw[i][2], rx[i]);
-#pragma unroll
-                for (int r = 0; r < RB; ++r) {
-                    float acc[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) acc[i] = b0[i];
-                    row_fma(acc, rx[r * S + 0], wp[0], w2[0]);
-                    row_fma(acc, rx[r * S + 1], wp[1], w2[1]);
-                    row_fma(acc, rx[r * S + 2], wp[2], w2[2]);
-                    uint2 o;
-                    float a[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) a[i] = g.dw_relu ? fmaxf(acc[i], 0.0f) : acc[i];
-                    o.x = pack_bf16x2(a[0], a[1]);
-                    o.y = pack_bf16x2(a[2], a[3]);
-                    // 8-byte half cg & 1 of 16-byte unit cg / 2 of the pixel's row
-                    reinterpret_cast<uint2*>(dl)[(r * g.CW + c) * P * 2 + cg] = o;
-                }
-            }
-        }
+    int k = 0;
+    for (int item = first; item < g.nitems; item += gridDim.x, ++k) {
+        const int b = k & 1;
+        // this band's staging has landed: each wave waits for its own
+        // copies, then the barrier (which also orders the previous band's
+        // pointwise reads of the tile, and the first time the set-up stores)
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
         __syncthreads();
-
-        // output-channel blocks two at a time (64 accumulators at most, next
-        // to the depthwise taps that stay live)
-        constexpr int MBG = MB < 2 ? MB : 2;
-        for (int T = wave; T < g.ptiles; T += kSepWaves) {
-            // output pixel of each half of the tile, or -1 past the band or the image
-            int pix[2];
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const int p = T * 32 + 16 * e + (lane & 15);
-                const int r = p / g.CW, c = p - r * g.CW;
-                const bool ok = r < RB && ho0 + r < g.Ho && wo0 + c < g.Wo;
-                pix[e] = ok ? ((n * g.Ho + ho0 + r) * g.Wo + wo0 + c) * g.Cout : -1;
-            }
-#pragma unroll 1
-            for (int m0 = 0; m0 < MB; m0 += MBG) {
-                f32x16 acc[MBG];
-#pragma unroll
-                for (int mb = 0; mb < MBG; ++mb)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const float4 b4 = *reinterpret_cast<const float4*>(&sbp[(m0 + mb) * 32 + 8 * q + 4 * h]);
-                        acc[mb][4 * q + 0] = b4.x;
-                        acc[mb][4 * q + 1] = b4.y;
-                        acc[mb][4 * q + 2] = b4.z;
-                        acc[mb][4 * q + 3] = b4.w;
-                    }
-                // slices past C are skipped (their weight reads would run past a row)
-#pragma unroll
-                for (int s = 0; s < kSepKS; ++s) {
-                    if (s * 16 < C) {
-                        const bf16x8 b = *reinterpret_cast<const bf16x8*>(b_base + (T * 32 * P + 2 * s) * 16);
-#pragma unroll
-                        for (int mb = 0; mb < MBG; ++mb) {
-                            const bf16x8 a =
-                                *reinterpret_cast<const bf16x8*>(a_base + ((m0 + mb) * 32 * P + 2 * s) * 16);
-                            acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[mb], 0, 0, 0);
-                        }
-                    }
-                }
-#pragma unroll
-                for (int mb = 0; mb < MBG; ++mb) {
-                    uint32_t pk[4][2];
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        float v[4];
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            v[r] = acc[mb][4 * q + r];
-                            if (g.pw_relu) v[r] = fmaxf(v[r], 0.0f);
-                        }
-                        pk[q][0] = pack_bf16x2(v[0], v[1]);
-                        pk[q][1] = pack_bf16x2(v[2], v[3]);
-                    }
-                    // D rows 8q + 4(lane/32) + r -> per lane 8 consecutive
-                    // channels of one pixel: swap the upper half of the wave
-                    // with the lower (32), then the 16-lane rows
-                    uint32_t r8[2][4];
-#pragma unroll
-                    for (int pr = 0; pr < 2; ++pr)
-#pragma unroll
-                        for (int w = 0; w < 2; ++w) {
-                            const auto sw =
-                                __builtin_amdgcn_permlane32_swap(pk[2 * pr][w], pk[2 * pr + 1][w], false, false);
-                            r8[pr][w] = sw[0];
-                            r8[pr][2 + w] = sw[1];
-                        }
-                    uint32_t o[2][4];
-#pragma unroll
-                    for (int d = 0; d < 4; ++d) {
-                        const auto sw = __builtin_amdgcn_permlane16_swap(r8[0][d], r8[1][d], false, false);
-                        o[0][d] = sw[0];
-                        o[1][d] = sw[1];
-                    }
-                    const int co = (m0 + mb) * 32 + cl;
-#pragma unroll
-                    for (int e = 0; e < 2; ++e) {
-                        const int off = (pix[e] + co) * 2;
-                        if (vec16) {
-                            store16(yr, pix[e] >= 0 && co < g.Cout ? off : kOOB,
-                                    make_uint4(o[e][0], o[e][1], o[e][2], o[e][3]));
-                        } else {
-                            store8(yr, pix[e] >= 0 && co < g.Cout ? off : kOOB, make_uint2(o[e][0], o[e][1]));
-                            store8(yr, pix[e] >= 0 && co + 4 < g.Cout ? off + 8 : kOOB,
-                                   make_uint2(o[e][2], o[e][3]));
-                        }
-                    }
-                }
-            }
-        }
+        const int next = item + (int)gridDim.x;
+        sep_band<S, RB, DWR>(xin + b * xbuf, xin + (b ^ 1) * xbuf, dl, wl, sbp, g, xr, yr, item,
+                                 next < g.nitems ? next : -1, wp, w2, b0);
     }
 }
 
-// Rows per band: four at stride 1 (6 input rows for 4 output rows), two at
-// stride 2 (5 for 2).
-constexpr int sep_rows(int stride) { return stride == 1 ? 4 : 2; }
-
 struct SepPlan {
     bool ok;
-    int mb;
     long long lds;  // dynamic LDS bytes
     SepGrid g;
 };
@@ -284,17 +300,19 @@ SepPlan sep_plan(const SepShape& s) {
     if (s.stride != 1 && s.stride != 2) return pl;
     if ((long long)s.N * s.H * s.W * s.C * 2 >= 0x7fff0000LL) return pl;
     if ((long long)s.N * s.Ho * s.Wo * s.Cout * 2 >= 0x7fff0000LL) return pl;
-    const int RB = sep_rows(s.stride);
-    const int mb = s.Cout <= 32 ? 1 : s.Cout <= 64 ? 2 : 4;
-    const long long unit = (long long)sep_pitch(s.C) * 16;  // bytes per pixel row of LDS
-    const long long wbytes = (long long)mb * 32 * unit;
-    // two workgroups per CU if a band of at least one column fits, else one
-    int cw = 0;
-    for (int per_cu = 2; per_cu >= 1 && cw < 1; --per_cu) {
-        const long long budget = 163840 / per_cu - kSepMaxCout * 4;
-        const long long px = (budget - wbytes) / unit / 32 * 32;
-        cw = (int)(px / RB < s.Wo ? px / RB : s.Wo);
-    }
+    const int S = s.stride, RB = sep_rows(S), NR = sep_staged_rows(S, RB), C8 = s.C / 8;
+    const long long unit = (long long)sep_pitch(s.C) * 16;  // bytes per pixel of the tile
+    const long long wbytes = (long long)(s.Cout + 15) / 16 * 16 * unit;
+    // band width: at most one column per thread of a channel group and half,
+    // and what LDS holds (weights, tile, two staging buffers)
+    auto rowp_of = [&](int cw) { return ((((cw - 1) * S + 3) * C8 + 63) / 64) * 64; };
+    auto lds_of = [&](int cw) {
+        const long long pblocks = (RB * cw + 15) / 16;
+        return wbytes + pblocks * 16 * unit + 2LL * NR * rowp_of(cw) * 16;
+    };
+    int cw = kSepHalf / (s.C / 4);
+    if (cw > s.Wo) cw = s.Wo;
+    while (cw > 0 && lds_of(cw) > kSepLds) --cw;
     if (cw < 1) return pl;
     const int ncb = (s.Wo + cw - 1) / cw;
     cw = (s.Wo + ncb - 1) / ncb;  // even the column chunks out
@@ -306,32 +324,31 @@ SepPlan sep_plan(const SepShape& s) {
     const long long items = (long long)s.N * g.nrb * g.ncb;
     if (items >= 0x7fffffffLL) return pl;
     g.nitems = (int)items;
-    g.ptiles = (RB * cw + 31) / 32;
+    g.pblocks = (RB * cw + 15) / 16;
+    g.rowp = rowp_of(cw);
+    g.cw_magic = (uint32_t)((0x100000000ULL + cw - 1) / cw);
     g.dw_bias = (s.dw_epilogue & CONV2D_EPI_BIAS) ? 1 : 0;
-    g.dw_relu = (s.dw_epilogue & CONV2D_EPI_RELU) ? 1 : 0;
     g.pw_bias = (s.pw_epilogue & CONV2D_EPI_BIAS) ? 1 : 0;
     g.pw_relu = (s.pw_epilogue & CONV2D_EPI_RELU) ? 1 : 0;
-    pl.mb = mb;
-    pl.lds = wbytes + (long long)g.ptiles * 32 * unit;
-    pl.ok = pl.lds + kSepMaxCout * 4 <= 163840;
+    pl.lds = lds_of(cw);
+    pl.ok = pl.lds <= kSepLds;
     return pl;
 }
 
-template <int S, int MB>
+template <int S, bool DWR>
 hipError_t launch_sep(const SepPlan& pl, const bf16_t* x, const bf16_t* wdw, const float* bdw, const bf16_t* wpw,
                       const float* bpw, bf16_t* y, hipStream_t st) {
-    auto kern = sep_kernel<S, sep_rows(S), MB>;
+    auto kern = sep_kernel<S, sep_rows(S), DWR>;
     int dev = 0;
     (void)hipGetDevice(&dev);
     static bool attr_set[64] = {};
     if (dev >= 0 && dev < 64 && !attr_set[dev]) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 163840 - kSepMaxCout * 4);
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, kSepLds);
         if (e != hipSuccess) return e;
         attr_set[dev] = true;
     }
-    const int by_regs = blocks_per_cu<sep_kernel<S, sep_rows(S), MB>>(kSepThreads, dev);
+    const int by_regs = blocks_per_cu<sep_kernel<S, sep_rows(S), DWR>>(kSepThreads, dev);
     const int by_lds = (int)(163840 / (pl.lds + kSepMaxCout * 4));
     const int bpc = by_lds < by_regs ? (by_lds < 1 ? 1 : by_lds) : by_regs;
     const long long resident = (long long)cu_count(dev) * bpc;
@@ -341,11 +358,10 @@ hipError_t launch_sep(const SepPlan& pl, const bf16_t* x, const bf16_t* wdw, con
 }
 
 template <int S>
-hipError_t launch_sep_mb(const SepPlan& pl, const bf16_t* x, const bf16_t* wdw, const float* bdw,
-                         const bf16_t* wpw, const float* bpw, bf16_t* y, hipStream_t st) {
-    if (pl.mb == 1) return launch_sep<S, 1>(pl, x, wdw, bdw, wpw, bpw, y, st);
-    if (pl.mb == 2) return launch_sep<S, 2>(pl, x, wdw, bdw, wpw, bpw, y, st);
-    return launch_sep<S, 4>(pl, x, wdw, bdw, wpw, bpw, y, st);
+hipError_t launch_sep_relu(const SepShape& s, const SepPlan& pl, const bf16_t* x, const bf16_t* wdw,
+                           const float* bdw, const bf16_t* wpw, const float* bpw, bf16_t* y, hipStream_t st) {
+    if (s.dw_epilogue & CONV2D_EPI_RELU) return launch_sep<S, true>(pl, x, wdw, bdw, wpw, bpw, y, st);
+    return launch_sep<S, false>(pl, x, wdw, bdw, wpw, bpw, y, st);
 }
 
 }  // namespace
@@ -361,8 +377,8 @@ hipError_t launch_separable(const SepShape& s, const void* x, const void* w_dw, 
     const bf16_t* wd = static_cast<const bf16_t*>(w_dw);
     const bf16_t* wq = static_cast<const bf16_t*>(w_pw);
     bf16_t* yt = static_cast<bf16_t*>(y);
-    if (s.stride == 1) return launch_sep_mb<1>(pl, xt, wd, b_dw, wq, b_pw, yt, st);
-    return launch_sep_mb<2>(pl, xt, wd, b_dw, wq, b_pw, yt, st);
+    if (s.stride == 1) return launch_sep_relu<1>(s, pl, xt, wd, b_dw, wq, b_pw, yt, st);
+    return launch_sep_relu<2>(s, pl, xt, wd, b_dw, wq, b_pw, yt, st);
 }
 
 }  // namespace conv2d
