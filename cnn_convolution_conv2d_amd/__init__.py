@@ -29,7 +29,8 @@ ERR_ARG, ERR_GROUPS, ERR_EMPTY_OUTPUT, ERR_UNSUPPORTED, ERR_HIP = -1, -2, -3, -4
 ERR_NULL, ERR_DTYPE, ERR_EPILOGUE, ERR_ALIGN = -6, -7, -8, -9
 
 # Every symbol include/conv2d.h declares.
-EXPORTS = ("conv2d_fwd", "conv2d_fwd_nhwc_packed", "conv2d_fwd_separable_nhwc",
+EXPORTS = ("conv2d_fwd", "conv2d_fwd_nhwc_packed", "conv2d_fwd_bn", "conv2d_fwd_nhwc_packed_bn",
+           "conv2d_fwd_separable_nhwc",
            "conv2d_packed_weight_bytes",
            "conv2d_pack_weights", "conv2d_nchw_to_nhwc", "conv2d_nhwc_to_nchw",
            "conv2d_out_dim", "conv2d_check_args", "conv2d_select_path",
@@ -56,6 +57,9 @@ def _load() -> ctypes.CDLL:
     for name in ("conv2d_fwd", "conv2d_fwd_nhwc_packed"):
         f = getattr(lib, name)
         f.argtypes, f.restype = conv_args, I
+    for name in ("conv2d_fwd_bn", "conv2d_fwd_nhwc_packed_bn"):
+        f = getattr(lib, name)
+        f.argtypes, f.restype = [P] * 6 + [I] * 13 + [P], I
     lib.conv2d_fwd_separable_nhwc.argtypes = [P] * 6 + [I] * 10 + [P]
     lib.conv2d_fwd_separable_nhwc.restype = I
     lib.conv2d_packed_weight_bytes.argtypes = [I] * 6
@@ -124,6 +128,23 @@ def conv2d_fwd_nhwc_packed(x, w_packed, bias, y, N, Cin, H, W, Cout, Kh, Kw, str
                                       Cout, Kh, Kw, stride, pad, dilation, groups, dtype, epilogue,
                                       _stream(stream)),
            "conv2d_fwd_nhwc_packed")
+
+
+def conv2d_fwd_bn(x, w, bias, scale, shift, y, N, Cin, H, W, Cout, Kh, Kw, stride, pad, dilation, groups,
+                  dtype, epilogue, stream=None) -> None:
+    """conv2d_fwd with the folded batch normalisation (fp32 scale, shift [Cout])."""
+    _check(lib.conv2d_fwd_bn(_ptr(x), _ptr(w), _ptr(bias), _ptr(scale), _ptr(shift), _ptr(y), N, Cin, H, W,
+                             Cout, Kh, Kw, stride, pad, dilation, groups, dtype, epilogue, _stream(stream)),
+           "conv2d_fwd_bn")
+
+
+def conv2d_fwd_nhwc_packed_bn(x, w_packed, bias, scale, shift, y, N, Cin, H, W, Cout, Kh, Kw, stride, pad,
+                              dilation, groups, dtype, epilogue, stream=None) -> None:
+    """conv2d_fwd_nhwc_packed with the folded batch normalisation."""
+    _check(lib.conv2d_fwd_nhwc_packed_bn(_ptr(x), _ptr(w_packed), _ptr(bias), _ptr(scale), _ptr(shift),
+                                         _ptr(y), N, Cin, H, W, Cout, Kh, Kw, stride, pad, dilation, groups,
+                                         dtype, epilogue, _stream(stream)),
+           "conv2d_fwd_nhwc_packed_bn")
 
 
 def conv2d_fwd_separable_nhwc(x, w_dw, bias_dw, w_pw, bias_pw, y, N, C, H, W, Cout, stride, pad,

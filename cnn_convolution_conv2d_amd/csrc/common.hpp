@@ -15,6 +15,10 @@ struct Shape {
     int cin_g, cout_g;   // channels per group
     int dtype;           // CONV2D_F32 / CONV2D_BF16
     int epilogue;        // CONV2D_EPI_* bits
+    // Folded batch normalisation of the epilogue (both null: none):
+    // v = (sum [+ bias]) * scale[co] + shift[co], then the ReLU.
+    const float* scale;
+    const float* shift;
 };
 
 // One fused depthwise-separable call (3x3 depthwise, then 1x1), validated on
@@ -56,12 +60,16 @@ template <typename T> __device__ __forceinline__ void store_f32(T* p, int i, flo
 template <> __device__ __forceinline__ void store_f32<float>(float* p, int i, float v) { p[i] = v; }
 template <> __device__ __forceinline__ void store_f32<bf16_t>(bf16_t* p, int i, float v) { p[i] = f32_to_bf16(v); }
 
-// Epilogue of every kernel: bias after the full sum, then ReLU (the fused
-// bias -> activation -> single store of the "Epilogue Fusion" passage).
+// Epilogue of every kernel: bias after the full sum, then the folded batch
+// normalisation scale and shift when given, then ReLU (the fused bias ->
+// scale/shift -> activation -> single store of the "Epilogue Fusion"
+// passage).
 template <bool BIAS, bool RELU>
-__device__ __forceinline__ float epilogue(float acc, const float* bias, int co) {
+__device__ __forceinline__ float epilogue(float acc, const float* bias, const float* scale, const float* shift,
+                                          int co) {
     float v = acc;
     if (BIAS) v += bias[co];
+    if (scale) v = fmaf(v, scale[co], shift[co]);
     if (RELU) v = fmaxf(v, 0.0f);
     return v;
 }

@@ -75,6 +75,7 @@ int validate(const void* x, const void* w, const float* bias, const void* y,
         s.Ho = (int)Ho; s.Wo = (int)Wo;
         s.cin_g = Cin / groups; s.cout_g = Cout / groups;
         s.dtype = dtype; s.epilogue = epilogue;
+        s.scale = nullptr; s.shift = nullptr;
         *out = s;
     }
     return CONV2D_OK;
@@ -181,6 +182,67 @@ int get_scratch(size_t bytes, void** out) {
     return CONV2D_OK;
 }
 
+// Validation shared by the forward entries; with_bn: the folded batch
+// normalisation tables are required (non-NULL) and stored in the shape.
+int validate_fwd(const void* x, const void* w, const float* bias, const float* scale, const float* shift,
+                 const void* y, int N, int Cin, int H, int W, int Cout, int Kh, int Kw, int stride, int pad,
+                 int dilation, int groups, int dtype, int epilogue, bool with_bn, Shape* s) {
+    int rc = validate(x, w, bias, y, N, Cin, H, W, Cout, Kh, Kw, stride, pad, dilation, groups, dtype, epilogue, s);
+    if (rc) return rc;
+    if (with_bn) {
+        if (!scale || !shift) return set_error(CONV2D_ERR_NULL, "scale and shift must be non-NULL");
+        s->scale = scale;
+        s->shift = shift;
+    }
+    return CONV2D_OK;
+}
+
+int fwd_nhwc_packed(const void* x, const void* w_packed, const float* bias, const float* scale, const float* shift,
+                    void* y, int N, int Cin, int H, int W, int Cout, int Kh, int Kw, int stride, int pad,
+                    int dilation, int groups, int dtype, int epilogue, hipStream_t stream, bool with_bn) {
+    Shape s;
+    int rc = validate_fwd(x, w_packed, bias, scale, shift, y, N, Cin, H, W, Cout, Kh, Kw, stride, pad, dilation,
+                          groups, dtype, epilogue, with_bn, &s);
+    if (rc) return rc;
+    int path = choose_path(s);
+    if (path < 0) return path;
+    return run_nhwc(path, s, x, w_packed, bias, y, stream);
+}
+
+int fwd_nchw(const void* x, const void* w, const float* bias, const float* scale, const float* shift, void* y,
+             int N, int Cin, int H, int W, int Cout, int Kh, int Kw, int stride, int pad, int dilation, int groups,
+             int dtype, int epilogue, hipStream_t stream, bool with_bn) {
+    Shape s;
+    int rc = validate_fwd(x, w, bias, scale, shift, y, N, Cin, H, W, Cout, Kh, Kw, stride, pad, dilation, groups,
+                          dtype, epilogue, with_bn, &s);
+    if (rc) return rc;
+    int path = choose_path(s);
+    if (path < 0) return path;
+    if (path == CONV2D_PATH_DIRECT) {
+        // The direct loop reads the pages' layouts as they are: no repack.
+        hipError_t e = launch_direct(s, x, NCHW, w, W_OIHW, bias, y, NCHW, stream);
+        return e == hipSuccess ? CONV2D_OK : hip_fail(e, "direct launch");
+    }
+    const size_t eb = elem_bytes(dtype);
+    const size_t wb = round_up(conv2d_packed_weight_bytes(Cout, Cin, Kh, Kw, groups, dtype), 256);
+    const size_t xb = round_up((size_t)N * Cin * H * W * eb, 256);
+    const size_t yb = round_up((size_t)N * Cout * s.Ho * s.Wo * eb, 256);
+    void* scratch = nullptr;
+    rc = get_scratch(wb + xb + yb, &scratch);
+    if (rc) return rc;
+    char* base = static_cast<char*>(scratch);
+    void* wp = base;
+    void* xn = base + wb;
+    void* yn = base + wb + xb;
+    rc = conv2d_pack_weights(w, wp, Cout, Cin, Kh, Kw, groups, dtype, stream);
+    if (rc) return rc;
+    rc = conv2d_nchw_to_nhwc(x, xn, N, Cin, H, W, dtype, stream);
+    if (rc) return rc;
+    rc = run_nhwc(path, s, xn, wp, bias, yn, stream);
+    if (rc) return rc;
+    return conv2d_nhwc_to_nchw(yn, y, N, Cout, s.Ho, s.Wo, dtype, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -264,48 +326,31 @@ int conv2d_fwd_nhwc_packed(const void* x, const void* w_packed, const float* bia
                            int N, int Cin, int H, int W, int Cout, int Kh, int Kw,
                            int stride, int pad, int dilation, int groups,
                            int dtype, int epilogue, hipStream_t stream) {
-    Shape s;
-    int rc = validate(x, w_packed, bias, y, N, Cin, H, W, Cout, Kh, Kw, stride, pad, dilation,
-                      groups, dtype, epilogue, &s);
-    if (rc) return rc;
-    int path = choose_path(s);
-    if (path < 0) return path;
-    return run_nhwc(path, s, x, w_packed, bias, y, stream);
+    return fwd_nhwc_packed(x, w_packed, bias, nullptr, nullptr, y, N, Cin, H, W, Cout, Kh, Kw, stride, pad,
+                           dilation, groups, dtype, epilogue, stream, false);
+}
+
+int conv2d_fwd_nhwc_packed_bn(const void* x, const void* w_packed, const float* bias, const float* scale,
+                              const float* shift, void* y, int N, int Cin, int H, int W, int Cout, int Kh,
+                              int Kw, int stride, int pad, int dilation, int groups, int dtype, int epilogue,
+                              hipStream_t stream) {
+    return fwd_nhwc_packed(x, w_packed, bias, scale, shift, y, N, Cin, H, W, Cout, Kh, Kw, stride, pad,
+                           dilation, groups, dtype, epilogue, stream, true);
 }
 
 int conv2d_fwd(const void* x, const void* w, const float* bias, void* y,
                int N, int Cin, int H, int W, int Cout, int Kh, int Kw,
                int stride, int pad, int dilation, int groups,
                int dtype, int epilogue, hipStream_t stream) {
-    Shape s;
-    int rc = validate(x, w, bias, y, N, Cin, H, W, Cout, Kh, Kw, stride, pad, dilation, groups,
-                      dtype, epilogue, &s);
-    if (rc) return rc;
-    int path = choose_path(s);
-    if (path < 0) return path;
-    if (path == CONV2D_PATH_DIRECT) {
-        // The direct loop reads the pages' layouts as they are: no repack.
-        hipError_t e = launch_direct(s, x, NCHW, w, W_OIHW, bias, y, NCHW, stream);
-        return e == hipSuccess ? CONV2D_OK : hip_fail(e, "direct launch");
-    }
-    const size_t eb = elem_bytes(dtype);
-    const size_t wb = round_up(conv2d_packed_weight_bytes(Cout, Cin, Kh, Kw, groups, dtype), 256);
-    const size_t xb = round_up((size_t)N * Cin * H * W * eb, 256);
-    const size_t yb = round_up((size_t)N * Cout * s.Ho * s.Wo * eb, 256);
-    void* scratch = nullptr;
-    rc = get_scratch(wb + xb + yb, &scratch);
-    if (rc) return rc;
-    char* base = static_cast<char*>(scratch);
-    void* wp = base;
-    void* xn = base + wb;
-    void* yn = base + wb + xb;
-    rc = conv2d_pack_weights(w, wp, Cout, Cin, Kh, Kw, groups, dtype, stream);
-    if (rc) return rc;
-    rc = conv2d_nchw_to_nhwc(x, xn, N, Cin, H, W, dtype, stream);
-    if (rc) return rc;
-    rc = run_nhwc(path, s, xn, wp, bias, yn, stream);
-    if (rc) return rc;
-    return conv2d_nhwc_to_nchw(yn, y, N, Cout, s.Ho, s.Wo, dtype, stream);
+    return fwd_nchw(x, w, bias, nullptr, nullptr, y, N, Cin, H, W, Cout, Kh, Kw, stride, pad, dilation, groups,
+                    dtype, epilogue, stream, false);
+}
+
+int conv2d_fwd_bn(const void* x, const void* w, const float* bias, const float* scale, const float* shift,
+                  void* y, int N, int Cin, int H, int W, int Cout, int Kh, int Kw, int stride, int pad,
+                  int dilation, int groups, int dtype, int epilogue, hipStream_t stream) {
+    return fwd_nchw(x, w, bias, scale, shift, y, N, Cin, H, W, Cout, Kh, Kw, stride, pad, dilation, groups,
+                    dtype, epilogue, stream, true);
 }
 
 int conv2d_fwd_separable_nhwc(const void* x, const void* w_dw, const float* bias_dw, const void* w_pw,

@@ -43,12 +43,17 @@ __device__ __forceinline__ void fma_v8(float acc[8], const V8& x, const float w[
 }
 
 template <bool BIAS, bool RELU>
-__device__ __forceinline__ V8 finish(const float acc[8], const float b[8]) {
+__device__ __forceinline__ V8 finish(const float acc[8], const float b[8], const float* scale, const float* shift,
+                                     int c0) {
     V8 o;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         float a0 = acc[2 * i], a1 = acc[2 * i + 1];
         if (BIAS) { a0 += b[2 * i]; a1 += b[2 * i + 1]; }
+        if (scale) {  // folded batch normalisation
+            a0 = fmaf(a0, scale[c0 + 2 * i], shift[c0 + 2 * i]);
+            a1 = fmaf(a1, scale[c0 + 2 * i + 1], shift[c0 + 2 * i + 1]);
+        }
         if (RELU) { a0 = fmaxf(a0, 0.0f); a1 = fmaxf(a1, 0.0f); }
         o.u[i] = pack_bf16x2(a0, a1);
     }
@@ -107,6 +112,10 @@ __global__ __launch_bounds__(kThreads) void dw3x3s1_kernel(const bf16_t* __restr
         row_fma(acc, r0, wp[0], w2[0]);
         row_fma(acc, r1, wp[1], w2[1]);
         row_fma(acc, r2, wp[2], w2[2]);
+        if (s.scale) {  // folded batch normalisation
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] = fmaf(acc[i], s.scale[c0 + i], s.shift[c0 + i]);
+        }
         V8 o;
 #pragma unroll
         for (int i = 0; i < 4; ++i) o.u[i] = pack_relu<RELU>(acc[2 * i], acc[2 * i + 1]);
@@ -174,7 +183,7 @@ __global__ __launch_bounds__(kThreads) void dw_generic_kernel(const bf16_t* __re
             }
         }
         *reinterpret_cast<V8*>(y + (((size_t)n * s.Ho + ho) * s.Wo + wo) * s.Cout + c0) =
-            finish<BIAS, RELU>(acc, br);
+            finish<BIAS, RELU>(acc, br, s.scale, s.shift, c0);
     }
 }
 

@@ -71,7 +71,7 @@ __global__ __launch_bounds__(kThreads) void direct_kernel(const T* __restrict__ 
     for (int j = 0; j < COB; ++j) {
         if (j < nco) {
             const int co = co_base + j;
-            const float v = epilogue<BIAS, RELU>(acc[j], bias, co);
+            const float v = epilogue<BIAS, RELU>(acc[j], bias, s.scale, s.shift, co);
             const int yi = (YL == NCHW) ? ((n * s.Cout + co) * s.Ho + ho) * s.Wo + wo
                                         : ((n * s.Ho + ho) * s.Wo + wo) * s.Cout + co;
             store_f32<T>(y, yi, v);

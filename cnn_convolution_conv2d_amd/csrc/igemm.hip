@@ -250,6 +250,7 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(const bf16_t* __restric
     // in acc[16*0 + 4*q + r] for q, r = 0..3, i.e. four runs of four
     // consecutive output channels of one pixel.
     char* ep = reinterpret_cast<char*>(lds_raw);
+    const Affine4 aff(s.scale, s.shift, s.Cout);
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -258,16 +259,16 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(const bf16_t* __restric
             const int co = co_tile + col;
             float4 b4 = make_float4(0.f, 0.f, 0.f, 0.f);
             if (BIAS) b4 = *reinterpret_cast<const float4*>(&sbias[col]);
-            (void)co;
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
                 const int row = wn * WTN + j * 32 + (lane & 31);      // pixel within the tile
                 float v[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    v[r] = acc[i][j][4 * q + r] + (&b4.x)[r];
+                for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * q + r] + (&b4.x)[r];
+                if (s.scale) aff.apply(v, g * s.cout_g + co);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
                     if (RELU) v[r] = fmaxf(v[r], 0.0f);
-                }
                 *reinterpret_cast<uint2*>(ep + row * ERS + col * 2) =
                     make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
             }

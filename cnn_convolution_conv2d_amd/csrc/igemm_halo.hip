@@ -333,6 +333,7 @@ __global__ __launch_bounds__(NT, waves_per_simd(NT, MINB, halo_lds_bytes(BM, TH,
             pix_[j] = (ho_ < s.Ho && wo_ < s.Wo) ? ((tc.n * s.Ho + ho_) * s.Wo + wo_) * s.Cout : -1; \
         }                                                                                    \
         const int cw_ = tc.ct * BM + wm * WTM;  /* first channel (within the group) of the wave */ \
+        const Affine4 aff_(s.scale, s.shift, s.Cout);                                        \
         _Pragma("unroll") for (int i = 0; i < TM; ++i) {                                     \
             float4 b4_[4];                                                                   \
             _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                  \
@@ -345,10 +346,11 @@ __global__ __launch_bounds__(NT, waves_per_simd(NT, MINB, halo_lds_bytes(BM, TH,
                 uint32_t pk_[4][2];                                                          \
                 _Pragma("unroll") for (int q = 0; q < 4; ++q) {                              \
                     float v_[4];                                                             \
-                    _Pragma("unroll") for (int r = 0; r < 4; ++r) {                          \
+                    _Pragma("unroll") for (int r = 0; r < 4; ++r)                            \
                         v_[r] = acc[i][j][4 * q + r] + (&b4_[q].x)[r];                       \
+                    if (s.scale) aff_.apply(v_, tc.g * s.cout_g + cw_ + i * 32 + 8 * q + 4 * half); \
+                    _Pragma("unroll") for (int r = 0; r < 4; ++r)                            \
                         if (RELU) v_[r] = fmaxf(v_[r], 0.0f);                                \
-                    }                                                                        \
                     pk_[q][0] = pack_bf16x2(v_[0], v_[1]);                                   \
                     pk_[q][1] = pack_bf16x2(v_[2], v_[3]);                                   \
                 }                                                                            \
@@ -493,6 +495,8 @@ __device__ __forceinline__ void tile_epilogue(f32x16 (&acc)[TM][TN], const char*
     // channel of this lane's 16-byte piece within a 32-channel block
     const int cl = ((lane >> 4) & 1) * 16 + half * 8;
     const int cw = co0 + wm * WTM;  // first channel (within the group) of the wave's rows
+    const Affine4 aff(s.scale, s.shift, s.Cout);
+    const int cga = tc.g * s.cout_g + cw;  // absolute channel of cw
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
         float4 b4[4];
@@ -509,10 +513,11 @@ __device__ __forceinline__ void tile_epilogue(f32x16 (&acc)[TM][TN], const char*
             for (int q = 0; q < 4; ++q) {
                 float v[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    v[r] = acc[i][j][4 * q + r] + (&b4[q].x)[r];
+                for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * q + r] + (&b4[q].x)[r];
+                if (s.scale) aff.apply(v, cga + i * 32 + 8 * q + 4 * half);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
                     if (RELU) v[r] = fmaxf(v[r], 0.0f);
-                }
                 pk[q][0] = pack_bf16x2(v[0], v[1]);
                 pk[q][1] = pack_bf16x2(v[2], v[3]);
             }

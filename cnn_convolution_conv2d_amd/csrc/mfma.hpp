@@ -42,6 +42,24 @@ __device__ __forceinline__ void store8(__amdgpu_buffer_rsrc_t r, int byte_off, u
     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, byte_off, 0, 0);
 }
 
+// The folded batch-normalisation step of an epilogue: v = v * scale[c] +
+// shift[c] for four consecutive output channels c .. c+3 (c a multiple of 4).
+// Both tables are read through descriptors sized to Cout, so the channels of
+// a tile's padding rows past Cout read zero (they are never stored).
+struct Affine4 {
+    __amdgpu_buffer_rsrc_t sc, sh;
+    __device__ __forceinline__ Affine4(const float* scale, const float* shift, int cout)
+        : sc(make_rsrc(scale, (uint32_t)cout * 4u)), sh(make_rsrc(shift, (uint32_t)cout * 4u)) {}
+    __device__ __forceinline__ void apply(float v[4], int c) const {
+        const float4 a = __builtin_bit_cast(float4, load16(sc, c * 4));
+        const float4 b = __builtin_bit_cast(float4, load16(sh, c * 4));
+        v[0] = fmaf(v[0], a.x, b.x);
+        v[1] = fmaf(v[1], a.y, b.y);
+        v[2] = fmaf(v[2], a.z, b.z);
+        v[3] = fmaf(v[3], a.w, b.w);
+    }
+};
+
 // An LDS row holds the BK channels of one K-step for one output channel (A)
 // or one pixel (B): BK*2 bytes = BK/8 16-byte chunks.  The chunk index is
 // XOR-swizzled with the row so that any 16 consecutive rows read at the same

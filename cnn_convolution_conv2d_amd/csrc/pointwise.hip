@@ -46,7 +46,8 @@ __global__ __launch_bounds__(kPwThreads, 2) void pw_kernel(const bf16_t* __restr
                                                        const float* __restrict__ bias,
                                                        bf16_t* __restrict__ y, int npix, int cin,
                                                        int cout, int ntiles, int nmh, int has_bias,
-                                                       int relu, int cin8_magic) {
+                                                       int relu, int cin8_magic, const float* scale,
+                                                       const float* shift) {
     // dynamic LDS: weights [rows][P units], then one activation tile
     // [32 pixels][P units] per wave
     extern __shared__ uint4 pw_lds[];
@@ -97,6 +98,7 @@ __global__ __launch_bounds__(kPwThreads, 2) void pw_kernel(const bf16_t* __restr
     // 32-channel block, of pixel 16*e + lane % 16 (e = 0, 1) of the tile
     const int cl = ((lane >> 4) & 1) * 16 + h * 8;
     const bool vec16 = cout % 8 == 0;
+    const Affine4 aff(scale, shift, cout);  // folded batch normalisation, when scale is given
 
     const int nw = gridDim.x * (kPwThreads / 64);
     const int w0 = blockIdx.x * (kPwThreads / 64) + wave;
@@ -172,10 +174,10 @@ __global__ __launch_bounds__(kPwThreads, 2) void pw_kernel(const bf16_t* __restr
             uint32_t pk_[4][2];                                                              \
             _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                  \
                 float v_[4];                                                                 \
-                _Pragma("unroll") for (int r = 0; r < 4; ++r) {                              \
-                    v_[r] = acc[mb][4 * q + r];                                              \
+                _Pragma("unroll") for (int r = 0; r < 4; ++r) v_[r] = acc[mb][4 * q + r];   \
+                if (scale) aff.apply(v_, c0_ + mb * 32 + 8 * q + 4 * h);                     \
+                _Pragma("unroll") for (int r = 0; r < 4; ++r)                                \
                     if (relu) v_[r] = fmaxf(v_[r], 0.0f);                                    \
-                }                                                                            \
                 pk_[q][0] = pack_bf16x2(v_[0], v_[1]);                                       \
                 pk_[q][1] = pack_bf16x2(v_[2], v_[3]);                                       \
             }                                                                                \
@@ -258,7 +260,7 @@ hipError_t launch_pw(const Shape& s, const bf16_t* x, const bf16_t* w, const flo
     const int grid = (int)(want < resident ? want : resident);
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kPwThreads), (unsigned)lds, st, x, w, b, y, npix, s.Cin, s.Cout,
                        ntiles, nmh, (s.epilogue & CONV2D_EPI_BIAS) ? 1 : 0, (s.epilogue & CONV2D_EPI_RELU) ? 1 : 0,
-                       magic);
+                       magic, s.scale, s.shift);
     return hipGetLastError();
 }
 

@@ -117,6 +117,29 @@ int conv2d_fwd_nhwc_packed(const void* x, const void* w_packed, const float* bia
                            int dtype, int epilogue, hipStream_t stream);
 
 /*
+ * conv2d_fwd_bn, conv2d_fwd_nhwc_packed_bn -- the same two forward entries
+ * with batch normalisation (inference form) folded into the epilogue
+ * (lincklin.cn lesson 9, section 31: bias, then the normalisation's
+ * per-channel scale and shift, then the activation, in registers before the
+ * single store):
+ *   Y[n,co,ho,wo] = [max]( (sum [+ bias[co]]) * scale[co] + shift[co] )
+ * For a normalisation with mean mu, variance var, gain gamma, offset beta and
+ * epsilon eps: scale = gamma / sqrt(var + eps), shift = beta - mu * scale.
+ *   scale, shift  fp32 [Cout] device memory, both required (non-NULL)
+ * Every other argument, layout, path and error as for conv2d_fwd /
+ * conv2d_fwd_nhwc_packed (epilogue: CONV2D_EPI_BIAS and CONV2D_EPI_RELU as
+ * there).  Every kernel path supports it.
+ */
+int conv2d_fwd_bn(const void* x, const void* w, const float* bias, const float* scale, const float* shift,
+                  void* y, int N, int Cin, int H, int W, int Cout, int Kh, int Kw,
+                  int stride, int pad, int dilation, int groups,
+                  int dtype, int epilogue, hipStream_t stream);
+int conv2d_fwd_nhwc_packed_bn(const void* x, const void* w_packed, const float* bias, const float* scale,
+                              const float* shift, void* y, int N, int Cin, int H, int W, int Cout,
+                              int Kh, int Kw, int stride, int pad, int dilation, int groups,
+                              int dtype, int epilogue, hipStream_t stream);
+
+/*
  * conv2d_fwd_separable_nhwc -- the depthwise-separable block as one fused
  * pass (lincklin.cn lesson 9, section 25; lpnh.cn section 4.1; lnrq.cn
  * section 3.1): a 3x3 depthwise convolution (groups == C, stride S, padding

@@ -214,3 +214,19 @@ def separable(x, w_dw, w_pw, bias_dw=None, bias_pw=None, stride=1, pad=1, dw_rel
     C = np.asarray(x).shape[1]
     t, _ = conv2d(x, w_dw, bias_dw, stride, pad, 1, C, relu=dw_relu, with_scale=False, lib=lib)
     return conv2d(bf16_round(t), w_pw, bias_pw, 1, 0, 1, 1, relu=pw_relu, lib=lib)
+
+
+def conv2d_bn(x, w, scale, shift, bias=None, stride=1, pad=0, dilation=1, groups=1, relu=False, lib=None):
+    """Convolution with batch normalisation (inference form) folded into the
+    epilogue (page "How a GPU executes NN convolution", lincklin.cn, section
+    31): the sum, plus the bias, times scale[co] plus shift[co], then ReLU.
+    Returns (y, S) with S = |scale| * (sum|x*w| + |bias|) + |shift|, the
+    magnitude the result is rounded against."""
+    y, s = conv2d(x, w, bias, stride, pad, dilation, groups, relu=False, lib=lib)
+    sc = _f64(scale)[None, :, None, None]
+    sh = _f64(shift)[None, :, None, None]
+    y = y * sc + sh
+    if relu:
+        y = np.maximum(y, 0.0)
+    b = 0.0 if bias is None else np.abs(_f64(bias))[None, :, None, None]
+    return y, np.abs(sc) * (s + b) + np.abs(sh)

@@ -93,8 +93,10 @@ def pack_weights(w_dev, Cout, Cin, Kh, Kw, groups, dtype):
     return wp
 
 
-def run_nhwc(x_nchw, w, bias, stride, pad, dil, groups, dtype, epilogue, return_dev=False):
-    """x (NCHW float32 values), w (OIHW), bias -> NHWC entry -> NCHW float64 result."""
+def run_nhwc(x_nchw, w, bias, stride, pad, dil, groups, dtype, epilogue, return_dev=False, scale=None,
+             shift=None):
+    """x (NCHW float32 values), w (OIHW), bias -> NHWC entry -> NCHW float64 result
+    (with scale and shift: the entry with the folded batch normalisation)."""
     import torch
     import cnn_convolution_conv2d_amd as c2
     N, Cin, H, W = x_nchw.shape
@@ -106,16 +108,22 @@ def run_nhwc(x_nchw, w, bias, stride, pad, dil, groups, dtype, epilogue, return_
     wp = pack_weights(wd, Cout, Cin, Kh, Kw, groups, dtype)
     bd = None if bias is None else torch.from_numpy(np.asarray(bias, np.float32)).cuda()
     yd = torch.full((N, Ho, Wo, Cout), float("nan"), dtype=torch_dtype(dtype), device="cuda")
-    c2.conv2d_fwd_nhwc_packed(xd, wp, bd, yd, N, Cin, H, W, Cout, Kh, Kw, stride, pad, dil, groups,
-                              lib_dtype(dtype), epilogue)
+    if scale is None:
+        c2.conv2d_fwd_nhwc_packed(xd, wp, bd, yd, N, Cin, H, W, Cout, Kh, Kw, stride, pad, dil, groups,
+                                  lib_dtype(dtype), epilogue)
+    else:
+        sd, hd = (torch.from_numpy(np.asarray(a, np.float32)).cuda() for a in (scale, shift))
+        c2.conv2d_fwd_nhwc_packed_bn(xd, wp, bd, sd, hd, yd, N, Cin, H, W, Cout, Kh, Kw, stride, pad, dil,
+                                     groups, lib_dtype(dtype), epilogue)
     torch.cuda.synchronize()
     if return_dev:
         return yd
     return ci.nhwc_to_nchw(yd.float().cpu().numpy()).astype(np.float64)
 
 
-def run_nchw(x_nchw, w, bias, stride, pad, dil, groups, dtype, epilogue):
-    """The NCHW entry (conv2d_fwd) on the pages' own layouts."""
+def run_nchw(x_nchw, w, bias, stride, pad, dil, groups, dtype, epilogue, scale=None, shift=None):
+    """The NCHW entry (conv2d_fwd, or conv2d_fwd_bn with scale and shift) on
+    the pages' own layouts."""
     import torch
     import cnn_convolution_conv2d_amd as c2
     N, Cin, H, W = x_nchw.shape
@@ -126,8 +134,13 @@ def run_nchw(x_nchw, w, bias, stride, pad, dil, groups, dtype, epilogue):
     wd = to_dev(w, dtype)
     bd = None if bias is None else torch.from_numpy(np.asarray(bias, np.float32)).cuda()
     yd = torch.full((N, Cout, Ho, Wo), float("nan"), dtype=torch_dtype(dtype), device="cuda")
-    c2.conv2d_fwd(xd, wd, bd, yd, N, Cin, H, W, Cout, Kh, Kw, stride, pad, dil, groups,
-                  lib_dtype(dtype), epilogue)
+    if scale is None:
+        c2.conv2d_fwd(xd, wd, bd, yd, N, Cin, H, W, Cout, Kh, Kw, stride, pad, dil, groups,
+                      lib_dtype(dtype), epilogue)
+    else:
+        sd, hd = (torch.from_numpy(np.asarray(a, np.float32)).cuda() for a in (scale, shift))
+        c2.conv2d_fwd_bn(xd, wd, bd, sd, hd, yd, N, Cin, H, W, Cout, Kh, Kw, stride, pad, dil, groups,
+                         lib_dtype(dtype), epilogue)
     torch.cuda.synchronize()
     return yd.float().cpu().numpy().astype(np.float64)
 

@@ -85,6 +85,14 @@ def test_forward_entries_reject_bad_args_before_any_gpu_work():
         rc = fn(P, P, None, P, 1, 8, 9, 9, 16, 3, 3, 1, 1, 1, 1, c2.BF16, c2.EPI_BIAS, None)
         assert rc == c2.ERR_NULL
         assert "bias" in c2.last_error()
+    for fn in (c2.lib.conv2d_fwd_bn, c2.lib.conv2d_fwd_nhwc_packed_bn):
+        # scale and shift are required; other checks as for the plain entries
+        rc = fn(P, P, P, None, P, P, 1, 8, 9, 9, 16, 3, 3, 1, 1, 1, 1, c2.BF16, 0, None)
+        assert rc == c2.ERR_NULL and "scale" in c2.last_error()
+        rc = fn(P, P, P, P, None, P, 1, 8, 9, 9, 16, 3, 3, 1, 1, 1, 1, c2.BF16, 0, None)
+        assert rc == c2.ERR_NULL
+        assert fn(P, P, P, P, P, P, 0, 8, 9, 9, 16, 3, 3, 1, 1, 1, 1, c2.BF16, 0, None) == c2.ERR_ARG
+        assert fn(P, P, P, P, P, P, 1, 8, 9, 9, 16, 3, 3, 1, 1, 1, 3, c2.BF16, 0, None) == c2.ERR_GROUPS
     assert c2.lib.conv2d_pack_weights(P, P, 16, 8, 3, 3, 3, c2.BF16, None) == c2.ERR_GROUPS
     assert c2.lib.conv2d_nchw_to_nhwc(P, None, 1, 8, 9, 9, c2.BF16, None) == c2.ERR_NULL
     assert c2.lib.conv2d_nhwc_to_nchw(P, P, 1, 8, 9, 9, 5, None) == c2.ERR_DTYPE

@@ -307,6 +307,37 @@ def test_p8_separable_block_without_relu_is_a_factorised_conv():
         np.testing.assert_array_equal(y, yb)
 
 
+# ------------------------------------------------------------- folded batch normalisation
+
+@pytest.mark.parametrize("relu,with_bias,groups", [(True, True, 1), (False, True, 2), (True, False, 1)])
+def test_bn_epilogue_matches_torch_batch_norm(relu, with_bias, groups):
+    """conv (+ bias), then torch's own batch normalisation in inference mode,
+    then ReLU, against the oracle given the folded per-channel scale and
+    shift: scale = gamma / sqrt(var + eps), shift = beta - mean * scale."""
+    rng = np.random.default_rng(31 + groups + 2 * relu)
+    N, Cin, H, W, Cout = 2, 8, 9, 7, 6
+    x = rng.standard_normal((N, Cin, H, W))
+    w = rng.standard_normal((Cout, Cin // groups, 3, 3)) * 0.3
+    b = rng.standard_normal(Cout) * 0.1 if with_bias else None
+    mean, var = rng.standard_normal(Cout), rng.uniform(0.2, 2.0, Cout)
+    gamma, beta, eps = rng.standard_normal(Cout), rng.standard_normal(Cout), 1e-5
+    scale = gamma / np.sqrt(var + eps)
+    shift = beta - mean * scale
+    y, s = oracle.conv2d_bn(x, w, scale, shift, b, 1, 1, 1, groups, relu=relu)
+    t = F.conv2d(torch.from_numpy(x), torch.from_numpy(w), None if b is None else torch.from_numpy(b),
+                 padding=1, groups=groups)
+    t = F.batch_norm(t, torch.from_numpy(mean), torch.from_numpy(var), torch.from_numpy(gamma),
+                     torch.from_numpy(beta), training=False, eps=eps)
+    if relu:
+        t = torch.relu(t)
+    np.testing.assert_allclose(y, t.numpy(), rtol=0, atol=1e-12 * float(s.max()))
+    # the tolerance scale: |scale| (sum |x w| + |b|) + |shift|
+    s0 = _torch_conv(np.abs(x), np.abs(w), None, 1, 1, 1, groups)
+    bb = 0 if b is None else np.abs(b)[None, :, None, None]
+    np.testing.assert_allclose(s, np.abs(scale)[None, :, None, None] * (s0 + bb) + np.abs(shift)[None, :, None, None],
+                               rtol=1e-12)
+
+
 # ------------------------------------------------------------- p9: 1x1 = GEMM
 
 def test_p9_pointwise_is_gemm():
