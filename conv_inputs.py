@@ -11,7 +11,8 @@ fp32 (the single-point example of "lpnh.cn/news/2674933" section 2.1), a
 112x112x128 -> 256 3x3 layer (that page's section 3.2 GEMM example, batched),
 a MobileNetV2-style depthwise + pointwise pair ("lnrq.cn/news/4475" section
 3.1), a dilated and grouped layer (lpnh.cn sections 2.2, 4.2) and
-ResNet-50-bottleneck-shaped layers (lnrq.cn section 5.3).
+ResNet-50-bottleneck-shaped layers (lnrq.cn section 5.3); a sixth workload
+holds the transposed-convolution layers of a decoder's upsampling stage.
 
 Storage types: fp32 tensors are drawn in fp64 and rounded to the nearest fp32;
 bf16 tensors are drawn in fp64, rounded to fp32, then to bf16 with
@@ -58,10 +59,22 @@ class Layer:
     w_std: float | None = None      # None: Kaiming normal, sqrt(2 / fan_in)
     bias_std: float = 0.01
     chained_from: str | None = None  # name of the layer whose output is this layer's x
+    transposed: bool = False         # transposed convolution: w is [Cin][Cout/G][Kh][Kw]
+    out_pad: int = 0                 # extra output rows/columns of a transposed layer
 
     @property
     def fan_in(self) -> int:
+        if self.transposed:
+            # products each output receives when the kernel is a multiple of
+            # the stride: (Cin/G) * (Kh/S) * (Kw/S)
+            return max(1, (self.Cin // self.groups) * -(-self.Kh // self.stride) * -(-self.Kw // self.stride))
         return (self.Cin // self.groups) * self.Kh * self.Kw
+
+    @property
+    def w_shape(self) -> tuple:
+        if self.transposed:
+            return (self.Cin, self.Cout // self.groups, self.Kh, self.Kw)
+        return (self.Cout, self.Cin // self.groups, self.Kh, self.Kw)
 
     @property
     def weight_std(self) -> float:
@@ -111,6 +124,16 @@ WORKLOADS = {
               chained_from="L2_3x3_64_64"),
         Layer("L4_3x3s2_128_128", 64, 128, 56, 56, 128, 3, 3, stride=2, pad=1,
               epilogue=EPI_BIAS | EPI_RELU),
+    )),
+    # A decoder's 2x upsampling stage built from transposed convolutions
+    # (lpnh.cn sections 2.3 and 4.2: upsampling in generative networks, with
+    # the kernel a multiple of the stride): 4x4 stride 2 pad 1 (28 -> 56) and
+    # 2x2 stride 2 (56 -> 112).  Inputs are post-ReLU activations.
+    6: Workload(6, "decoder_upsampling_transposed_bf16_n32", (
+        Layer("up4x4s2_256_128", 32, 256, 28, 28, 128, 4, 4, stride=2, pad=1,
+              epilogue=EPI_BIAS | EPI_RELU, x_dist=("halfnormal", 1.0), transposed=True),
+        Layer("up2x2s2_128_64", 32, 128, 56, 56, 64, 2, 2, stride=2, pad=0,
+              epilogue=EPI_BIAS | EPI_RELU, x_dist=("halfnormal", 1.0), transposed=True),
     )),
 }
 
@@ -172,6 +195,8 @@ def _draw(rng: np.random.Generator, dist: tuple, shape) -> np.ndarray:
         return rng.standard_normal(size=shape) * scale
     if kind == "uniform":
         return rng.uniform(-scale, scale, size=shape)
+    if kind == "halfnormal":
+        return np.abs(rng.standard_normal(size=shape)) * scale
     raise ValueError(kind)
 
 
@@ -190,7 +215,7 @@ def layer_tensors(cid: int, layer_idx: int, *, N: int | None = None, H: int | No
     h = ly.H if H is None else H
     w_ = ly.W if W is None else W
     xs = (n, ly.Cin, h, w_)
-    ws = (ly.Cout, ly.Cin // ly.groups, ly.Kh, ly.Kw)
+    ws = ly.w_shape
     rx = np.random.default_rng(seed_of(cid, layer_idx, 1))
     rw = np.random.default_rng(seed_of(cid, layer_idx, 2))
     rb = np.random.default_rng(seed_of(cid, layer_idx, 3))

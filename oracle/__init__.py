@@ -58,6 +58,12 @@ def load_library(path: str | None = None):
     lib.oracle_conv2d_points_f64.argtypes = [P, P, P, ctypes.c_int, P, L, P, P] + [L] * 11
     lib.oracle_im2col_f64.restype = ctypes.c_int
     lib.oracle_im2col_f64.argtypes = [P, P] + [L] * 9
+    lib.oracle_transpose_out_dim.restype = L
+    lib.oracle_transpose_out_dim.argtypes = [L] * 6
+    lib.oracle_conv_transpose2d_f64.restype = ctypes.c_int
+    lib.oracle_conv_transpose2d_f64.argtypes = [P, P, P, ctypes.c_int, P, P] + [L] * 12
+    lib.oracle_conv_transpose2d_points_f64.restype = ctypes.c_int
+    lib.oracle_conv_transpose2d_points_f64.argtypes = [P, P, P, ctypes.c_int, P, L, P, P] + [L] * 12
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     _libs[key] = lib
@@ -230,3 +236,57 @@ def conv2d_bn(x, w, scale, shift, bias=None, stride=1, pad=0, dilation=1, groups
         y = np.maximum(y, 0.0)
     b = 0.0 if bias is None else np.abs(_f64(bias))[None, :, None, None]
     return y, np.abs(sc) * (s + b) + np.abs(sh)
+
+
+def transpose_out_dim(size: int, k: int, stride: int = 1, pad: int = 0, dilation: int = 1,
+                      out_pad: int = 0, lib=None) -> int:
+    """Output extent of the transposed convolution:
+    (size-1)*stride - 2*pad + dilation*(k-1) + out_pad + 1, with
+    0 <= out_pad < max(stride, dilation); -1 for arguments out of range."""
+    return int(_load(lib).oracle_transpose_out_dim(size, k, stride, pad, dilation, out_pad))
+
+
+def conv_transpose2d(x, w, bias=None, stride=1, pad=0, out_pad=0, dilation=1, groups=1, relu=False,
+                     lib=None):
+    """Transposed convolution ("lpnh.cn/news/2674933" sections 2.3, 4.2) in
+    fp64 by scattering W^T X: every input pixel times the whole filter, added
+    into the output window it spans.  x is NCHW, w is [Cin][Cout/G][Kh][Kw].
+    Returns (y, S), S = sum |x*w| of the products each output received."""
+    x, w = _f64(x), _f64(w)
+    N, Cin, H, W = x.shape
+    cin_w, cout_g, Kh, Kw = w.shape
+    if cin_w != Cin:
+        raise ValueError("weight's first dimension must be Cin")
+    Cout = cout_g * groups
+    b = None if bias is None else _f64(bias)
+    Ho = transpose_out_dim(H, Kh, stride, pad, dilation, out_pad, lib=lib)
+    Wo = transpose_out_dim(W, Kw, stride, pad, dilation, out_pad, lib=lib)
+    if Ho < 1 or Wo < 1:
+        raise ValueError("empty output")
+    y = np.empty((N, Cout, Ho, Wo), np.float64)
+    s = np.empty_like(y)
+    rc = _load(lib).oracle_conv_transpose2d_f64(_ptr(x), _ptr(w), _ptr(b), int(bool(relu)), _ptr(y), _ptr(s),
+                                             N, Cin, H, W, Cout, Kh, Kw, stride, pad, out_pad, dilation, groups)
+    if rc:
+        raise ValueError(f"oracle_conv_transpose2d_f64 rejected the shape (rc={rc})")
+    return y, s
+
+
+def conv_transpose2d_points(x, w, idx, bias=None, stride=1, pad=0, out_pad=0, dilation=1, groups=1,
+                            relu=False, lib=None):
+    """Selected outputs of the transposed convolution by flat NCHW index, each
+    gathered from the input pixels whose window covers it.  Returns
+    (y[idx], S[idx])."""
+    x, w = _f64(x), _f64(w)
+    N, Cin, H, W = x.shape
+    _, cout_g, Kh, Kw = w.shape
+    b = None if bias is None else _f64(bias)
+    idx = np.ascontiguousarray(idx, dtype=np.int64)
+    y = np.empty(idx.shape[0], np.float64)
+    s = np.empty_like(y)
+    rc = _load(lib).oracle_conv_transpose2d_points_f64(
+        _ptr(x), _ptr(w), _ptr(b), int(bool(relu)), _ptr(idx), idx.shape[0], _ptr(y), _ptr(s),
+        N, Cin, H, W, cout_g * groups, Kh, Kw, stride, pad, out_pad, dilation, groups)
+    if rc:
+        raise ValueError(f"oracle_conv_transpose2d_points_f64 rejected the call (rc={rc})")
+    return y, s

@@ -518,6 +518,150 @@ def test_generator_is_deterministic_and_bf16_exact():
     assert bias is not None and bias.dtype == np.float32
 
 
+# ------------------------------------------------------------- t: transposed convolution
+# "lpnh.cn/news/2674933" sections 2.3 and 4.2: a transposed convolution
+# upsamples; it is the stride-1 convolution of the input with S-1 zeros
+# inserted between neighbouring pixels, and in matrix form Y = W^T X, the
+# transpose of the standard convolution's matrix.
+
+def _torch_convT(x, w, b, stride, pad, out_pad, dil, groups, relu=False):
+    y = F.conv_transpose2d(torch.from_numpy(np.asarray(x, np.float64)), torch.from_numpy(np.asarray(w, np.float64)),
+                           None if b is None else torch.from_numpy(np.asarray(b, np.float64)),
+                           stride=stride, padding=pad, output_padding=out_pad, groups=groups, dilation=dil)
+    if relu:
+        y = torch.relu(y)
+    return y.numpy()
+
+
+# (N, Cin, H, W, Cout, K, stride, pad, out_pad, dil, groups)
+T_CASES = [
+    (2, 4, 5, 6, 6, 4, 2, 1, 0, 1, 1),   # 2x upsampling, kernel divisible by the stride
+    (1, 6, 4, 4, 4, 2, 2, 0, 0, 1, 2),   # kernel = stride: non-overlapping blocks, grouped
+    (2, 3, 5, 4, 5, 3, 2, 1, 1, 1, 1),   # odd kernel, output padding
+    (1, 4, 3, 5, 2, 3, 3, 0, 2, 1, 1),   # stride 3, output padding 2
+    (1, 2, 6, 5, 4, 3, 1, 1, 0, 1, 2),   # stride 1
+    (2, 4, 4, 3, 4, 3, 2, 2, 1, 2, 2),   # dilation 2, padding larger than the stride
+    (1, 3, 4, 4, 3, 5, 2, 3, 0, 1, 1),   # padding 3 with a 5x5 kernel
+    (1, 2, 3, 3, 2, 1, 2, 0, 1, 1, 1),   # 1x1 kernel, stride 2: odd outputs receive nothing
+    (1, 4, 5, 3, 4, 3, 2, 0, 1, 3, 1),   # dilation 3 with stride 2 (output padding < dilation)
+]
+
+
+def _t_tensors(case, seed, integer=False):
+    N, Cin, H, W, Cout, K, S, P, OP, D, G = case
+    rng = np.random.default_rng(seed)
+    if integer:
+        x = rng.integers(-3, 4, (N, Cin, H, W)).astype(np.float64)
+        w = rng.integers(-2, 3, (Cin, Cout // G, K, K)).astype(np.float64)
+        b = rng.integers(-4, 5, Cout).astype(np.float64)
+    else:
+        x = rng.standard_normal((N, Cin, H, W))
+        w = rng.standard_normal((Cin, Cout // G, K, K))
+        b = rng.standard_normal(Cout)
+    return x, w, b
+
+
+def test_t1_transposed_output_size():
+    """(H-1)S - 2P + D(K-1) + OP + 1; a standard convolution with the same
+    (K, S, P, D) maps every such output size back onto H (the transposed
+    convolution is that convolution's adjoint), and 2x upsampling layers give
+    twice the input."""
+    assert oracle.transpose_out_dim(28, 4, 2, 1) == 56
+    assert oracle.transpose_out_dim(56, 2, 2, 0) == 112
+    assert oracle.transpose_out_dim(7, 3, 2, 1, 1, 1) == 14
+    assert oracle.transpose_out_dim(5, 3, 1, 1) == 5
+    for H in range(1, 9):
+        for K in range(1, 6):
+            for S in range(1, 4):
+                for D in range(1, 3):
+                    for P in range(0, 3):
+                        for OP in range(0, S):   # the S sizes the strided convolution folds together
+                            Ho = oracle.transpose_out_dim(H, K, S, P, D, OP)
+                            if Ho >= 1 and Ho + 2 * P >= D * (K - 1) + 1:
+                                assert oracle.out_dim(Ho, K, S, P, D) == H, (H, K, S, P, D, OP)
+    assert oracle.transpose_out_dim(5, 3, 2, 1, 1, 2) == -1   # OP must stay below max(S, D)
+    assert oracle.transpose_out_dim(5, 3, 2, 1, 3, 2) == 5 * 2 - 2 + 6 + 2 - 1
+
+
+@pytest.mark.parametrize("case", T_CASES)
+def test_t2_transposed_equals_zero_insertion_then_stride1_conv(case):
+    """The page's own construction: insert S-1 zeros between neighbouring
+    input pixels, pad by D(K-1)-P (OP more at the far edge; a negative pad
+    crops), then a stride-1 convolution (the pinned direct loop) with the
+    kernel rotated by 180 degrees and, per group, input and output channel
+    roles swapped."""
+    N, Cin, H, W, Cout, K, S, P, OP, D, G = case
+    x, w, b = _t_tensors(case, 7)
+    y, s = oracle.conv_transpose2d(x, w, b, S, P, OP, D, G, relu=True)
+    z = np.zeros((N, Cin, (H - 1) * S + 1, (W - 1) * S + 1))
+    z[:, :, ::S, ::S] = x
+    e = D * (K - 1) - P
+    lo, hi = e, e + OP
+    z = np.pad(z, ((0, 0), (0, 0), (max(lo, 0), max(hi, 0)), (max(lo, 0), max(hi, 0))))
+    if lo < 0:
+        z = z[:, :, -lo:, -lo:]
+    if hi < 0:
+        z = z[:, :, :hi, :hi]
+    cin_g, cout_g = Cin // G, Cout // G
+    wc = np.zeros((Cout, cin_g, K, K))
+    for g in range(G):
+        blk = w[g * cin_g:(g + 1) * cin_g]                    # [cin_g][cout_g][K][K]
+        wc[g * cout_g:(g + 1) * cout_g] = blk.transpose(1, 0, 2, 3)[:, :, ::-1, ::-1]
+    yc, _ = oracle.conv2d(z, wc, b, 1, 0, D, G, relu=True)
+    assert yc.shape == y.shape
+    np.testing.assert_allclose(y, yc, rtol=0, atol=1e-12 * (float(s.max()) + 1))
+
+
+@pytest.mark.parametrize("case", T_CASES)
+def test_t3_transposed_is_the_adjoint_of_the_convolution(case):
+    """Y = W^T X: for integer tensors <conv(u), v> equals <u, convT(v)>
+    exactly, with the same weight read as the standard convolution's
+    [C_out'][C_in'/G][K][K] weight (Cin of the transposed convolution = the
+    standard convolution's output channels)."""
+    N, Cin, H, W, Cout, K, S, P, OP, D, G = case
+    v, w, _ = _t_tensors(case, 11, integer=True)
+    t, _ = oracle.conv_transpose2d(v, w, None, S, P, OP, D, G)
+    u = np.random.default_rng(13).integers(-3, 4, t.shape).astype(np.float64)
+    cu, _ = oracle.conv2d(u, w, None, S, P, D, G)
+    assert cu.shape == v.shape
+    assert float(np.sum(cu * v)) == float(np.sum(u * t))
+
+
+@pytest.mark.parametrize("case", T_CASES)
+def test_t4_transposed_matches_torch(case):
+    N, Cin, H, W, Cout, K, S, P, OP, D, G = case
+    x, w, b = _t_tensors(case, 17)
+    y, s = oracle.conv_transpose2d(x, w, b, S, P, OP, D, G, relu=True)
+    yt = _torch_convT(x, w, b, S, P, OP, D, G, relu=True)
+    assert y.shape == yt.shape
+    np.testing.assert_allclose(y, yt, rtol=0, atol=1e-12 * (float(s.max()) + 1))
+    sa, _ = oracle.conv_transpose2d(np.abs(x), np.abs(w), None, S, P, OP, D, G)
+    np.testing.assert_allclose(s, sa, rtol=1e-12, atol=0)
+
+
+def test_t5_kernel_equal_to_stride_is_blockwise_outer_product():
+    """K = S, P = 0: windows do not overlap, so output block (ih, iw) is
+    exactly sum_ci x[ci, ih, iw] * w[ci, co, :, :] plus the bias."""
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((2, 5, 3, 4))
+    w = rng.standard_normal((5, 3, 2, 2))
+    b = rng.standard_normal(3)
+    y, _ = oracle.conv_transpose2d(x, w, b, 2, 0, 0, 1, 1)
+    want = np.einsum("nchw,cokl->nohkwl", x, w).reshape(2, 3, 6, 8) + b[None, :, None, None]
+    np.testing.assert_allclose(y, want, rtol=0, atol=1e-12)
+
+
+def test_t6_transposed_points_match_full():
+    case = (2, 4, 5, 6, 6, 4, 2, 1, 1, 1, 2)
+    N, Cin, H, W, Cout, K, S, P, OP, D, G = case
+    x, w, b = _t_tensors(case, 23)
+    y, s = oracle.conv_transpose2d(x, w, b, S, P, OP, D, G, relu=True)
+    idx = np.random.default_rng(3).choice(y.size, 300, replace=False)
+    yp, sp = oracle.conv_transpose2d_points(x, w, idx, b, S, P, OP, D, G, relu=True)
+    np.testing.assert_allclose(yp, y.reshape(-1)[idx], rtol=0, atol=1e-12 * (float(s.max()) + 1))
+    np.testing.assert_allclose(sp, s.reshape(-1)[idx], rtol=1e-12, atol=1e-300)
+
+
 # ------------------------------------------------------------- planted mistakes
 
 _MUTATIONS = {
@@ -532,6 +676,20 @@ _MUTATIONS = {
     "relu_before_bias": ("double v = acc + (bias ? bias[co] : 0.0);\n    if (relu && v < 0.0) v = 0.0;",
                          "double v = (relu && acc < 0.0) ? 0.0 : acc;\n    v += (bias ? bias[co] : 0.0);"),
 }
+# the same kinds of mistakes in the transposed convolution's scatter
+_T_MUTATIONS = {
+    "t_drop_last_tap": ("for (long kw = 0; kw < Kw; ++kw) {\n                                const long ow",
+                        "for (long kw = 0; kw < Kw - (Kw > 1); ++kw) {\n                                const long ow"),
+    "t_unflipped_scatter": ("const long oh = ih * stride - pad + kh * dil;",
+                            "const long oh = ih * stride - pad + (Kh - 1 - kh) * dil;"),
+    "t_pad_sign": ("const long ow = iw * stride - pad + kw * dil;",
+                   "const long ow = iw * stride + pad + kw * dil;"),
+    "t_weight_roles_swapped": ("w[((c * cout_g + col) * Kh + kh) * Kw + kw];\n                                yp",
+                               "w[((col * cin_g + ci) * Kh + kh) * Kw + kw];\n                                yp"),
+    "t_stride_ignored": ("const long oh = ih * stride - pad + kh * dil;", "const long oh = ih - pad + kh * dil;"),
+    "t_wrong_group_base": ("const long c = g * cin_g + ci;\n                for (long ih",
+                           "const long c = ci;\n                for (long ih"),
+}
 
 
 @pytest.fixture(scope="module")
@@ -540,7 +698,7 @@ def mutant_libs():
     tmp = tempfile.mkdtemp(prefix="oracle_mut_")
     libs = {}
     try:
-        for name, (a, b) in _MUTATIONS.items():
+        for name, (a, b) in {**_MUTATIONS, **_T_MUTATIONS}.items():
             assert src.count(a) >= 1, name
             path = os.path.join(tmp, f"{name}.c")
             open(path, "w").write(src.replace(a, b, 1))
@@ -562,3 +720,16 @@ def test_planted_mistake_is_caught(name, mutant_libs):
     y, s = oracle.conv2d(x, w, b, 1, 2, 2, 2, relu=True, lib=lib)
     yt = _torch_conv(x, w, b, 1, 2, 2, 2, relu=True)
     assert not np.all(np.abs(y - yt) <= 1e-12 * (s + np.abs(b)[None, :, None, None]))
+
+
+@pytest.mark.parametrize("name", list(_T_MUTATIONS))
+def test_planted_transposed_mistake_is_caught(name, mutant_libs):
+    """Each planted mistake in the scatter makes the torch cross-check of a
+    small grouped, padded stride-2 transposed convolution fail."""
+    lib = mutant_libs[name]
+    case = (2, 4, 5, 4, 6, 3, 2, 1, 1, 1, 2)
+    N, Cin, H, W, Cout, K, S, P, OP, D, G = case
+    x, w, b = _t_tensors(case, 41)
+    y, s = oracle.conv_transpose2d(x, w, b, S, P, OP, D, G, relu=True, lib=lib)
+    yt = _torch_convT(x, w, b, S, P, OP, D, G, relu=True)
+    assert not np.all(np.abs(y - yt) <= 1e-12 * (s + 1))
