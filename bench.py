@@ -57,20 +57,37 @@ ROTATE_BYTES = 512 << 20
 METRIC = "conv2d fwd TFLOP/s (GB/s for depthwise) and % of MI355X roofline, 1 GPU"
 KERNEL_SOURCES = {"direct": ["direct.hip"], "depthwise": ["depthwise.hip", "dwrow.hpp"],
                   "gemm1x1": ["pointwise.hip", "igemm.hip"], "igemm_gather": ["igemm.hip"],
-                  "igemm_halo": ["igemm_halo.hip"], "separable": ["separable.hip", "dwrow.hpp"]}
+                  "igemm_halo": ["igemm_halo.hip"], "separable": ["separable.hip", "dwrow.hpp"],
+                  "transposed_igemm_gather": ["igemm.hip"], "transposed_direct": ["transposed.hip"]}
 
 
 def out_hw(ly):
+    if ly.transposed:
+        ho = (ly.H - 1) * ly.stride - 2 * ly.pad + ly.dilation * (ly.Kh - 1) + ly.out_pad + 1
+        wo = (ly.W - 1) * ly.stride - 2 * ly.pad + ly.dilation * (ly.Kw - 1) + ly.out_pad + 1
+        return ho, wo
     ho = (ly.H + 2 * ly.pad - ly.dilation * (ly.Kh - 1) - 1) // ly.stride + 1
     wo = (ly.W + 2 * ly.pad - ly.dilation * (ly.Kw - 1) - 1) // ly.stride + 1
     return ho, wo
 
 
+def _landing_pairs(n_in, k, stride, pad, dil, n_out):
+    """(input, tap) pairs along one axis whose product lands inside the output
+    of a transposed convolution."""
+    return sum(1 for i in range(n_in) for t in range(k) if 0 <= i * stride - pad + t * dil < n_out)
+
+
 def algorithmic(ly):
-    """Nominal FLOPs and bytes (each tensor moved once) of one launch."""
+    """Nominal FLOPs and bytes (each tensor moved once) of one launch.  A
+    transposed layer counts the products that land inside its output."""
     ho, wo = out_hw(ly)
     esz = 4 if ly.dtype == ci.F32 else 2
-    flops = 2 * ly.N * ho * wo * ly.Cout * (ly.Cin // ly.groups) * ly.Kh * ly.Kw
+    if ly.transposed:
+        flops = 2 * ly.N * ly.Cout * (ly.Cin // ly.groups) \
+            * _landing_pairs(ly.H, ly.Kh, ly.stride, ly.pad, ly.dilation, ho) \
+            * _landing_pairs(ly.W, ly.Kw, ly.stride, ly.pad, ly.dilation, wo)
+    else:
+        flops = 2 * ly.N * ho * wo * ly.Cout * (ly.Cin // ly.groups) * ly.Kh * ly.Kw
     nbytes = esz * (ly.N * ly.Cin * ly.H * ly.W + ly.Cout * (ly.Cin // ly.groups) * ly.Kh * ly.Kw
                     + ly.N * ly.Cout * ho * wo)
     if ly.epilogue & ci.EPI_BIAS:
@@ -135,15 +152,19 @@ def cpu_baseline(cid, li, x, w, b, target_s, unit):
     k = 0
     t0 = time.perf_counter()
     while k < ly.N and (k == 0 or time.perf_counter() - t0 < target_s):
-        oracle.conv2d(x[k:k + 1], w, b, ly.stride, ly.pad, ly.dilation, ly.groups, relu=relu,
-                      with_scale=False)
+        if ly.transposed:
+            oracle.conv_transpose2d(x[k:k + 1], w, b, ly.stride, ly.pad, ly.out_pad, ly.dilation, ly.groups,
+                                    relu=relu)
+        else:
+            oracle.conv2d(x[k:k + 1], w, b, ly.stride, ly.pad, ly.dilation, ly.groups, relu=relu,
+                          with_scale=False)
         k += 1
     dt = time.perf_counter() - t0
     frac = k / ly.N
     value = (flops * frac / dt / 1e12) if unit == "TFLOP/s" else (nbytes * frac / dt / 1e9)
     return {"value": round(value, 6), "unit": unit, "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"first {k} of {ly.N} images, all {ly.Cout} output channels, fp64 direct "
-                      f"loop ({dt:.1f} s)",
+            "sample": f"first {k} of {ly.N} images, all {ly.Cout} output channels, fp64 "
+                      f"{'scatter' if ly.transposed else 'direct'} loop ({dt:.1f} s)",
             "host_cpu": host_cpu()}
 
 
@@ -156,9 +177,14 @@ def bench_layer(cid, li, steps, warmup, cpu_seconds, with_cpu):
     dt_lib = c2.F32 if ly.dtype == ci.F32 else c2.BF16
     tdt = torch.float32 if ly.dtype == ci.F32 else torch.bfloat16
     esz = 4 if ly.dtype == ci.F32 else 2
-    path = c2.conv2d_select_path(ly.N, ly.Cin, ly.H, ly.W, ly.Cout, ly.Kh, ly.Kw, ly.stride, ly.pad,
-                                 ly.dilation, ly.groups, dt_lib)
-    pname = c2.PATH_NAMES[path]
+    if ly.transposed:
+        path = c2.conv2d_transpose_select_path(ly.N, ly.Cin, ly.H, ly.W, ly.Cout, ly.Kh, ly.Kw, ly.stride,
+                                               ly.pad, ly.out_pad, ly.dilation, ly.groups, dt_lib)
+        pname = "transposed_" + c2.PATH_NAMES[path]
+    else:
+        path = c2.conv2d_select_path(ly.N, ly.Cin, ly.H, ly.W, ly.Cout, ly.Kh, ly.Kw, ly.stride, ly.pad,
+                                     ly.dilation, ly.groups, dt_lib)
+        pname = c2.PATH_NAMES[path]
     flops, nbytes = algorithmic(ly)
     bound = bound_of(ly)
 
@@ -170,7 +196,10 @@ def bench_layer(cid, li, steps, warmup, cpu_seconds, with_cpu):
     w_dev = torch.from_numpy(w).to(dev).to(tdt)
     wp = torch.empty(c2.conv2d_packed_weight_bytes(ly.Cout, ly.Cin, ly.Kh, ly.Kw, ly.groups, dt_lib)
                      // esz, dtype=tdt, device=dev)
-    c2.conv2d_pack_weights(w_dev, wp, ly.Cout, ly.Cin, ly.Kh, ly.Kw, ly.groups, dt_lib)
+    if ly.transposed:
+        c2.conv2d_transpose_pack_weights(w_dev, wp, ly.Cin, ly.Cout, ly.Kh, ly.Kw, ly.groups, dt_lib)
+    else:
+        c2.conv2d_pack_weights(w_dev, wp, ly.Cout, ly.Cin, ly.Kh, ly.Kw, ly.groups, dt_lib)
     bias = torch.from_numpy(b).to(dev) if b is not None else None
     set_bytes = esz * (x.size + ly.N * ly.Cout * ho * wo)
     R = max(1, min(16, math.ceil(ROTATE_BYTES / set_bytes)))
@@ -182,9 +211,14 @@ def bench_layer(cid, li, steps, warmup, cpu_seconds, with_cpu):
 
     def step(i):
         j = i % R
-        c2.conv2d_fwd_nhwc_packed(xs[j], wp, bias, ys[j], ly.N, ly.Cin, ly.H, ly.W, ly.Cout, ly.Kh,
-                                  ly.Kw, ly.stride, ly.pad, ly.dilation, ly.groups, dt_lib,
-                                  ly.epilogue, stream)
+        if ly.transposed:
+            c2.conv2d_transpose_fwd_nhwc_packed(xs[j], wp, bias, ys[j], ly.N, ly.Cin, ly.H, ly.W, ly.Cout,
+                                                ly.Kh, ly.Kw, ly.stride, ly.pad, ly.out_pad, ly.dilation,
+                                                ly.groups, dt_lib, ly.epilogue, stream)
+        else:
+            c2.conv2d_fwd_nhwc_packed(xs[j], wp, bias, ys[j], ly.N, ly.Cin, ly.H, ly.W, ly.Cout, ly.Kh,
+                                      ly.Kw, ly.stride, ly.pad, ly.dilation, ly.groups, dt_lib,
+                                      ly.epilogue, stream)
 
     for i in range(warmup):
         step(i)
@@ -228,7 +262,8 @@ def bench_layer(cid, li, steps, warmup, cpu_seconds, with_cpu):
         "dtype": "f32" if ly.dtype == ci.F32 else "bf16",
         "data": "synthetic (seeded, workload shapes and distributions; no dataset)",
         "config": {
-            "workload": f"cfg{cid} {ly.name}: N={ly.N} Cin={ly.Cin} {ly.H}x{ly.W} -> Cout={ly.Cout} "
+            "workload": f"cfg{cid} {ly.name}: {'transposed ' if ly.transposed else ''}N={ly.N} Cin={ly.Cin} "
+                        f"{ly.H}x{ly.W} -> Cout={ly.Cout} {ho}x{wo} "
                         f"{ly.Kh}x{ly.Kw} s{ly.stride} p{ly.pad} d{ly.dilation} g{ly.groups}"
                         f"{' bias' if ly.epilogue & ci.EPI_BIAS else ''}"
                         f"{' relu' if ly.epilogue & ci.EPI_RELU else ''}",

@@ -31,6 +31,8 @@ ERR_NULL, ERR_DTYPE, ERR_EPILOGUE, ERR_ALIGN = -6, -7, -8, -9
 # Every symbol include/conv2d.h declares.
 EXPORTS = ("conv2d_fwd", "conv2d_fwd_nhwc_packed", "conv2d_fwd_bn", "conv2d_fwd_nhwc_packed_bn",
            "conv2d_fwd_separable_nhwc",
+           "conv2d_transpose_fwd", "conv2d_transpose_fwd_nhwc_packed", "conv2d_transpose_pack_weights",
+           "conv2d_transpose_out_dim", "conv2d_transpose_check_args", "conv2d_transpose_select_path",
            "conv2d_packed_weight_bytes",
            "conv2d_pack_weights", "conv2d_nchw_to_nhwc", "conv2d_nhwc_to_nchw",
            "conv2d_out_dim", "conv2d_check_args", "conv2d_select_path",
@@ -62,6 +64,15 @@ def _load() -> ctypes.CDLL:
         f.argtypes, f.restype = [P] * 6 + [I] * 13 + [P], I
     lib.conv2d_fwd_separable_nhwc.argtypes = [P] * 6 + [I] * 10 + [P]
     lib.conv2d_fwd_separable_nhwc.restype = I
+    for name in ("conv2d_transpose_fwd", "conv2d_transpose_fwd_nhwc_packed"):
+        f = getattr(lib, name)
+        f.argtypes, f.restype = [P] * 4 + [I] * 14 + [P], I
+    lib.conv2d_transpose_pack_weights.argtypes = [P, P] + [I] * 6 + [P]
+    lib.conv2d_transpose_pack_weights.restype = I
+    lib.conv2d_transpose_out_dim.argtypes, lib.conv2d_transpose_out_dim.restype = [I] * 6, I
+    lib.conv2d_transpose_check_args.argtypes = [P] * 4 + [I] * 14
+    lib.conv2d_transpose_check_args.restype = I
+    lib.conv2d_transpose_select_path.argtypes, lib.conv2d_transpose_select_path.restype = [I] * 13, I
     lib.conv2d_packed_weight_bytes.argtypes = [I] * 6
     lib.conv2d_packed_weight_bytes.restype = ctypes.c_size_t
     lib.conv2d_pack_weights.argtypes = [P, P] + [I] * 6 + [P]
@@ -155,6 +166,45 @@ def conv2d_fwd_separable_nhwc(x, w_dw, bias_dw, w_pw, bias_pw, y, N, C, H, W, Co
                                          _ptr(y), N, C, H, W, Cout, stride, pad, dtype, dw_epilogue,
                                          pw_epilogue, _stream(stream)),
            "conv2d_fwd_separable_nhwc")
+
+
+def conv2d_transpose_fwd(x, w, bias, y, N, Cin, H, W, Cout, Kh, Kw, stride, pad, output_padding, dilation,
+                         groups, dtype, epilogue, stream=None) -> None:
+    """Transposed convolution: NCHW x, [Cin][Cout/G][Kh][Kw] w, fp32 bias or None, NCHW y."""
+    _check(lib.conv2d_transpose_fwd(_ptr(x), _ptr(w), _ptr(bias), _ptr(y), N, Cin, H, W, Cout, Kh, Kw, stride,
+                                    pad, output_padding, dilation, groups, dtype, epilogue, _stream(stream)),
+           "conv2d_transpose_fwd")
+
+
+def conv2d_transpose_fwd_nhwc_packed(x, w_packed, bias, y, N, Cin, H, W, Cout, Kh, Kw, stride, pad,
+                                     output_padding, dilation, groups, dtype, epilogue, stream=None) -> None:
+    """Transposed convolution: NHWC x, packed w (conv2d_transpose_pack_weights), NHWC y."""
+    _check(lib.conv2d_transpose_fwd_nhwc_packed(_ptr(x), _ptr(w_packed), _ptr(bias), _ptr(y), N, Cin, H, W,
+                                                Cout, Kh, Kw, stride, pad, output_padding, dilation, groups,
+                                                dtype, epilogue, _stream(stream)),
+           "conv2d_transpose_fwd_nhwc_packed")
+
+
+def conv2d_transpose_pack_weights(w, w_packed, Cin, Cout, Kh, Kw, groups, dtype, stream=None) -> None:
+    _check(lib.conv2d_transpose_pack_weights(_ptr(w), _ptr(w_packed), Cin, Cout, Kh, Kw, groups, dtype,
+                                             _stream(stream)), "conv2d_transpose_pack_weights")
+
+
+def conv2d_transpose_out_dim(size, k, stride=1, pad=0, dilation=1, output_padding=0) -> int:
+    return int(lib.conv2d_transpose_out_dim(size, k, stride, pad, dilation, output_padding))
+
+
+def conv2d_transpose_check_args(x, w, bias, y, N, Cin, H, W, Cout, Kh, Kw, stride, pad, output_padding,
+                                dilation, groups, dtype, epilogue) -> int:
+    return int(lib.conv2d_transpose_check_args(_ptr(x), _ptr(w), _ptr(bias), _ptr(y), N, Cin, H, W, Cout, Kh,
+                                               Kw, stride, pad, output_padding, dilation, groups, dtype,
+                                               epilogue))
+
+
+def conv2d_transpose_select_path(N, Cin, H, W, Cout, Kh, Kw, stride, pad, output_padding, dilation, groups,
+                                 dtype) -> int:
+    return _check(int(lib.conv2d_transpose_select_path(N, Cin, H, W, Cout, Kh, Kw, stride, pad, output_padding,
+                                                       dilation, groups, dtype)), "conv2d_transpose_select_path")
 
 
 def conv2d_packed_weight_bytes(Cout, Cin, Kh, Kw, groups, dtype) -> int:

@@ -19,6 +19,9 @@ struct Shape {
     // v = (sum [+ bias]) * scale[co] + shift[co], then the ReLU.
     const float* scale;
     const float* shift;
+    // Transposed convolution only: extra output rows/columns at the far edge
+    // (H, W are then the input extent and Ho, Wo the upsampled output).
+    int out_pad;
 };
 
 // One fused depthwise-separable call (3x3 depthwise, then 1x1), validated on
@@ -31,7 +34,9 @@ struct SepShape {
 };
 
 enum Layout { NCHW = 0, NHWC = 1 };
-enum WLayout { W_OIHW = 0, W_PACKED = 1, W_DW = 2 };  // raw, [Cout][Kh][Kw][Cin/G], [Kh][Kw][C]
+// raw [Cout][Cin/G][Kh][Kw], packed [Cout][Kh][Kw][Cin/G], depthwise [Kh][Kw][C],
+// transposed-convolution raw [Cin][Cout/G][Kh][Kw]
+enum WLayout { W_OIHW = 0, W_PACKED = 1, W_DW = 2, W_IOHW = 3 };
 
 typedef uint16_t bf16_t;   // raw bf16 bit pattern
 
@@ -123,6 +128,15 @@ bool pointwise_supports(const Shape& s);
 hipError_t launch_separable(const SepShape& s, const void* x, const void* w_dw, const float* b_dw,
                             const void* w_pw, const float* b_pw, void* y, hipStream_t st);
 bool separable_supports(const SepShape& s);
+
+// Transposed convolution (s.H, s.W input; s.Ho, s.Wo output).
+hipError_t launch_tconv_direct(const Shape& s, const void* x, int xl, const void* w, int wl,
+                               const float* bias, void* y, int yl, hipStream_t st);
+hipError_t launch_igemm_transposed(const Shape& s, const void* x, const void* w_packed, const float* bias,
+                                   void* y, hipStream_t st);
+bool igemm_transposed_supports(const Shape& s);
+hipError_t launch_tpack_weights(const void* w, void* wp, int Cin, int cout_g, int groups, int Kh, int Kw,
+                                int elem_bytes, hipStream_t st);
 
 hipError_t launch_transpose(const void* src, void* dst, int batch, int rows, int cols,
                             int elem_bytes, hipStream_t st);

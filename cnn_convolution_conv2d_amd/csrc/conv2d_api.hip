@@ -76,6 +76,7 @@ int validate(const void* x, const void* w, const float* bias, const void* y,
         s.cin_g = Cin / groups; s.cout_g = Cout / groups;
         s.dtype = dtype; s.epilogue = epilogue;
         s.scale = nullptr; s.shift = nullptr;
+        s.out_pad = 0;
         *out = s;
     }
     return CONV2D_OK;
@@ -243,6 +244,81 @@ int fwd_nchw(const void* x, const void* w, const float* bias, const float* scale
     return conv2d_nhwc_to_nchw(yn, y, N, Cout, s.Ho, s.Wo, dtype, stream);
 }
 
+// ---- transposed convolution
+
+// Output extent of the transposed convolution: (in-1)S - 2P + D(k-1) + OP + 1.
+long long tout_extent(long long in, long long k, long long s, long long p, long long d, long long op) {
+    return (in - 1) * s - 2 * p + d * (k - 1) + op + 1;
+}
+
+int validate_transposed(const void* x, const void* w, const float* bias, const void* y, int N, int Cin, int H,
+                        int W, int Cout, int Kh, int Kw, int stride, int pad, int out_pad, int dilation,
+                        int groups, int dtype, int epilogue, Shape* out) {
+    if (dtype != CONV2D_F32 && dtype != CONV2D_BF16)
+        return set_error(CONV2D_ERR_DTYPE, "unknown dtype %d", dtype);
+    if (epilogue < 0 || (epilogue & ~(CONV2D_EPI_BIAS | CONV2D_EPI_RELU)))
+        return set_error(CONV2D_ERR_EPILOGUE, "unknown epilogue bits 0x%x", epilogue);
+    if (N < 1 || Cin < 1 || H < 1 || W < 1 || Cout < 1 || Kh < 1 || Kw < 1)
+        return set_error(CONV2D_ERR_ARG, "sizes must be >= 1 (N=%d Cin=%d H=%d W=%d Cout=%d Kh=%d Kw=%d)",
+                         N, Cin, H, W, Cout, Kh, Kw);
+    if (stride < 1 || dilation < 1 || pad < 0 || groups < 1)
+        return set_error(CONV2D_ERR_ARG, "need stride>=1, dilation>=1, pad>=0, groups>=1 (got %d %d %d %d)",
+                         stride, dilation, pad, groups);
+    if (out_pad < 0 || (out_pad >= stride && out_pad >= dilation))
+        return set_error(CONV2D_ERR_ARG, "output padding %d must be >= 0 and below stride %d or dilation %d",
+                         out_pad, stride, dilation);
+    if (Cin % groups || Cout % groups)
+        return set_error(CONV2D_ERR_GROUPS, "Cin=%d and Cout=%d must be divisible by groups=%d", Cin, Cout, groups);
+    if (!x || !w || !y) return set_error(CONV2D_ERR_NULL, "x, w and y must be non-NULL");
+    if ((epilogue & CONV2D_EPI_BIAS) && !bias)
+        return set_error(CONV2D_ERR_NULL, "bias is NULL but the epilogue asks for it");
+    const long long Ho = tout_extent(H, Kh, stride, pad, dilation, out_pad);
+    const long long Wo = tout_extent(W, Kw, stride, pad, dilation, out_pad);
+    if (Ho < 1 || Wo < 1) return set_error(CONV2D_ERR_EMPTY_OUTPUT, "empty output (Ho=%lld Wo=%lld)", Ho, Wo);
+    const long long xe = (long long)N * Cin * H * W, ye = (long long)N * Cout * Ho * Wo;
+    const long long we = (long long)Cout * (Cin / groups) * Kh * Kw;
+    if (xe >= INT_MAX || ye >= INT_MAX || we >= INT_MAX || Ho >= INT_MAX / 2 || Wo >= INT_MAX / 2 ||
+        (long long)pad + (long long)dilation * Kh >= INT_MAX / 2 || (long long)dilation * Kw >= INT_MAX / 2)
+        return set_error(CONV2D_ERR_UNSUPPORTED, "tensor too large for 32-bit element offsets");
+    if (out) {
+        Shape s;
+        s.N = N; s.Cin = Cin; s.H = H; s.W = W; s.Cout = Cout; s.Kh = Kh; s.Kw = Kw;
+        s.stride = stride; s.pad = pad; s.dil = dilation; s.groups = groups;
+        s.Ho = (int)Ho; s.Wo = (int)Wo;
+        s.cin_g = Cin / groups; s.cout_g = Cout / groups;
+        s.dtype = dtype; s.epilogue = epilogue;
+        s.scale = nullptr; s.shift = nullptr;
+        s.out_pad = out_pad;
+        *out = s;
+    }
+    return CONV2D_OK;
+}
+
+// Transposed paths: the phase-split implicit GEMM (reported as the gather
+// path) for channel-aligned bf16, the direct loop otherwise.
+int choose_tpath(const Shape& s) {
+    const bool mfma = s.dtype == CONV2D_BF16 && igemm_transposed_supports(s);
+    const int forced = __atomic_load_n(&g_path_override, __ATOMIC_RELAXED);
+    if (forced == CONV2D_PATH_AUTO) return mfma ? CONV2D_PATH_IGEMM_GATHER : CONV2D_PATH_DIRECT;
+    if (forced == CONV2D_PATH_DIRECT) return CONV2D_PATH_DIRECT;
+    if ((forced == CONV2D_PATH_IGEMM || forced == CONV2D_PATH_IGEMM_GATHER) && mfma)
+        return CONV2D_PATH_IGEMM_GATHER;
+    return set_error(CONV2D_ERR_UNSUPPORTED, "forced path %d cannot run this transposed convolution", forced);
+}
+
+int run_tnhwc(int path, const Shape& s, const void* x, const void* wp, const float* bias, void* y,
+              hipStream_t st) {
+    hipError_t e;
+    if (path == CONV2D_PATH_DIRECT) {
+        e = launch_tconv_direct(s, x, NHWC, wp, W_PACKED, bias, y, NHWC, st);
+    } else {
+        if (!(aligned16(x) && aligned16(wp) && aligned16(y)))
+            return set_error(CONV2D_ERR_ALIGN, "x, w_packed and y must be 16-byte aligned for path %d", path);
+        e = launch_igemm_transposed(s, x, wp, bias, y, st);
+    }
+    return e == hipSuccess ? CONV2D_OK : hip_fail(e, "transposed kernel launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -388,6 +464,93 @@ int conv2d_fwd_separable_nhwc(const void* x, const void* w_dw, const float* bias
         return set_error(CONV2D_ERR_ALIGN, "x, w_dw, w_pw and y must be 16-byte aligned");
     const hipError_t e = launch_separable(ss, x, w_dw, bias_dw, w_pw, bias_pw, y, stream);
     return e == hipSuccess ? CONV2D_OK : hip_fail(e, "separable launch");
+}
+
+int conv2d_transpose_out_dim(int in, int k, int stride, int pad, int dilation, int output_padding) {
+    if (stride < 1 || dilation < 1 || k < 1 || pad < 0 || in < 1 || output_padding < 0 ||
+        (output_padding >= stride && output_padding >= dilation))
+        return CONV2D_ERR_ARG;
+    const long long r = tout_extent(in, k, stride, pad, dilation, output_padding);
+    if (r > INT_MAX) return CONV2D_ERR_ARG;
+    return r < 0 ? 0 : (int)r;
+}
+
+int conv2d_transpose_check_args(const void* x, const void* w, const float* bias, const void* y, int N, int Cin,
+                                int H, int W, int Cout, int Kh, int Kw, int stride, int pad, int output_padding,
+                                int dilation, int groups, int dtype, int epilogue) {
+    return validate_transposed(x, w, bias, y, N, Cin, H, W, Cout, Kh, Kw, stride, pad, output_padding, dilation,
+                               groups, dtype, epilogue, nullptr);
+}
+
+int conv2d_transpose_select_path(int N, int Cin, int H, int W, int Cout, int Kh, int Kw, int stride, int pad,
+                                 int output_padding, int dilation, int groups, int dtype) {
+    Shape s;
+    static const char dummy[16] = {};
+    int rc = validate_transposed(dummy, dummy, nullptr, dummy, N, Cin, H, W, Cout, Kh, Kw, stride, pad,
+                                 output_padding, dilation, groups, dtype, 0, &s);
+    if (rc) return rc;
+    return choose_tpath(s);
+}
+
+int conv2d_transpose_pack_weights(const void* w, void* w_packed, int Cin, int Cout, int Kh, int Kw, int groups,
+                                  int dtype, hipStream_t stream) {
+    if (dtype != CONV2D_F32 && dtype != CONV2D_BF16) return set_error(CONV2D_ERR_DTYPE, "unknown dtype %d", dtype);
+    if (Cout < 1 || Cin < 1 || Kh < 1 || Kw < 1 || groups < 1)
+        return set_error(CONV2D_ERR_ARG, "sizes must be >= 1");
+    if (Cin % groups || Cout % groups) return set_error(CONV2D_ERR_GROUPS, "channels not divisible by groups");
+    if (!w || !w_packed) return set_error(CONV2D_ERR_NULL, "w and w_packed must be non-NULL");
+    if ((long long)Cout * (Cin / groups) * Kh * Kw >= INT_MAX)
+        return set_error(CONV2D_ERR_UNSUPPORTED, "weight too large");
+    hipError_t e = launch_tpack_weights(w, w_packed, Cin, Cout / groups, groups, Kh, Kw, (int)elem_bytes(dtype),
+                                        stream);
+    return e == hipSuccess ? CONV2D_OK : hip_fail(e, "transpose_pack_weights launch");
+}
+
+int conv2d_transpose_fwd_nhwc_packed(const void* x, const void* w_packed, const float* bias, void* y, int N,
+                                     int Cin, int H, int W, int Cout, int Kh, int Kw, int stride, int pad,
+                                     int output_padding, int dilation, int groups, int dtype, int epilogue,
+                                     hipStream_t stream) {
+    Shape s;
+    int rc = validate_transposed(x, w_packed, bias, y, N, Cin, H, W, Cout, Kh, Kw, stride, pad, output_padding,
+                                 dilation, groups, dtype, epilogue, &s);
+    if (rc) return rc;
+    const int path = choose_tpath(s);
+    if (path < 0) return path;
+    return run_tnhwc(path, s, x, w_packed, bias, y, stream);
+}
+
+int conv2d_transpose_fwd(const void* x, const void* w, const float* bias, void* y, int N, int Cin, int H, int W,
+                         int Cout, int Kh, int Kw, int stride, int pad, int output_padding, int dilation,
+                         int groups, int dtype, int epilogue, hipStream_t stream) {
+    Shape s;
+    int rc = validate_transposed(x, w, bias, y, N, Cin, H, W, Cout, Kh, Kw, stride, pad, output_padding,
+                                 dilation, groups, dtype, epilogue, &s);
+    if (rc) return rc;
+    const int path = choose_tpath(s);
+    if (path < 0) return path;
+    if (path == CONV2D_PATH_DIRECT) {
+        // the direct loop reads the pages' layouts as they are
+        const hipError_t e = launch_tconv_direct(s, x, NCHW, w, W_IOHW, bias, y, NCHW, stream);
+        return e == hipSuccess ? CONV2D_OK : hip_fail(e, "transposed direct launch");
+    }
+    const size_t eb = elem_bytes(dtype);
+    const size_t wb = round_up(conv2d_packed_weight_bytes(Cout, Cin, Kh, Kw, groups, dtype), 256);
+    const size_t xb = round_up((size_t)N * Cin * H * W * eb, 256);
+    const size_t yb = round_up((size_t)N * Cout * s.Ho * s.Wo * eb, 256);
+    void* scratch = nullptr;
+    rc = get_scratch(wb + xb + yb, &scratch);
+    if (rc) return rc;
+    char* base = static_cast<char*>(scratch);
+    void* wp = base;
+    void* xn = base + wb;
+    void* yn = base + wb + xb;
+    rc = conv2d_transpose_pack_weights(w, wp, Cin, Cout, Kh, Kw, groups, dtype, stream);
+    if (rc) return rc;
+    rc = conv2d_nchw_to_nhwc(x, xn, N, Cin, H, W, dtype, stream);
+    if (rc) return rc;
+    rc = run_tnhwc(path, s, xn, wp, bias, yn, stream);
+    if (rc) return rc;
+    return conv2d_nhwc_to_nchw(yn, y, N, Cout, s.Ho, s.Wo, dtype, stream);
 }
 
 void conv2d_release_scratch(void) {

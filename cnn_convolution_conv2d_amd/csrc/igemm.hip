@@ -29,6 +29,18 @@
 // 1x1 / stride 1 / pad 0 / groups 1 (lincklin.cn sections 21-22; lpnh.cn
 // section 4.3): B[k][p] = X[p][k], the NHWC activation read as a row-major
 // [N*H*W][Cin] matrix -- a plain GEMM with no window arithmetic.
+//
+// Transposed convolution (lpnh.cn sections 2.3 and 4.2: the stride-1
+// convolution of the input with S-1 zeros inserted between neighbouring
+// pixels).  Most taps of that convolution meet an inserted zero.  Which taps
+// do not depends only on the output pixel's phase (oh mod S, ow mod S): for
+// the outputs oh = ph + S*u, tap kh reaches input row (oh + P - kh*D)/S when
+// kh*D = (ph + P) mod S, i.e. for kh = k0, k0 + S/gcd(S,D), ...; the input
+// row is then u + base - j*D/gcd(S,D) for the j-th such tap.  Each workgroup
+// therefore owns one phase and runs the same implicit GEMM over only that
+// phase's taps (per axis about K/S of them), on the packed weight
+// [Cout][Kh][Kw][Cin/G] of the transposed weight; its output pixels sit S
+// apart in the output.
 #include "mfma.hpp"
 #include "../../include/conv2d.h"
 
@@ -54,13 +66,41 @@ namespace {
 
 constexpr int kThreads = 256;
 
-template <int BM, int BN, int WGM, int WGN, int BK, bool IS1X1, bool BIAS, bool RELU>
+// What the implicit GEMM computes: a convolution, the 1x1 plain GEMM, or one
+// output phase of a transposed convolution.
+enum Mode { kConv = 0, kGemm1x1 = 1, kTransposed = 2 };
+
+// The taps of one output phase along one axis (transposed convolution):
+// taps k0 + j*kstep for j < n; tap j reads input u + base + j*d for the
+// phase's output u.
+struct TapAxis {
+    int n, k0, kstep, base, d;
+};
+
+__device__ __forceinline__ TapAxis tap_axis(int ph, int K, int S, int P, int D) {
+    TapAxis a;
+    const int r = (ph + P) % S;
+    int k0 = -1;
+    for (int k = 0; k < S && k < K; ++k)
+        if ((k * D) % S == r) { k0 = k; break; }
+    int gcd = S, b = D;  // gcd(S, D)
+    while (b) { const int t = gcd % b; gcd = b; b = t; }
+    a.kstep = S / gcd;
+    a.n = k0 < 0 ? 0 : (K - 1 - k0) / a.kstep + 1;
+    a.k0 = k0 < 0 ? 0 : k0;
+    a.base = (ph + P) / S - (a.k0 * D) / S;
+    a.d = -(D / gcd);
+    return a;
+}
+
+template <int BM, int BN, int WGM, int WGN, int BK, int MODE, bool BIAS, bool RELU>
 __global__ __launch_bounds__(kThreads) void igemm_kernel(const bf16_t* __restrict__ x,
                                                          const bf16_t* __restrict__ wp,
                                                          const float* __restrict__ bias,
                                                          bf16_t* __restrict__ y, Shape s,
                                                          int n_ptiles, int n_ctiles) {
     static_assert(BK == 32 || BK == 64, "K step of 32 or 64 channels");
+    constexpr bool IS1X1 = MODE == kGemm1x1, TR = MODE == kTransposed;
     constexpr int kChunks = BK / 8;                // 16-byte chunks per LDS row
     constexpr int KS = BK / 16;                    // MFMA K slices per step
     constexpr int WTM = BM / WGM, WTN = BN / WGN;  // wave tile
@@ -81,12 +121,32 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(const bf16_t* __restric
     const int ct = tile % n_ctiles;          // output-channel tile (fastest)
     tile /= n_ctiles;
     const int g = tile % s.groups;           // group
-    const int pt = tile / s.groups;          // pixel tile (slowest)
+    int pt = tile / s.groups;                // pixel tile (slowest)
 
-    const int npix = s.N * s.Ho * s.Wo;
-    const int KK = s.Kh * s.Kw;
+    // Transposed: the phase (ph_h, ph_w) sits between the group and the pixel
+    // tile, so neighbouring workgroups share input rows.  Its pixel grid is
+    // N x uh_n x uw_n with output (ph_h + S*uh, ph_w + S*uw).
+    int ph_h = 0, ph_w = 0, uh_n = 1, uw_n = 1;
+    TapAxis ah = {}, aw = {};
+    if constexpr (TR) {
+        const int nph = s.stride * s.stride;
+        const int ph = pt % nph;
+        pt /= nph;
+        ph_h = ph / s.stride;
+        ph_w = ph % s.stride;
+        uh_n = (s.Ho - ph_h + s.stride - 1) / s.stride;
+        uw_n = (s.Wo - ph_w + s.stride - 1) / s.stride;
+        ah = tap_axis(ph_h, s.Kh, s.stride, s.pad, s.dil);
+        aw = tap_axis(ph_w, s.Kw, s.stride, s.pad, s.dil);
+    }
+    const int npix = TR ? s.N * uh_n * uw_n : s.N * s.Ho * s.Wo;
+    if (TR && pt * BN >= npix) return;  // a phase with fewer pixels than the largest (uniform)
+    const int KK = s.Kh * s.Kw;                   // taps of the packed weight
+    const int ntaps = TR ? ah.n * aw.n : KK;      // taps this workgroup walks
+    const int tap_dh = TR ? ah.d : s.dil, tap_dw = TR ? aw.d : s.dil;
+    const int ntw = TR ? aw.n : s.Kw;
     const int nchunk = (s.cin_g + BK - 1) / BK;
-    const int nsteps = KK * nchunk;
+    const int nsteps = ntaps * nchunk;
     const int co_tile = ct * BM;
 
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)s.N * s.H * s.W * s.Cin * 2u);
@@ -113,11 +173,16 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(const bf16_t* __restric
         const int p = pt * BN + prow;
         const bool ok = p < npix;
         const int pp = ok ? p : 0;
-        const int wo = pp % s.Wo;
-        const int t = pp / s.Wo;
-        const int ho = t % s.Ho;
-        const int n = t / s.Ho;
-        if (IS1X1) {
+        const int ow_n = TR ? uw_n : s.Wo, oh_n = TR ? uh_n : s.Ho;
+        const int wo = pp % ow_n;
+        const int t = pp / ow_n;
+        const int ho = t % oh_n;
+        const int n = t / oh_n;
+        if (TR) {
+            b_base[i] = n * s.H * s.W * s.Cin + g * s.cin_g + ch * 8;
+            b_hb[i] = ok ? ho + ah.base : -(1 << 29);  // never inside the image
+            b_wb[i] = wo + aw.base;
+        } else if (IS1X1) {
             b_base[i] = pp * s.Cin + ch * 8;
             b_hb[i] = 0;
             b_wb[i] = 0;
@@ -137,7 +202,7 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(const bf16_t* __restric
         for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
 
     // Load cursor: the next K-step to fetch, tap (kh, kw) outer, channel chunk
-    // inner.
+    // inner (for a transposed phase, lkh and lkw count that phase's taps).
     int ltap = 0, lkh = 0, lkw = 0, lc0 = 0;
 
     // global -> registers for the cursor's K-step, then advance the cursor;
@@ -145,17 +210,19 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(const bf16_t* __restric
 #define IGEMM_LOAD_STEP(RA, RB)                                                             \
     do {                                                                                    \
         _Pragma("unroll") for (int i = 0; i < AV; ++i) {                                    \
-            const bool ok = lc0 + a_c[i] < s.cin_g && ltap < KK;                            \
-            RA[i] = load16(wr, ok ? a_off[i] + (ltap * s.cin_g + lc0) * 2 : kOOB);          \
+            const bool ok = lc0 + a_c[i] < s.cin_g && ltap < ntaps;                         \
+            const int wtap_ = TR ? (ah.k0 + lkh * ah.kstep) * s.Kw + aw.k0 + lkw * aw.kstep  \
+                                 : ltap;                                                    \
+            RA[i] = load16(wr, ok ? a_off[i] + (wtap_ * s.cin_g + lc0) * 2 : kOOB);         \
         }                                                                                   \
         _Pragma("unroll") for (int i = 0; i < BV; ++i) {                                    \
             int off;                                                                        \
-            bool ok = lc0 + b_c[i] < s.cin_g && ltap < KK;                                  \
+            bool ok = lc0 + b_c[i] < s.cin_g && ltap < ntaps;                               \
             if (IS1X1) {                                                                    \
                 off = b_base[i] + lc0;                                                      \
             } else {                                                                        \
-                const int hi = b_hb[i] + lkh * s.dil;                                       \
-                const int wi = b_wb[i] + lkw * s.dil;                                       \
+                const int hi = b_hb[i] + lkh * tap_dh;                                      \
+                const int wi = b_wb[i] + lkw * tap_dw;                                      \
                 ok = ok && (unsigned)hi < (unsigned)s.H && (unsigned)wi < (unsigned)s.W;    \
                 off = b_base[i] + (hi * s.W + wi) * s.Cin + lc0;                            \
             }                                                                               \
@@ -165,7 +232,7 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(const bf16_t* __restric
         if (lc0 >= s.cin_g) {                                                               \
             lc0 = 0;                                                                        \
             ++ltap;                                                                         \
-            if (++lkw == s.Kw) { lkw = 0; ++lkh; }                                          \
+            if (++lkw == ntw) { lkw = 0; ++lkh; }                                           \
         }                                                                                   \
     } while (0)
 
@@ -283,7 +350,13 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(const bf16_t* __restric
         const int co = co_tile + c * 8;
         if (p >= npix || co >= s.cout_g) continue;
         const uint4 v = *reinterpret_cast<const uint4*>(ep + row * ERS + c * 16);
-        bf16_t* dst = y + (size_t)p * s.Cout + g * s.cout_g + co;
+        int opix = p;  // output pixel (n, ho, wo) as one index
+        if (TR) {
+            const int uw = p % uw_n, t = p / uw_n;
+            const int uh = t % uh_n, n = t / uh_n;
+            opix = (n * s.Ho + ph_h + s.stride * uh) * s.Wo + ph_w + s.stride * uw;
+        }
+        bf16_t* dst = y + (size_t)opix * s.Cout + g * s.cout_g + co;
         if (vec16 && co + 8 <= s.cout_g) {
             *reinterpret_cast<uint4*>(dst) = v;
         } else {
@@ -293,38 +366,43 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(const bf16_t* __restric
     }
 }
 
-template <int BM, int BN, int WGM, int WGN, int BK, bool IS1X1>
+template <int BM, int BN, int WGM, int WGN, int BK, int MODE>
 hipError_t launch_cfg(const Shape& s, const bf16_t* x, const bf16_t* w, const float* b, bf16_t* y,
                       hipStream_t st) {
-    const int npix = s.N * s.Ho * s.Wo;
-    const int n_ptiles = (npix + BN - 1) / BN;
+    // a transposed convolution: pixel tiles of the largest phase (phase 0), per phase
+    const int S = s.stride;
+    const long long npix = MODE == kTransposed
+                               ? (long long)s.N * ((s.Ho + S - 1) / S) * ((s.Wo + S - 1) / S)
+                               : (long long)s.N * s.Ho * s.Wo;
+    const long long n_ptiles = (npix + BN - 1) / BN;
     const int n_ctiles = (s.cout_g + BM - 1) / BM;
-    const long long blocks = (long long)n_ptiles * n_ctiles * s.groups;
+    const long long blocks = n_ptiles * n_ctiles * s.groups * (MODE == kTransposed ? S * S : 1);
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     dim3 grid((unsigned)blocks);
+    const int npt = (int)n_ptiles;
     const bool bias = s.epilogue & CONV2D_EPI_BIAS, relu = s.epilogue & CONV2D_EPI_RELU;
     if (bias && relu)
-        hipLaunchKernelGGL((igemm_kernel<BM, BN, WGM, WGN, BK, IS1X1, true, true>), grid, dim3(kThreads), 0, st, x, w, b, y, s, n_ptiles, n_ctiles);
+        hipLaunchKernelGGL((igemm_kernel<BM, BN, WGM, WGN, BK, MODE, true, true>), grid, dim3(kThreads), 0, st, x, w, b, y, s, npt, n_ctiles);
     else if (bias)
-        hipLaunchKernelGGL((igemm_kernel<BM, BN, WGM, WGN, BK, IS1X1, true, false>), grid, dim3(kThreads), 0, st, x, w, b, y, s, n_ptiles, n_ctiles);
+        hipLaunchKernelGGL((igemm_kernel<BM, BN, WGM, WGN, BK, MODE, true, false>), grid, dim3(kThreads), 0, st, x, w, b, y, s, npt, n_ctiles);
     else if (relu)
-        hipLaunchKernelGGL((igemm_kernel<BM, BN, WGM, WGN, BK, IS1X1, false, true>), grid, dim3(kThreads), 0, st, x, w, b, y, s, n_ptiles, n_ctiles);
+        hipLaunchKernelGGL((igemm_kernel<BM, BN, WGM, WGN, BK, MODE, false, true>), grid, dim3(kThreads), 0, st, x, w, b, y, s, npt, n_ctiles);
     else
-        hipLaunchKernelGGL((igemm_kernel<BM, BN, WGM, WGN, BK, IS1X1, false, false>), grid, dim3(kThreads), 0, st, x, w, b, y, s, n_ptiles, n_ctiles);
+        hipLaunchKernelGGL((igemm_kernel<BM, BN, WGM, WGN, BK, MODE, false, false>), grid, dim3(kThreads), 0, st, x, w, b, y, s, npt, n_ctiles);
     return hipGetLastError();
 }
 
-template <bool IS1X1>
+template <int MODE>
 hipError_t launch_any(const Shape& s, const void* x, const void* w, const float* b, void* y, hipStream_t st) {
     const bf16_t* xt = static_cast<const bf16_t*>(x);
     const bf16_t* wt = static_cast<const bf16_t*>(w);
     bf16_t* yt = static_cast<bf16_t*>(y);
     // Tile shape by output channels per group: cover them in as few tiles as
     // possible so each input pixel is fetched once per tap for all of them.
-    if (s.cout_g > 128) return launch_cfg<IGEMM_TILE_M256, IS1X1>(s, xt, wt, b, yt, st);
-    if (s.cout_g > 64) return launch_cfg<IGEMM_TILE_M128, IS1X1>(s, xt, wt, b, yt, st);
-    if (s.cout_g > 32) return launch_cfg<IGEMM_TILE_M64, IS1X1>(s, xt, wt, b, yt, st);
-    return launch_cfg<IGEMM_TILE_M32, IS1X1>(s, xt, wt, b, yt, st);
+    if (s.cout_g > 128) return launch_cfg<IGEMM_TILE_M256, MODE>(s, xt, wt, b, yt, st);
+    if (s.cout_g > 64) return launch_cfg<IGEMM_TILE_M128, MODE>(s, xt, wt, b, yt, st);
+    if (s.cout_g > 32) return launch_cfg<IGEMM_TILE_M64, MODE>(s, xt, wt, b, yt, st);
+    return launch_cfg<IGEMM_TILE_M32, MODE>(s, xt, wt, b, yt, st);
 }
 
 bool mfma_channels_ok(const Shape& s) {
@@ -343,13 +421,21 @@ bool gemm1x1_supports(const Shape& s) {
 hipError_t launch_igemm(const Shape& s, const void* x, const void* w_packed, const float* bias,
                         void* y, hipStream_t st) {
     (void)hipGetLastError();  // report only this launch's error
-    return launch_any<false>(s, x, w_packed, bias, y, st);
+    return launch_any<kConv>(s, x, w_packed, bias, y, st);
 }
 
 hipError_t launch_gemm1x1(const Shape& s, const void* x, const void* w_packed, const float* bias,
                           void* y, hipStream_t st) {
     (void)hipGetLastError();  // report only this launch's error
-    return launch_any<true>(s, x, w_packed, bias, y, st);
+    return launch_any<kGemm1x1>(s, x, w_packed, bias, y, st);
+}
+
+bool igemm_transposed_supports(const Shape& s) { return mfma_channels_ok(s); }
+
+hipError_t launch_igemm_transposed(const Shape& s, const void* x, const void* w_packed, const float* bias,
+                                   void* y, hipStream_t st) {
+    (void)hipGetLastError();  // report only this launch's error
+    return launch_any<kTransposed>(s, x, w_packed, bias, y, st);
 }
 
 }  // namespace conv2d

@@ -170,6 +170,71 @@ int conv2d_fwd_separable_nhwc(const void* x, const void* w_dw, const float* bias
                               int dtype, int dw_epilogue, int pw_epilogue, hipStream_t stream);
 
 /*
+ * Transposed convolution (lpnh.cn sections 2.3 and 4.2: upsampling; the
+ * stride-1 convolution of the input with S-1 zeros inserted between
+ * neighbouring pixels; in matrix form Y = W^T X, the transpose of the
+ * standard convolution's matrix).  Every input pixel's products with the
+ * whole filter are added into the output window it spans:
+ *   Y[n, co, ih*S - P + kh*D, iw*S - P + kw*D] += X[n, ci, ih, iw] * W[ci, co', kh, kw]
+ *   ci in group g = co / (Cout/G), co' = co - g*Cout/G; sums that land
+ *   outside the output are dropped; then epi (bias, ReLU) as above.
+ *   Ho = (H-1)*S - 2P + D*(Kh-1) + OP + 1, likewise Wo, with the output
+ *   padding OP (extra rows/columns at the far edge) 0 <= OP < max(S, D).
+ *
+ * conv2d_transpose_fwd -- the pages' layouts:
+ *   x    [N][Cin][H][W]         (NCHW)
+ *   w    [Cin][Cout/G][Kh][Kw]  (the standard weight's shapes reversed)
+ *   bias fp32 [Cout], required iff epilogue has CONV2D_EPI_BIAS
+ *   y    [N][Cout][Ho][Wo]      (NCHW), written completely
+ * fp32 runs the direct kernel on these layouts; bf16 repacks x and w, runs
+ * the chosen kernel and repacks y, in the same per-device scratch as
+ * conv2d_fwd (so it may allocate and block; calls on one device share it).
+ *
+ * conv2d_transpose_fwd_nhwc_packed -- channels-last, allocates nothing:
+ *   x        [N][H][W][Cin]     (NHWC)
+ *   w_packed conv2d_transpose_pack_weights of w: [Cout][Kh][Kw][Cin/G]
+ *   y        [N][Ho][Wo][Cout]  (NHWC)
+ *
+ * Paths: CONV2D_PATH_IGEMM_GATHER (bf16, Cin/G % 8 == 0, Cout/G % 4 == 0)
+ * splits the output into its S x S phases (rows and columns of one residue
+ * mod S); each phase is an implicit GEMM on MFMA over only the taps that
+ * reach it.  CONV2D_PATH_DIRECT serves every other shape and dtype.
+ * conv2d_set_path_override applies (CONV2D_PATH_IGEMM means the phase GEMM;
+ * any other forced path returns CONV2D_ERR_UNSUPPORTED).  Alignment, stream
+ * and error behaviour as for conv2d_fwd / conv2d_fwd_nhwc_packed; an output
+ * padding out of range returns CONV2D_ERR_ARG.
+ */
+int conv2d_transpose_fwd(const void* x, const void* w, const float* bias, void* y,
+                         int N, int Cin, int H, int W, int Cout, int Kh, int Kw,
+                         int stride, int pad, int output_padding, int dilation, int groups,
+                         int dtype, int epilogue, hipStream_t stream);
+int conv2d_transpose_fwd_nhwc_packed(const void* x, const void* w_packed, const float* bias, void* y,
+                                     int N, int Cin, int H, int W, int Cout, int Kh, int Kw,
+                                     int stride, int pad, int output_padding, int dilation, int groups,
+                                     int dtype, int epilogue, hipStream_t stream);
+
+/* [Cin][Cout/G][Kh][Kw] -> [Cout][Kh][Kw][Cin/G] (the packed layout below;
+ * conv2d_packed_weight_bytes(Cout, Cin, Kh, Kw, groups, dtype) bytes).
+ * Enqueued on the stream; w and w_packed must not overlap. */
+int conv2d_transpose_pack_weights(const void* w, void* w_packed, int Cin, int Cout, int Kh, int Kw,
+                                  int groups, int dtype, hipStream_t stream);
+
+/* (in-1)*stride - 2*pad + dilation*(k-1) + output_padding + 1, or a value
+ * <= 0 when that is empty; CONV2D_ERR_ARG for a stride/dilation/k/pad out of
+ * range or output_padding outside [0, max(stride, dilation)).  Host only. */
+int conv2d_transpose_out_dim(int in, int k, int stride, int pad, int dilation, int output_padding);
+
+/* Host-only: the code a transposed call with these arguments would return
+ * (CONV2D_OK if valid), and the path it would run. */
+int conv2d_transpose_check_args(const void* x, const void* w, const float* bias, const void* y,
+                                int N, int Cin, int H, int W, int Cout, int Kh, int Kw,
+                                int stride, int pad, int output_padding, int dilation, int groups,
+                                int dtype, int epilogue);
+int conv2d_transpose_select_path(int N, int Cin, int H, int W, int Cout, int Kh, int Kw,
+                                 int stride, int pad, int output_padding, int dilation, int groups,
+                                 int dtype);
+
+/*
  * Packed weight layout (the reduction order the NHWC kernels walk: tap
  * (kh, kw) outer, input channel inner; the row/column order of W_matrix,
  * lincklin.cn section 7, with K ordered to match channels-last input):

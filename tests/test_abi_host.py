@@ -185,3 +185,78 @@ def test_path_selection_fallbacks_and_override():
     finally:
         c2.conv2d_set_path_override(c2.PATH_AUTO)
     assert c2.lib.conv2d_set_path_override(9) == c2.ERR_ARG
+
+
+# ------------------------------------------------------------------ transposed convolution
+
+def test_transpose_out_dim_agrees_with_oracle():
+    for H in (1, 2, 5, 28, 56):
+        for K in (1, 2, 3, 4, 5):
+            for S in (1, 2, 3):
+                for P in (0, 1, 2, 3):
+                    for D in (1, 2):
+                        for OP in range(max(S, D)):
+                            want = oracle.transpose_out_dim(H, K, S, P, D, OP)
+                            got = c2.conv2d_transpose_out_dim(H, K, S, P, D, OP)
+                            assert got == max(want, 0), (H, K, S, P, D, OP)
+    assert c2.conv2d_transpose_out_dim(5, 3, 2, 1, 1, 2) == c2.ERR_ARG   # OP >= max(S, D)
+    assert c2.conv2d_transpose_out_dim(5, 3, 0, 1, 1, 0) == c2.ERR_ARG
+    assert c2.conv2d_transpose_out_dim(5, 3, 2, -1, 1, 0) == c2.ERR_ARG
+
+
+TGOOD = dict(x=P, w=P, bias=P, y=P, N=2, Cin=16, H=7, W=9, Cout=24, Kh=4, Kw=4, stride=2, pad=1,
+             output_padding=0, dilation=1, groups=2, dtype=c2.BF16, epilogue=3)
+
+
+@pytest.mark.parametrize("over,code", [
+    ({}, c2.OK),
+    ({"dtype": 5}, c2.ERR_DTYPE),
+    ({"epilogue": 4}, c2.ERR_EPILOGUE),
+    ({"N": 0}, c2.ERR_ARG),
+    ({"Kh": 0}, c2.ERR_ARG),
+    ({"stride": 0}, c2.ERR_ARG),
+    ({"pad": -1}, c2.ERR_ARG),
+    ({"output_padding": 2}, c2.ERR_ARG),
+    ({"output_padding": -1}, c2.ERR_ARG),
+    ({"output_padding": 1, "stride": 1, "dilation": 2}, c2.OK),
+    ({"groups": 5}, c2.ERR_GROUPS),
+    ({"x": None}, c2.ERR_NULL),
+    ({"bias": None}, c2.ERR_NULL),
+    ({"bias": None, "epilogue": 2}, c2.OK),
+    ({"H": 1, "W": 1, "Kh": 1, "Kw": 1, "pad": 1}, c2.ERR_EMPTY_OUTPUT),
+    ({"N": 4096, "Cin": 1024, "H": 64, "W": 64}, c2.ERR_UNSUPPORTED),
+])
+def test_transpose_check_args_codes(over, code):
+    a = dict(TGOOD, **over)
+    assert c2.conv2d_transpose_check_args(**a) == code
+
+
+def test_transpose_entries_reject_bad_args_before_any_gpu_work():
+    for fn in (c2.lib.conv2d_transpose_fwd, c2.lib.conv2d_transpose_fwd_nhwc_packed):
+        assert fn(P, P, P, P, 1, 8, 9, 9, 16, 3, 3, 2, 1, 2, 1, 1, c2.BF16, 0, None) == c2.ERR_ARG
+        assert fn(None, P, P, P, 1, 8, 9, 9, 16, 3, 3, 2, 1, 0, 1, 1, c2.BF16, 0, None) == c2.ERR_NULL
+        assert fn(P, P, P, P, 1, 8, 9, 9, 16, 3, 3, 2, 1, 0, 1, 3, c2.BF16, 0, None) == c2.ERR_GROUPS
+    lib = c2.lib
+    assert lib.conv2d_transpose_pack_weights(P, P, 16, 8, 3, 3, 3, c2.BF16, None) == c2.ERR_GROUPS
+    assert lib.conv2d_transpose_pack_weights(None, P, 16, 8, 3, 3, 1, c2.BF16, None) == c2.ERR_NULL
+    assert lib.conv2d_transpose_pack_weights(P, P, 16, 8, 3, 3, 1, 9, None) == c2.ERR_DTYPE
+
+
+def test_transpose_path_selection():
+    sel = c2.conv2d_transpose_select_path
+    for li in range(2):
+        ly = ci.layer(6, li)
+        assert sel(ly.N, ly.Cin, ly.H, ly.W, ly.Cout, ly.Kh, ly.Kw, ly.stride, ly.pad, ly.out_pad, ly.dilation,
+                   ly.groups, c2.BF16) == c2.PATH_IGEMM_GATHER
+    assert sel(1, 12, 8, 8, 16, 4, 4, 2, 1, 0, 1, 1, c2.BF16) == c2.PATH_DIRECT   # Cin % 8 != 0
+    assert sel(1, 16, 8, 8, 16, 4, 4, 2, 1, 0, 1, 1, c2.F32) == c2.PATH_DIRECT
+    prev = c2.conv2d_set_path_override(c2.PATH_DEPTHWISE)
+    try:
+        with pytest.raises(c2.Conv2dError):
+            sel(1, 16, 8, 8, 16, 4, 4, 2, 1, 0, 1, 1, c2.BF16)
+        c2.conv2d_set_path_override(c2.PATH_DIRECT)
+        assert sel(1, 16, 8, 8, 16, 4, 4, 2, 1, 0, 1, 1, c2.BF16) == c2.PATH_DIRECT
+        c2.conv2d_set_path_override(c2.PATH_IGEMM)
+        assert sel(1, 16, 8, 8, 16, 4, 4, 2, 1, 0, 1, 1, c2.BF16) == c2.PATH_IGEMM_GATHER
+    finally:
+        c2.conv2d_set_path_override(prev)
