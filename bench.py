@@ -58,7 +58,8 @@ METRIC = "conv2d fwd TFLOP/s (GB/s for depthwise) and % of MI355X roofline, 1 GP
 KERNEL_SOURCES = {"direct": ["direct.hip"], "depthwise": ["depthwise.hip", "dwrow.hpp"],
                   "gemm1x1": ["pointwise.hip", "igemm.hip"], "igemm_gather": ["igemm.hip"],
                   "igemm_halo": ["igemm_halo.hip"], "separable": ["separable.hip", "dwrow.hpp"],
-                  "transposed_igemm_gather": ["igemm.hip"], "transposed_direct": ["transposed.hip"]}
+                  "transposed_igemm_gather": ["igemm.hip"], "transposed_direct": ["transposed.hip"],
+                  "winograd": ["winograd.hip"]}
 
 
 def out_hw(ly):
@@ -168,7 +169,7 @@ def cpu_baseline(cid, li, x, w, b, target_s, unit):
             "host_cpu": host_cpu()}
 
 
-def bench_layer(cid, li, steps, warmup, cpu_seconds, with_cpu):
+def bench_layer(cid, li, steps, warmup, cpu_seconds, with_cpu, winograd=False):
     import torch
     import cnn_convolution_conv2d_amd as c2
 
@@ -177,7 +178,9 @@ def bench_layer(cid, li, steps, warmup, cpu_seconds, with_cpu):
     dt_lib = c2.F32 if ly.dtype == ci.F32 else c2.BF16
     tdt = torch.float32 if ly.dtype == ci.F32 else torch.bfloat16
     esz = 4 if ly.dtype == ci.F32 else 2
-    if ly.transposed:
+    if winograd:
+        path, pname = None, "winograd"
+    elif ly.transposed:
         path = c2.conv2d_transpose_select_path(ly.N, ly.Cin, ly.H, ly.W, ly.Cout, ly.Kh, ly.Kw, ly.stride,
                                                ly.pad, ly.out_pad, ly.dilation, ly.groups, dt_lib)
         pname = "transposed_" + c2.PATH_NAMES[path]
@@ -194,9 +197,12 @@ def bench_layer(cid, li, steps, warmup, cpu_seconds, with_cpu):
     # inputs resident in HBM, channels-last, before the timed region
     x_nchw = torch.from_numpy(x).to(dev).to(tdt)
     w_dev = torch.from_numpy(w).to(dev).to(tdt)
-    wp = torch.empty(c2.conv2d_packed_weight_bytes(ly.Cout, ly.Cin, ly.Kh, ly.Kw, ly.groups, dt_lib)
-                     // esz, dtype=tdt, device=dev)
-    if ly.transposed:
+    wbytes = c2.conv2d_winograd_weight_bytes(ly.Cout, ly.Cin, dt_lib) if winograd else \
+        c2.conv2d_packed_weight_bytes(ly.Cout, ly.Cin, ly.Kh, ly.Kw, ly.groups, dt_lib)
+    wp = torch.empty(wbytes // esz, dtype=tdt, device=dev)
+    if winograd:
+        c2.conv2d_winograd_transform_weights(w_dev, wp, ly.Cout, ly.Cin, dt_lib)
+    elif ly.transposed:
         c2.conv2d_transpose_pack_weights(w_dev, wp, ly.Cin, ly.Cout, ly.Kh, ly.Kw, ly.groups, dt_lib)
     else:
         c2.conv2d_pack_weights(w_dev, wp, ly.Cout, ly.Cin, ly.Kh, ly.Kw, ly.groups, dt_lib)
@@ -211,7 +217,10 @@ def bench_layer(cid, li, steps, warmup, cpu_seconds, with_cpu):
 
     def step(i):
         j = i % R
-        if ly.transposed:
+        if winograd:
+            c2.conv2d_fwd_winograd_nhwc(xs[j], wp, bias, ys[j], ly.N, ly.Cin, ly.H, ly.W, ly.Cout, ly.pad, dt_lib,
+                                        ly.epilogue, stream)
+        elif ly.transposed:
             c2.conv2d_transpose_fwd_nhwc_packed(xs[j], wp, bias, ys[j], ly.N, ly.Cin, ly.H, ly.W, ly.Cout,
                                                 ly.Kh, ly.Kw, ly.stride, ly.pad, ly.out_pad, ly.dilation,
                                                 ly.groups, dt_lib, ly.epilogue, stream)
@@ -246,7 +255,7 @@ def bench_layer(cid, li, steps, warmup, cpu_seconds, with_cpu):
         value = nbytes / (ms_per_step * 1e-3) / 1e9
         achieved = nbytes / (mean_ms * 1e-3) / 1e9
         peak = PEAK_HBM_GBS
-    key = f"cfg{cid}:{ly.name}"
+    key = f"cfg{cid}:{ly.name}" + (":winograd" if winograd else "")
     traffic = measured_traffic(key, pname)
     line = {
         "metric": METRIC,
@@ -267,7 +276,8 @@ def bench_layer(cid, li, steps, warmup, cpu_seconds, with_cpu):
                         f"{ly.Kh}x{ly.Kw} s{ly.stride} p{ly.pad} d{ly.dilation} g{ly.groups}"
                         f"{' bias' if ly.epilogue & ci.EPI_BIAS else ''}"
                         f"{' relu' if ly.epilogue & ci.EPI_RELU else ''}",
-            "layout": "NHWC activations, packed weights", "path": pname,
+            "layout": "NHWC activations, " + ("Winograd-transformed weights" if winograd else "packed weights"),
+            "path": pname,
             "gflop_per_step": round(flops / 1e9, 4), "algorithmic_mb_per_step": round(nbytes / 1e6, 3),
             "rotating_buffer_sets": R, "device": torch.cuda.get_device_name(dev),
         },
@@ -279,6 +289,11 @@ def bench_layer(cid, li, steps, warmup, cpu_seconds, with_cpu):
             "kernel_median_us": round(float(np.median(launch_ms)) * 1e3, 3),
         },
     }
+    if winograd:
+        # FLOP/s above count the convolution's own multiply-adds; the matrix
+        # cores execute 16/36 of them (F(2x2,3x3)) on the transformed data
+        line["config"]["mfma_gflop_per_step"] = round(flops * 16 / 36 / 1e9, 4)
+        line["config"]["flop_count"] = "direct convolution's 2*N*Ho*Wo*Cout*Cin*9"
     if with_cpu:
         line["cpu_baseline"] = cpu_baseline(cid, li, x, w, b, cpu_seconds, unit)
     return line
@@ -411,6 +426,8 @@ def main(argv=None):
     ap.add_argument("--all", action="store_true", help="time every workload layer and the fused pair")
     ap.add_argument("--separable", action="store_true",
                     help="time the fused depthwise-separable pair of config 3")
+    ap.add_argument("--winograd", action="store_true",
+                    help="time the 3x3 layer through the Winograd F(2x2,3x3) entry")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -441,6 +458,11 @@ def main(argv=None):
     b = _builder()
     if not os.path.exists(b.OUT):
         b.build()
+    if a.winograd and not a.all:
+        cid, li = (int(v) for v in a.layer.split(":"))
+        print(json.dumps(bench_layer(cid, li, a.steps, a.warmup, a.cpu_seconds, with_cpu=not a.no_cpu_baseline,
+                                     winograd=True)), flush=True)
+        return 0
     if a.separable and not a.all:
         print(json.dumps(bench_separable(a.steps, a.warmup, a.cpu_seconds,
                                          with_cpu=not a.no_cpu_baseline)), flush=True)
@@ -451,6 +473,9 @@ def main(argv=None):
         line = bench_layer(cid, li, a.steps, a.warmup, a.cpu_seconds,
                            with_cpu=not a.no_cpu_baseline)
         print(json.dumps(line), flush=True)
+        if a.all and cid == 2:
+            print(json.dumps(bench_layer(cid, li, a.steps, a.warmup, a.cpu_seconds,
+                                         with_cpu=not a.no_cpu_baseline, winograd=True)), flush=True)
         if a.all and cid == 3 and li == len(ci.WORKLOADS[3].layers) - 1:
             print(json.dumps(bench_separable(a.steps, a.warmup, a.cpu_seconds,
                                              with_cpu=not a.no_cpu_baseline)), flush=True)

@@ -31,6 +31,7 @@ ERR_NULL, ERR_DTYPE, ERR_EPILOGUE, ERR_ALIGN = -6, -7, -8, -9
 # Every symbol include/conv2d.h declares.
 EXPORTS = ("conv2d_fwd", "conv2d_fwd_nhwc_packed", "conv2d_fwd_bn", "conv2d_fwd_nhwc_packed_bn",
            "conv2d_fwd_separable_nhwc",
+           "conv2d_winograd_weight_bytes", "conv2d_winograd_transform_weights", "conv2d_fwd_winograd_nhwc",
            "conv2d_transpose_fwd", "conv2d_transpose_fwd_nhwc_packed", "conv2d_transpose_pack_weights",
            "conv2d_transpose_out_dim", "conv2d_transpose_check_args", "conv2d_transpose_select_path",
            "conv2d_packed_weight_bytes",
@@ -64,6 +65,12 @@ def _load() -> ctypes.CDLL:
         f.argtypes, f.restype = [P] * 6 + [I] * 13 + [P], I
     lib.conv2d_fwd_separable_nhwc.argtypes = [P] * 6 + [I] * 10 + [P]
     lib.conv2d_fwd_separable_nhwc.restype = I
+    lib.conv2d_winograd_weight_bytes.argtypes = [I] * 3
+    lib.conv2d_winograd_weight_bytes.restype = ctypes.c_size_t
+    lib.conv2d_winograd_transform_weights.argtypes = [P, P] + [I] * 3 + [P]
+    lib.conv2d_winograd_transform_weights.restype = I
+    lib.conv2d_fwd_winograd_nhwc.argtypes = [P] * 4 + [I] * 8 + [P]
+    lib.conv2d_fwd_winograd_nhwc.restype = I
     for name in ("conv2d_transpose_fwd", "conv2d_transpose_fwd_nhwc_packed"):
         f = getattr(lib, name)
         f.argtypes, f.restype = [P] * 4 + [I] * 14 + [P], I
@@ -166,6 +173,22 @@ def conv2d_fwd_separable_nhwc(x, w_dw, bias_dw, w_pw, bias_pw, y, N, C, H, W, Co
                                          _ptr(y), N, C, H, W, Cout, stride, pad, dtype, dw_epilogue,
                                          pw_epilogue, _stream(stream)),
            "conv2d_fwd_separable_nhwc")
+
+
+def conv2d_winograd_weight_bytes(Cout, Cin, dtype) -> int:
+    return int(lib.conv2d_winograd_weight_bytes(Cout, Cin, dtype))
+
+
+def conv2d_winograd_transform_weights(w, w_wino, Cout, Cin, dtype, stream=None) -> None:
+    """[Cout][Cin][3][3] bf16 -> G g G^T as [16][Cin/8][Cout][8] bf16."""
+    _check(lib.conv2d_winograd_transform_weights(_ptr(w), _ptr(w_wino), Cout, Cin, dtype, _stream(stream)),
+           "conv2d_winograd_transform_weights")
+
+
+def conv2d_fwd_winograd_nhwc(x, w_wino, bias, y, N, Cin, H, W, Cout, pad, dtype, epilogue, stream=None) -> None:
+    """3x3 stride-1 convolution by Winograd F(2x2,3x3): NHWC x, transformed w, NHWC y."""
+    _check(lib.conv2d_fwd_winograd_nhwc(_ptr(x), _ptr(w_wino), _ptr(bias), _ptr(y), N, Cin, H, W, Cout, pad, dtype,
+                                        epilogue, _stream(stream)), "conv2d_fwd_winograd_nhwc")
 
 
 def conv2d_transpose_fwd(x, w, bias, y, N, Cin, H, W, Cout, Kh, Kw, stride, pad, output_padding, dilation,

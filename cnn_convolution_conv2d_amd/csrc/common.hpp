@@ -138,6 +138,12 @@ bool igemm_transposed_supports(const Shape& s);
 hipError_t launch_tpack_weights(const void* w, void* wp, int Cin, int cout_g, int groups, int Kh, int Kw,
                                 int elem_bytes, hipStream_t st);
 
+// Winograd F(2x2, 3x3) (bf16, 3x3, stride 1, dilation 1, groups 1).
+bool winograd_supports(const Shape& s);
+hipError_t launch_winograd(const Shape& s, const void* x, const void* w_wino, const float* bias, void* y,
+                           hipStream_t st);
+hipError_t launch_winograd_weights(const void* w, void* w_wino, int Cout, int Cin, hipStream_t st);
+
 hipError_t launch_transpose(const void* src, void* dst, int batch, int rows, int cols,
                             int elem_bytes, hipStream_t st);
 hipError_t launch_pack_weights(const void* w, void* wp, int Cout, int cin_g, int Kh, int Kw,

@@ -466,6 +466,37 @@ int conv2d_fwd_separable_nhwc(const void* x, const void* w_dw, const float* bias
     return e == hipSuccess ? CONV2D_OK : hip_fail(e, "separable launch");
 }
 
+size_t conv2d_winograd_weight_bytes(int Cout, int Cin, int dtype) {
+    if (Cout < 1 || Cin < 1 || Cin % 8 || dtype != CONV2D_BF16) return 0;
+    if (16LL * Cout * Cin * 2 >= INT_MAX) return 0;
+    return (size_t)16 * Cout * Cin * 2;
+}
+
+int conv2d_winograd_transform_weights(const void* w, void* w_wino, int Cout, int Cin, int dtype, hipStream_t stream) {
+    if (dtype != CONV2D_F32 && dtype != CONV2D_BF16) return set_error(CONV2D_ERR_DTYPE, "unknown dtype %d", dtype);
+    if (Cout < 1 || Cin < 1) return set_error(CONV2D_ERR_ARG, "sizes must be >= 1");
+    if (!w || !w_wino) return set_error(CONV2D_ERR_NULL, "w and w_wino must be non-NULL");
+    if (dtype != CONV2D_BF16 || Cin % 8 || 16LL * Cout * Cin * 2 >= INT_MAX)
+        return set_error(CONV2D_ERR_UNSUPPORTED, "Winograd weights need bf16, Cin %% 8 == 0 (got Cin=%d)", Cin);
+    const hipError_t e = launch_winograd_weights(w, w_wino, Cout, Cin, stream);
+    return e == hipSuccess ? CONV2D_OK : hip_fail(e, "winograd weight transform launch");
+}
+
+int conv2d_fwd_winograd_nhwc(const void* x, const void* w_wino, const float* bias, void* y, int N, int Cin, int H,
+                             int W, int Cout, int pad, int dtype, int epilogue, hipStream_t stream) {
+    Shape s;
+    int rc = validate(x, w_wino, bias, y, N, Cin, H, W, Cout, 3, 3, 1, pad, 1, 1, dtype, epilogue, &s);
+    if (rc) return rc;
+    if (!winograd_supports(s))
+        return set_error(CONV2D_ERR_UNSUPPORTED,
+                         "Winograd F(2x2,3x3) needs bf16, Cin %% 8 == 0, Cout %% 4 == 0 and tensors below 2 GiB "
+                         "(got dtype %d Cin=%d Cout=%d)", dtype, Cin, Cout);
+    if (!(aligned16(x) && aligned16(w_wino) && aligned16(y)))
+        return set_error(CONV2D_ERR_ALIGN, "x, w_wino and y must be 16-byte aligned");
+    const hipError_t e = launch_winograd(s, x, w_wino, bias, y, stream);
+    return e == hipSuccess ? CONV2D_OK : hip_fail(e, "winograd launch");
+}
+
 int conv2d_transpose_out_dim(int in, int k, int stride, int pad, int dilation, int output_padding) {
     if (stride < 1 || dilation < 1 || k < 1 || pad < 0 || in < 1 || output_padding < 0 ||
         (output_padding >= stride && output_padding >= dilation))

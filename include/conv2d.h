@@ -170,6 +170,36 @@ int conv2d_fwd_separable_nhwc(const void* x, const void* w_dw, const float* bias
                               int dtype, int dw_epilogue, int pw_epilogue, hipStream_t stream);
 
 /*
+ * Winograd minimal filtering F(2x2, 3x3) (lpnh.cn section 3.3; lnrq.cn
+ * section 2.2): the same 3x3, stride-1 convolution as conv2d_fwd_nhwc_packed
+ * (dilation 1, groups 1, padding P, epilogue bias/ReLU), computed per 2x2
+ * output block as Y = A^T [ (G g G^T) (.) (B^T d B) ] A summed over input
+ * channels: 16 multiplications per block and channel pair instead of 36.
+ * Numerics: the transformed input B^T d B and the transformed filter
+ * G g G^T are each rounded to bf16 before the fp32-accumulated products, so
+ * the result is not the direct path's bit for bit; integer-valued data with
+ * small magnitudes stays exact.
+ *
+ * conv2d_winograd_transform_weights -- w [Cout][Cin][3][3] bf16 (the pages'
+ *   layout) -> w_wino [16][Cin/8][Cout][8] bf16 holding G g G^T (computed in
+ *   fp32, rounded to nearest even); conv2d_winograd_weight_bytes(Cout, Cin,
+ *   dtype) bytes (0 on bad arguments).  Needs bf16 and Cin % 8 == 0
+ *   (else CONV2D_ERR_UNSUPPORTED).  Enqueued on the stream.
+ * conv2d_fwd_winograd_nhwc -- x [N][H][W][Cin] bf16 (NHWC), w_wino from the
+ *   transform, bias fp32 [Cout] (iff CONV2D_EPI_BIAS), y [N][Ho][Wo][Cout]
+ *   bf16 with Ho = H + 2P - 2, Wo = W + 2P - 2.  Runs bf16 with Cin % 8 == 0
+ *   and Cout % 4 == 0; other valid calls return CONV2D_ERR_UNSUPPORTED.
+ *   x, w_wino and y 16-byte aligned.  Allocates nothing; errors as for
+ *   conv2d_fwd_nhwc_packed.
+ */
+size_t conv2d_winograd_weight_bytes(int Cout, int Cin, int dtype);
+int conv2d_winograd_transform_weights(const void* w, void* w_wino, int Cout, int Cin, int dtype,
+                                      hipStream_t stream);
+int conv2d_fwd_winograd_nhwc(const void* x, const void* w_wino, const float* bias, void* y,
+                             int N, int Cin, int H, int W, int Cout, int pad,
+                             int dtype, int epilogue, hipStream_t stream);
+
+/*
  * Transposed convolution (lpnh.cn sections 2.3 and 4.2: upsampling; the
  * stride-1 convolution of the input with S-1 zeros inserted between
  * neighbouring pixels; in matrix form Y = W^T X, the transpose of the

@@ -211,3 +211,24 @@ def run_tnchw(x_nchw, w, bias, stride, pad, out_pad, dil, groups, dtype, epilogu
                             lib_dtype(dtype), epilogue)
     torch.cuda.synchronize()
     return yd.float().cpu().numpy().astype(np.float64)
+
+
+def run_winograd(x_nchw, w, bias, pad, epilogue, return_dev=False):
+    """x (NCHW float32 values, bf16-exact), w [Cout][Cin][3][3] -> the
+    Winograd weight transform and conv2d_fwd_winograd_nhwc -> NCHW float64."""
+    import torch
+    import cnn_convolution_conv2d_amd as c2
+    N, Cin, H, W = x_nchw.shape
+    Cout = w.shape[0]
+    Ho, Wo = H + 2 * pad - 2, W + 2 * pad - 2
+    xd = to_dev(ci.nchw_to_nhwc(x_nchw), ci.BF16)
+    wd = to_dev(w, ci.BF16)
+    vw = torch.empty(c2.conv2d_winograd_weight_bytes(Cout, Cin, c2.BF16) // 2, dtype=torch.bfloat16, device="cuda")
+    c2.conv2d_winograd_transform_weights(wd, vw, Cout, Cin, c2.BF16)
+    bd = None if bias is None else torch.from_numpy(np.asarray(bias, np.float32)).cuda()
+    yd = torch.full((N, Ho, Wo, Cout), float("nan"), dtype=torch.bfloat16, device="cuda")
+    c2.conv2d_fwd_winograd_nhwc(xd, vw, bd, yd, N, Cin, H, W, Cout, pad, c2.BF16, epilogue)
+    torch.cuda.synchronize()
+    if return_dev:
+        return yd
+    return ci.nhwc_to_nchw(yd.float().cpu().numpy()).astype(np.float64)

@@ -260,3 +260,28 @@ def test_transpose_path_selection():
         assert sel(1, 16, 8, 8, 16, 4, 4, 2, 1, 0, 1, 1, c2.BF16) == c2.PATH_IGEMM_GATHER
     finally:
         c2.conv2d_set_path_override(prev)
+
+
+# ------------------------------------------------------------------ Winograd
+
+def test_winograd_entries_reject_bad_args_before_any_gpu_work():
+    assert c2.conv2d_winograd_weight_bytes(256, 128, c2.BF16) == 16 * 256 * 128 * 2
+    assert c2.conv2d_winograd_weight_bytes(256, 12, c2.BF16) == 0
+    assert c2.conv2d_winograd_weight_bytes(256, 128, c2.F32) == 0
+    f = c2.lib.conv2d_fwd_winograd_nhwc
+    assert f(None, P, P, P, 1, 16, 8, 8, 16, 1, c2.BF16, 0, None) == c2.ERR_NULL
+    assert f(P, P, None, P, 1, 16, 8, 8, 16, 1, c2.BF16, 1, None) == c2.ERR_NULL
+    assert f(P, P, P, P, 1, 16, 8, 8, 16, -1, c2.BF16, 0, None) == c2.ERR_ARG
+    assert f(P, P, P, P, 0, 16, 8, 8, 16, 1, c2.BF16, 0, None) == c2.ERR_ARG
+    assert f(P, P, P, P, 1, 16, 2, 2, 16, 0, c2.BF16, 0, None) == c2.ERR_EMPTY_OUTPUT
+    assert f(P, P, P, P, 1, 16, 8, 8, 16, 1, c2.F32, 0, None) == c2.ERR_UNSUPPORTED
+    assert f(P, P, P, P, 1, 12, 8, 8, 16, 1, c2.BF16, 0, None) == c2.ERR_UNSUPPORTED
+    assert f(P, P, P, P, 1, 16, 8, 8, 18, 1, c2.BF16, 0, None) == c2.ERR_UNSUPPORTED
+    assert f(P, P, P, P, 1, 16, 8, 8, 16, 1, 7, 0, None) == c2.ERR_DTYPE
+    assert f(P, P, P, P, 1, 16, 8, 8, 16, 1, c2.BF16, 8, None) == c2.ERR_EPILOGUE
+    assert f(P + 2, P, P, P, 1, 16, 8, 8, 16, 1, c2.BF16, 0, None) == c2.ERR_ALIGN
+    t = c2.lib.conv2d_winograd_transform_weights
+    assert t(None, P, 16, 16, c2.BF16, None) == c2.ERR_NULL
+    assert t(P, P, 16, 12, c2.BF16, None) == c2.ERR_UNSUPPORTED
+    assert t(P, P, 16, 16, c2.F32, None) == c2.ERR_UNSUPPORTED
+    assert t(P, P, 0, 16, c2.BF16, None) == c2.ERR_ARG
