@@ -16,17 +16,20 @@
 // bf16 (the only roundings besides the final one).
 //
 // Workgroup: 8x8 output blocks (16x16 outputs) of one image x 64 output
-// channels; 4 waves, wave w owns output channels 32*(w/2).. and block rows
-// 4*(w%2).. of the 8x8, i.e. one 32x32 MFMA tile for each of the 16 xi (256
-// fp32 accumulators per lane).  Input channels are walked in chunks of 16:
-//   - V of the chunk ([16 xi][2 halves][64 co][8 c] bf16, 32 KB) and the
-//     18x18 input patch ([18][18][2 halves][8 c], 10 KB) are copied into LDS
-//     with buffer-to-LDS loads, double-buffered: the next chunk's copies are
-//     in flight while this one computes;
+// channels; 4 waves, wave w owns block rows 2w, 2w+1 (16 blocks) and all 64
+// output channels: for each of the 16 xi, four 16x16 MFMA tiles (16 output
+// channels x 16 blocks; 256 fp32 accumulators per lane).  Input channels are
+// walked in chunks of 32:
+//   - V of the chunk ([16 xi][4 quarters][64 co][8 c] bf16, 64 KB) is copied
+//     into LDS with buffer-to-LDS loads, double-buffered (the next chunk's
+//     copy is in flight during this chunk); the 18x18 input patch of the
+//     chunk ([18][18][4 quarters + 1 pad][8 c], 26 KB) is single-buffered:
+//     its next copy starts once every wave has transformed this one;
 //   - each lane transforms the 4x4 patch of its own block for its 8 channels
-//     in registers (B^T d B, fp32 adds, one bf16 rounding) -- exactly the MFMA
-//     B operand of that lane for each xi, so U never goes through memory;
-//   - 16 MFMAs, one per xi.
+//     in registers (B^T d B, fp32 adds, one bf16 rounding) -- exactly that
+//     lane's MFMA B operand for each xi, so U never goes through memory, and
+//     every block is transformed once per workgroup;
+//   - 64 MFMAs v_mfma_f32_16x16x32_bf16 (16 xi x 4 channel tiles).
 // After the last chunk every lane holds all 16 M_xi of its (channel, block)
 // pairs, so the output transform A^T M A, bias, ReLU and the bf16 rounding
 // happen in registers before one store per output.
@@ -38,54 +41,69 @@ namespace conv2d {
 namespace {
 
 constexpr int kWThreads = 256;
-constexpr int kWBlk = 8;                          // output blocks per workgroup side
-constexpr int kWCo = 64;                          // output channels per workgroup
-constexpr int kWPatch = 2 * kWBlk + 2;            // input patch side: 18
-constexpr int kWXSlots = kWPatch * kWPatch * 2;   // 16-byte units of one patch chunk: 648
-constexpr int kWXPad = (kWXSlots + 63) / 64 * 64; // whole waves of units: 704
-constexpr int kWVSlots = 16 * 2 * kWCo;           // 16-byte units of one V chunk: 2048
-constexpr int kWBuf = kWVSlots + kWXPad;          // units per buffer
-constexpr int kWLds = 2 * kWBuf * 16;             // bytes of dynamic LDS: 88064
+constexpr int kWBlk = 8;                            // output blocks per workgroup side
+constexpr int kWCo = 64;                            // output channels per workgroup
+constexpr int kWPatch = 2 * kWBlk + 2;              // input patch side: 18
+constexpr int kWPix = 5;                            // 16-byte units per patch pixel: 4 quarters + 1 pad
+constexpr int kWXUnits = kWPatch * kWPatch * kWPix; // 1620
+constexpr int kWXPad = (kWXUnits + 63) / 64 * 64;   // whole waves of units: 1664
+constexpr int kWVUnits = 16 * 4 * kWCo;             // 16-byte units of one V chunk: 4096
+constexpr int kWLds = (2 * kWVUnits + kWXPad) * 16; // bytes of dynamic LDS: 157696
 
 struct WinoGrid {
     int N, Cin, H, W, Cout, pad, Ho, Wo;
     int C8;            // Cin / 8
     int nbr, nbc;      // 8x8-block groups per image (rows, columns)
     int ncb;           // 64-channel output groups
-    int nchunk;        // 16-channel input chunks
+    int nchunk;        // 32-channel input chunks
     int bias, relu;
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// Copy chunk kc (input channels 16*kc ..) of V and of the input patch into
-// one LDS buffer.  V: unit (xi, half, co) -> one wave instruction per (xi,
-// half), lane = output channel.  Patch: unit ((row*18 + col)*2 + half) ->
-// eleven wave instructions of 64 consecutive units.  Units past the tensor
-// (output channels >= Cout, channels >= Cin, pixels outside the image) read 0.
-__device__ __forceinline__ void wino_stage(uint4* __restrict__ vdst, uint4* __restrict__ xdst, const WinoGrid& g,
-                                           __amdgpu_buffer_rsrc_t vr, __amdgpu_buffer_rsrc_t xr, int kc, int co0,
-                                           int n, int ih0, int iw0, int wave, int lane) {
+// This wave's LDS operations complete, then the workgroup barrier; buffer
+// loads in flight (copies into the other buffers) are not waited for.
+__device__ __forceinline__ void lds_barrier() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt at their maxima (no wait)
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Copy V of chunk kc (input channels 32*kc ..) into vdst: unit (xi, quarter,
+// co), one wave instruction per (xi, quarter) with lane = output channel.
+// Output channels >= Cout and channels >= Cin read 0.
+__device__ __forceinline__ void wino_stage_v(uint4* __restrict__ vdst, const WinoGrid& g, __amdgpu_buffer_rsrc_t vr,
+                                             int kc, int co0, int wave, int lane) {
     const int co = co0 + lane;
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-        const int i = wave + 4 * m;             // (xi, half) pair
-        const int xi = i >> 1, half = i & 1;
-        const int cg = 2 * kc + half;           // 8-channel group of the whole input
+    for (int m = 0; m < 16; ++m) {
+        const int i = wave + 4 * m;   // (xi, quarter)
+        const int xi = i >> 2, qt = i & 3;
+        const int cg = 4 * kc + qt;   // 8-channel group of the whole input
         const bool ok = co < g.Cout && cg < g.C8;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_ptr_t)(vdst + i * 64),
-                                                 16, ok ? ((xi * g.C8 + cg) * g.Cout + co) * 16 : kOOB, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_ptr_t)(vdst + i * 64), 16,
+                                                 ok ? ((xi * g.C8 + cg) * g.Cout + co) * 16 : kOOB, 0, 0, 0);
     }
+}
+
+// Copy the input patch of chunk kc into xdst: unit pixel*5 + quarter (the
+// fifth unit of a pixel is padding, so that neighbouring blocks' reads fall
+// in different banks).  Pixels outside the image, channels >= Cin and the
+// padding units read 0.
+__device__ __forceinline__ void wino_stage_x(uint4* __restrict__ xdst, const WinoGrid& g, __amdgpu_buffer_rsrc_t xr,
+                                             int kc, int n, int ih0, int iw0, int wave, int lane) {
 #pragma unroll
-    for (int m = 0; m < 3; ++m) {
+    for (int m = 0; m < (kWXPad / 64 + 3) / 4; ++m) {
         const int k = wave + 4 * m;
         if (k * 64 >= kWXPad) break;
         const int s = k * 64 + lane;
-        const int p = s >> 1, half = s & 1;
+        const int p = s / kWPix, qt = s - p * kWPix;
         const int row = p / kWPatch, col = p - row * kWPatch;
         const int ih = ih0 + row, iw = iw0 + col;
-        const int cg = 2 * kc + half;
-        const bool ok = s < kWXSlots && (unsigned)ih < (unsigned)g.H && (unsigned)iw < (unsigned)g.W && cg < g.C8;
+        const int cg = 4 * kc + qt;
+        const bool ok = qt < 4 && p < kWPatch * kWPatch && (unsigned)ih < (unsigned)g.H &&
+                        (unsigned)iw < (unsigned)g.W && cg < g.C8;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)(xdst + k * 64), 16,
                                                  ok ? (((n * g.H + ih) * g.W + iw) * g.C8 + cg) * 16 : kOOB, 0, 0, 0);
     }
@@ -94,72 +112,89 @@ __device__ __forceinline__ void wino_stage(uint4* __restrict__ vdst, uint4* __re
 __device__ __forceinline__ float blo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bhi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 
-// 8 bf16 (one 16-byte unit) -> 8 fp32
-__device__ __forceinline__ void unpack8(const uint4& v, float f[8]) {
-    f[0] = blo(v.x); f[1] = bhi(v.x); f[2] = blo(v.y); f[3] = bhi(v.y);
-    f[4] = blo(v.z); f[5] = bhi(v.z); f[6] = blo(v.w); f[7] = bhi(v.w);
+// U = B^T d B for 2 channels (the two bf16 of 32-bit word w of each unit of
+// the 4x4 patch d); out[xi] = the bf16 pair of U[xi] for those channels.
+__device__ __forceinline__ void wino_transform2(const uint4 d[4][4], int w, uint32_t out[16]) {
+    float lo_[4][4], hi_[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const uint32_t u = w == 0 ? d[a][b].x : w == 1 ? d[a][b].y : w == 2 ? d[a][b].z : d[a][b].w;
+            lo_[a][b] = blo(u);
+            hi_[a][b] = bhi(u);
+        }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float rl[4], rh[4];   // row i of B^T d
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            if (i == 0) { rl[b] = lo_[0][b] - lo_[2][b]; rh[b] = hi_[0][b] - hi_[2][b]; }
+            else if (i == 1) { rl[b] = lo_[1][b] + lo_[2][b]; rh[b] = hi_[1][b] + hi_[2][b]; }
+            else if (i == 2) { rl[b] = lo_[2][b] - lo_[1][b]; rh[b] = hi_[2][b] - hi_[1][b]; }
+            else { rl[b] = lo_[1][b] - lo_[3][b]; rh[b] = hi_[1][b] - hi_[3][b]; }
+        }
+        out[4 * i + 0] = pack_bf16x2(rl[0] - rl[2], rh[0] - rh[2]);
+        out[4 * i + 1] = pack_bf16x2(rl[1] + rl[2], rh[1] + rh[2]);
+        out[4 * i + 2] = pack_bf16x2(rl[2] - rl[1], rh[2] - rh[1]);
+        out[4 * i + 3] = pack_bf16x2(rl[1] - rl[3], rh[1] - rh[3]);
+    }
 }
 
-__device__ __forceinline__ bf16x8 pack8(const float f[8]) {
-    const uint4 u = make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
-                               pack_bf16x2(f[6], f[7]));
-    return __builtin_bit_cast(bf16x8, u);
-}
-
-// One chunk: start copying the next chunk (next >= 0) into (vn, xn), then
-// for this lane's block and 8 channels: U = B^T d B, and acc[xi] += V_xi U_xi.
-// Each LDS buffer is its own restrict argument, so the compiler does not
-// wait for the copies in flight before reading the current buffers.
-__device__ __forceinline__ void wino_chunk(const uint4* __restrict__ vc, const uint4* __restrict__ xc,
-                                           uint4* __restrict__ vn, uint4* __restrict__ xn, f32x16 acc[16],
-                                           const WinoGrid& g, __amdgpu_buffer_rsrc_t vr, __amdgpu_buffer_rsrc_t xr,
-                                           int next, int co0, int n, int ih0, int iw0, int wave, int lane,
-                                           int xoff, int voff) {
-    if (next >= 0) wino_stage(vn, xn, g, vr, xr, next, co0, n, ih0, iw0, wave, lane);
-    // the 4x4 patch of this lane's block, rows a, columns b: units
-    // ((2*tr + a)*18 + 2*tc + b)*2 + half
+// Read this lane's 4x4 patch (block (tr, tc), channel quarter kq) from the
+// patch buffer and transform it: bo[xi] = the MFMA B operand of xi.
+__device__ __forceinline__ void wino_transform(const uint4* __restrict__ xc, int xoff, bf16x8 bo[16]) {
     uint4 d[4][4];
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) d[a][b] = xc[xoff + (a * kWPatch + b) * 2];
+        for (int b = 0; b < 4; ++b) d[a][b] = xc[xoff + (a * kWPatch + b) * kWPix];
+    uint32_t u0[16], u1[16], u2[16], u3[16];
+    wino_transform2(d, 0, u0);
+    wino_transform2(d, 1, u1);
+    wino_transform2(d, 2, u2);
+    wino_transform2(d, 3, u3);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        bf16x8 av[4];   // V of xi = 4i .. 4i+3 for this lane's output channel and 8 channels
+    for (int xi = 0; xi < 16; ++xi) bo[xi] = __builtin_bit_cast(bf16x8, make_uint4(u0[xi], u1[xi], u2[xi], u3[xi]));
+}
+
+// acc[xi][cb] += V_xi (output channels 16cb.., this chunk) x U_xi (16 blocks).
+__device__ __forceinline__ void wino_mfma(const uint4* __restrict__ vc, int voff, const bf16x8 bo[16],
+                                          f32x4 acc[16][4]) {
+    // two-stage pipeline: the A operands of xi+1 are read while the MFMAs of
+    // xi issue; the scheduling fence keeps the compiler from hoisting every
+    // read to the front (64 operands would not fit in registers)
+    bf16x8 av[2][4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) av[j] = __builtin_bit_cast(bf16x8, vc[voff + (4 * i + j) * 2 * kWCo]);
-        // row i of B^T d, per column b and channel
-        float r[4][8];
+    for (int cb = 0; cb < 4; ++cb) av[0][cb] = __builtin_bit_cast(bf16x8, vc[voff + 16 * cb]);
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            float d0[8], d1[8], d2[8], d3[8];
-            unpack8(d[0][b], d0);
-            unpack8(d[1][b], d1);
-            unpack8(d[2][b], d2);
-            unpack8(d[3][b], d3);
+    for (int xi = 0; xi < 16; ++xi) {
+        if (xi + 1 < 16)
 #pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                if (i == 0) r[b][c] = d0[c] - d2[c];
-                else if (i == 1) r[b][c] = d1[c] + d2[c];
-                else if (i == 2) r[b][c] = d2[c] - d1[c];
-                else r[b][c] = d1[c] - d3[c];
-            }
-        }
-        // (B^T d B)[i][j] = the same combination of the row's columns
+            for (int cb = 0; cb < 4; ++cb)
+                av[(xi + 1) & 1][cb] = __builtin_bit_cast(bf16x8, vc[voff + (xi + 1) * 4 * kWCo + 16 * cb]);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            float u[8];
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                if (j == 0) u[c] = r[0][c] - r[2][c];
-                else if (j == 1) u[c] = r[1][c] + r[2][c];
-                else if (j == 2) u[c] = r[2][c] - r[1][c];
-                else u[c] = r[1][c] - r[3][c];
-            }
-            const int xi = 4 * i + j;
-            acc[xi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[j], pack8(u), acc[xi], 0, 0, 0);
-        }
+        for (int cb = 0; cb < 4; ++cb)
+            acc[xi][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[xi & 1][cb], bo[xi], acc[xi][cb], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
     }
+}
+
+// One chunk after its copies have landed: start the next chunk's V copy,
+// transform the patch, release the patch buffer to the next chunk's copy,
+// then the matrix products.  Every LDS buffer is its own restrict argument
+// so the compiler does not wait for copies in flight into the others.
+__device__ __forceinline__ void wino_chunk(const uint4* __restrict__ vc, uint4* __restrict__ vn,
+                                           uint4* __restrict__ xb, f32x4 acc[16][4], const WinoGrid& g,
+                                           __amdgpu_buffer_rsrc_t vr, __amdgpu_buffer_rsrc_t xr, int kc, int co0,
+                                           int n, int ih0, int iw0, int wave, int lane, int xoff, int voff) {
+    const bool more = kc + 1 < g.nchunk;
+    if (more) wino_stage_v(vn, g, vr, kc + 1, co0, wave, lane);
+    bf16x8 bo[16];
+    wino_transform(xb, xoff, bo);
+    lds_barrier();   // every wave has read the patch
+    if (more) wino_stage_x(xb, g, xr, kc + 1, n, ih0, iw0, wave, lane);
+    wino_mfma(vc, voff, bo, acc);
 }
 
 template <bool BIAS, bool RELU>
@@ -186,39 +221,41 @@ __global__ __launch_bounds__(kWThreads, 1) void wino_kernel(const bf16_t* __rest
     const __amdgpu_buffer_rsrc_t vr = make_rsrc(v, (uint32_t)16 * g.Cin * g.Cout * 2u);
     const __amdgpu_buffer_rsrc_t yr = make_rsrc(y, (uint32_t)g.N * g.Ho * g.Wo * g.Cout * 2u);
 
-    // this lane: MFMA column t = lane % 32 is its block (tr, tc) of the
-    // wave's 4x8 blocks; half = lane / 32 its 8 channels of the chunk
-    const int cb = wave >> 1, tb = wave & 1;
-    const int t = lane & 31, half = lane >> 5;
-    const int tr = 4 * tb + (t >> 3), tc = t & 7;
-    const int xoff = ((2 * tr) * kWPatch + 2 * tc) * 2 + half;
-    const int voff = half * kWCo + 32 * cb + t;   // + xi * 2 * 64: V row of output channel 32*cb + t
+    // this lane: MFMA column t = lane % 16 is its block (tr, tc) of the
+    // wave's 2x8 blocks; kq = lane / 16 its 8 channels of the chunk (the K
+    // rows 8kq .. 8kq+7 of its A and B operands)
+    const int t = lane & 15, kq = lane >> 4;
+    const int tr = 2 * wave + (t >> 3), tc = t & 7;
+    const int xoff = ((2 * tr) * kWPatch + 2 * tc) * kWPix + kq;
+    const int voff = kq * kWCo + t;   // + xi*4*64 + 16*cb: V row of output channel 16*cb + t
 
-    f32x16 acc[16];
+    f32x4 acc[16][4];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = f32x16{};
+    for (int i = 0; i < 16; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{};
 
-    uint4* const buf0 = wlds;
-    uint4* const buf1 = wlds + kWBuf;
-    wino_stage(buf0, buf0 + kWVSlots, g, vr, xr, 0, co0, n, ih0, iw0, wave, lane);
+    uint4* const v0 = wlds;
+    uint4* const v1 = wlds + kWVUnits;
+    uint4* const xb = wlds + 2 * kWVUnits;
+    wino_stage_v(v0, g, vr, 0, co0, wave, lane);
+    wino_stage_x(xb, g, xr, 0, n, ih0, iw0, wave, lane);
     for (int kc = 0; kc < g.nchunk; ++kc) {
         // chunk kc has landed (each wave waits for its own copies, the barrier
-        // for everyone's) and every wave is done with the other buffer
+        // for everyone's) and every wave is done with the other V buffer
         __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
         __syncthreads();
-        uint4* const cur = (kc & 1) ? buf1 : buf0;
-        uint4* const nxt = (kc & 1) ? buf0 : buf1;
-        wino_chunk(cur, cur + kWVSlots, nxt, nxt + kWVSlots, acc, g, vr, xr, kc + 1 < g.nchunk ? kc + 1 : -1, co0,
-                   n, ih0, iw0, wave, lane, xoff, voff);
+        wino_chunk((kc & 1) ? v1 : v0, (kc & 1) ? v0 : v1, xb, acc, g, vr, xr, kc, co0, n, ih0, iw0, wave, lane,
+                   xoff, voff);
     }
 
-    // Output transform.  MFMA result layout: lane l holds column l % 32 (its
-    // block) and rows 8q + 4*(l/32) + r (output channels) in acc[xi][4q + r].
+    // Output transform.  MFMA result layout: lane l holds column l % 16 (its
+    // block) and rows 4*(l/16) + r of each 16-channel tile cb in acc[xi][cb][r].
     const int oh = oh0 + 2 * tr, ow = ow0 + 2 * tc;
     const __amdgpu_buffer_rsrc_t br_ = make_rsrc(bias, (uint32_t)g.Cout * 4u);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int co = co0 + 32 * cb + 8 * q + 4 * half;   // 4 consecutive output channels
+    for (int cb = 0; cb < 4; ++cb) {
+        const int co = co0 + 16 * cb + 4 * kq;   // 4 consecutive output channels
         float bq[4] = {0.f, 0.f, 0.f, 0.f};
         if (BIAS) {
             const float4 b4 = __builtin_bit_cast(float4, load16(br_, co < g.Cout ? co * 4 : kOOB));
@@ -229,7 +266,7 @@ __global__ __launch_bounds__(kWThreads, 1) void wino_kernel(const bf16_t* __rest
         for (int r = 0; r < 4; ++r) {
             float m[16];
 #pragma unroll
-            for (int xi = 0; xi < 16; ++xi) m[xi] = acc[xi][4 * q + r];
+            for (int xi = 0; xi < 16; ++xi) m[xi] = acc[xi][cb][r];
             float z0[4], z1[4];   // A^T M
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -293,7 +330,7 @@ WinoGrid wino_grid(const Shape& s) {
     g.nbr = (bh + kWBlk - 1) / kWBlk;
     g.nbc = (bw + kWBlk - 1) / kWBlk;
     g.ncb = (s.Cout + kWCo - 1) / kWCo;
-    g.nchunk = (s.Cin + 15) / 16;
+    g.nchunk = (s.Cin + 31) / 32;
     g.bias = (s.epilogue & CONV2D_EPI_BIAS) != 0;
     g.relu = (s.epilogue & CONV2D_EPI_RELU) != 0;
     return g;
