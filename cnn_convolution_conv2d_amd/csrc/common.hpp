@@ -135,6 +135,10 @@ hipError_t launch_tconv_direct(const Shape& s, const void* x, int xl, const void
 hipError_t launch_igemm_transposed(const Shape& s, const void* x, const void* w_packed, const float* bias,
                                    void* y, hipStream_t st);
 bool igemm_transposed_supports(const Shape& s);
+// kernel == stride, no padding: the pointwise GEMM with pixel-shuffled output
+bool pw_shuffle_supports(const Shape& s);
+hipError_t launch_pw_shuffle(const Shape& s, const void* x, const void* w_packed, const float* bias, void* y,
+                             hipStream_t st);
 hipError_t launch_tpack_weights(const void* w, void* wp, int Cin, int cout_g, int groups, int Kh, int Kw,
                                 int elem_bytes, hipStream_t st);
 

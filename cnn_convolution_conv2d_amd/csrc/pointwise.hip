@@ -19,6 +19,15 @@
 //    fp32 accumulators initialised with the bias;
 //  * the same register epilogue as the halo kernel: ReLU, bf16, two lane
 //    swaps, and stores of 64 contiguous bytes per pixel per instruction.
+//
+// Pixel-shuffle mode (SHUF): a transposed convolution whose kernel equals its
+// stride (K = S, no padding, lpnh.cn sections 2.3 and 4.2) has windows that
+// do not overlap, so Y = W^T X needs no col2im: input pixel (n, ih, iw) times
+// weight row (tap, co) lands in output pixel (ih*S + kh, iw*S + kw), channel
+// co, and every output receives exactly one such row.  The kernel then runs
+// the same GEMM with Cout*S*S rows, ordered (tap, co) when the packed
+// transposed weight [Cout][Kh][Kw][Cin] is staged, and the epilogue sends
+// each row to its output pixel.
 #include "mfma.hpp"
 #include "../../include/conv2d.h"
 
@@ -30,6 +39,19 @@ constexpr int kPwThreads = 256;
 constexpr int kPwWaves = kPwThreads / 64;
 constexpr int kPwMaxLds = 64 * 1024;  // bytes of staged weights
 constexpr int kPwMaxCout = 256;
+constexpr int kPwMaxLdsShuf = 72 * 1024;  // staged weights in pixel-shuffle mode (256 rows x 17 units)
+// Pixel-shuffle mode: activations through LDS (one workgroup per CU: 72 KB
+// of weights plus the tiles) or straight into operand registers; overridable
+// at build time for tuning.
+#ifndef PW_SHUF_STAGED
+#define PW_SHUF_STAGED 0
+#endif
+
+// Pixel-shuffle mode: output channels, kernel width, stride, input and
+// output extents.
+struct PwShuf {
+    int cout, kk, kw, stride, h, w, ho, wo;
+};
 
 // Row pitch of the staged weights and activations in 16-byte units: odd (no
 // bank conflicts), and at least two units per 16-channel slice, so the last
@@ -40,14 +62,14 @@ __host__ __device__ constexpr int pw_pitch(int cin) { return (2 * ((cin + 15) / 
 // of the input (Cin <= 16*KS).  A work item is one 32-pixel tile and one
 // group of MB*32 output channels (nmh groups cover Cout); the items of one
 // tile are consecutive, so the later ones find its activations in cache.
-template <int MB, int KS, bool STAGED>
+template <int MB, int KS, bool STAGED, bool SHUF>
 __global__ __launch_bounds__(kPwThreads, 2) void pw_kernel(const bf16_t* __restrict__ x,
                                                        const bf16_t* __restrict__ wp,
                                                        const float* __restrict__ bias,
                                                        bf16_t* __restrict__ y, int npix, int cin,
                                                        int cout, int ntiles, int nmh, int has_bias,
                                                        int relu, int cin8_magic, const float* scale,
-                                                       const float* shift) {
+                                                       const float* shift, PwShuf sh) {
     // dynamic LDS: weights [rows][P units], then one activation tile
     // [32 pixels][P units] per wave
     extern __shared__ uint4 pw_lds[];
@@ -62,14 +84,16 @@ __global__ __launch_bounds__(kPwThreads, 2) void pw_kernel(const bf16_t* __restr
     {
         // all loads first (zero for padding units), then the LDS stores, so
         // the staging costs one memory latency
-        constexpr int kUnits = (kPwMaxLds / 16 + kPwThreads - 1) / kPwThreads;
+        constexpr int kUnits = ((SHUF ? kPwMaxLdsShuf : kPwMaxLds) / 16 + kPwThreads - 1) / kPwThreads;
         const __amdgpu_buffer_rsrc_t wr = make_rsrc(wp, (uint32_t)cout * (uint32_t)cin * 2u);
         uint4 v[kUnits];
 #pragma unroll
         for (int k = 0; k < kUnits; ++k) {
             const int u = tid + k * kPwThreads;
             const int r = u / P, c = u - r * P;
-            v[k] = load16(wr, (u < rows * P && r < cout && c * 8 < cin) ? (r * cin + c * 8) * 2 : kOOB);
+            // pixel shuffle: LDS row (tap, co) is packed row co*kk + tap
+            const int gr = SHUF ? (r % sh.cout) * sh.kk + r / sh.cout : r;
+            v[k] = load16(wr, (u < rows * P && r < cout && c * 8 < cin) ? (gr * cin + c * 8) * 2 : kOOB);
         }
 #pragma unroll
         for (int k = 0; k < kUnits; ++k) {
@@ -77,7 +101,8 @@ __global__ __launch_bounds__(kPwThreads, 2) void pw_kernel(const bf16_t* __restr
             if (u < rows * P) wl[u] = v[k];
         }
     }
-    for (int i = tid; i < rows; i += kPwThreads) sb[i] = (has_bias && i < cout) ? bias[i] : 0.0f;
+    for (int i = tid; i < rows; i += kPwThreads)
+        sb[i] = (has_bias && i < cout) ? bias[SHUF ? i % sh.cout : i] : 0.0f;
     // pad units of every pixel row of the activation tiles (never written
     // by the staging) are zero
     if (STAGED)
@@ -168,7 +193,14 @@ __global__ __launch_bounds__(kPwThreads, 2) void pw_kernel(const bf16_t* __restr
         int pix_[2];                                                                         \
         _Pragma("unroll") for (int e = 0; e < 2; ++e) {                                      \
             const int p_ = (T) * 32 + 16 * e + (lane & 15);                                  \
-            pix_[e] = p_ < npix ? p_ * cout : -1;                                            \
+            if (SHUF) {                                                                      \
+                /* output pixel (n, ih*S, iw*S): the tap adds kh*Wo + kw */                  \
+                const int iw_ = p_ % sh.w, t_ = p_ / sh.w;                                   \
+                const int ih_ = t_ % sh.h, n_ = t_ / sh.h;                                   \
+                pix_[e] = p_ < npix ? (n_ * sh.ho + ih_ * sh.stride) * sh.wo + iw_ * sh.stride : -1; \
+            } else {                                                                         \
+                pix_[e] = p_ < npix ? p_ * cout : -1;                                        \
+            }                                                                                \
         }                                                                                    \
         _Pragma("unroll") for (int mb = 0; mb < MB; ++mb) {                                  \
             uint32_t pk_[4][2];                                                              \
@@ -195,8 +227,15 @@ __global__ __launch_bounds__(kPwThreads, 2) void pw_kernel(const bf16_t* __restr
                 o_[1][d] = sw_[1];                                                           \
             }                                                                                \
             const int co_ = c0_ + mb * 32 + cl;                                              \
+            int tapoff_ = 0, cc_ = co_;  /* pixel shuffle: row (tap, cc) */                  \
+            if (SHUF) {                                                                      \
+                const int tap_ = co_ / sh.cout;                                              \
+                cc_ = co_ - tap_ * sh.cout;                                                  \
+                const int kh_ = tap_ / sh.kw;                                                \
+                tapoff_ = kh_ * sh.wo + tap_ - kh_ * sh.kw;                                  \
+            }                                                                                \
             _Pragma("unroll") for (int e = 0; e < 2; ++e) {                                  \
-                const int off_ = (pix_[e] + co_) * 2;                                        \
+                const int off_ = SHUF ? ((pix_[e] + tapoff_) * sh.cout + cc_) * 2 : (pix_[e] + co_) * 2; \
                 if (vec16) {                                                                 \
                     store16(yr, pix_[e] >= 0 && co_ < cout ? off_ : kOOB,                    \
                             make_uint4(o_[e][0], o_[e][1], o_[e][2], o_[e][3]));             \
@@ -237,19 +276,38 @@ long long pw_lds_bytes(int cin, int rows, bool staged) {
 // otherwise (wide inputs keep two workgroups per CU that way).
 bool pw_staged(int cin, int cout) { return cin <= 128 && cout >= 128; }
 
-template <int MB, int KS, bool STAGED>
-hipError_t launch_pw(const Shape& s, const bf16_t* x, const bf16_t* w, const float* b, bf16_t* y,
+// One launch: npix rows of the activation matrix, cin channels, cout GEMM
+// rows (output channels, or (tap, channel) rows in pixel-shuffle mode).
+struct PwArgs {
+    int npix, cin, cout, epilogue;
+    const float* scale;
+    const float* shift;
+    PwShuf sh;
+};
+
+template <int MB, int KS, bool STAGED, bool SHUF>
+hipError_t launch_pw(const PwArgs& a, const bf16_t* x, const bf16_t* w, const float* b, bf16_t* y,
                      hipStream_t st) {
-    auto kern = pw_kernel<MB, KS, STAGED>;
-    const int npix = s.N * s.Ho * s.Wo;
+    auto kern = pw_kernel<MB, KS, STAGED, SHUF>;
+    const int npix = a.npix;
     const int ntiles = (npix + 31) / 32;
-    const int nmh = (s.Cout + MB * 32 - 1) / (MB * 32);
-    const long long lds = pw_lds_bytes(s.Cin, nmh * MB * 32, STAGED);
+    const int nmh = (a.cout + MB * 32 - 1) / (MB * 32);
+    const long long lds = pw_lds_bytes(a.cin, nmh * MB * 32, STAGED);
     // unit -> pixel of a tile: (u * magic) >> 16 == u / (Cin/8) for u < 32*Cin/8
-    const int cin8 = s.Cin / 8, magic = (65536 + cin8 - 1) / cin8;
+    const int cin8 = a.cin / 8, magic = (65536 + cin8 - 1) / cin8;
     int dev = 0;
     (void)hipGetDevice(&dev);
-    const int by_regs = blocks_per_cu<pw_kernel<MB, KS, STAGED>>(kPwThreads, dev);
+    if (lds > 64 * 1024) {
+        // above the default dynamic-LDS limit: raise it once per kernel
+        static bool raised = false;
+        if (!raised) {
+            const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            if (e != hipSuccess) return e;
+            raised = true;
+        }
+    }
+    const int by_regs = blocks_per_cu<pw_kernel<MB, KS, STAGED, SHUF>>(kPwThreads, dev);
     const int by_lds = (int)(163840 / (lds + kPwMaxCout * 4));
     const int bpc = by_lds < by_regs ? (by_lds < 1 ? 1 : by_lds) : by_regs;
     // at most two workgroups per CU: with more, the waves' activation streams
@@ -258,28 +316,28 @@ hipError_t launch_pw(const Shape& s, const bf16_t* x, const bf16_t* w, const flo
     const long long resident = (long long)cu_count(dev) * (bpc < 2 ? bpc : 2);
     const long long want = ((long long)ntiles * nmh + kPwWaves - 1) / kPwWaves;
     const int grid = (int)(want < resident ? want : resident);
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(kPwThreads), (unsigned)lds, st, x, w, b, y, npix, s.Cin, s.Cout,
-                       ntiles, nmh, (s.epilogue & CONV2D_EPI_BIAS) ? 1 : 0, (s.epilogue & CONV2D_EPI_RELU) ? 1 : 0,
-                       magic, s.scale, s.shift);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kPwThreads), (unsigned)lds, st, x, w, b, y, npix, a.cin, a.cout,
+                       ntiles, nmh, (a.epilogue & CONV2D_EPI_BIAS) ? 1 : 0, (a.epilogue & CONV2D_EPI_RELU) ? 1 : 0,
+                       magic, a.scale, a.shift, a.sh);
     return hipGetLastError();
 }
 
-template <int MB, bool STAGED>
-hipError_t launch_pw_ks(const Shape& s, const bf16_t* x, const bf16_t* w, const float* b, bf16_t* y,
+template <int MB, bool STAGED, bool SHUF>
+hipError_t launch_pw_ks(const PwArgs& a, const bf16_t* x, const bf16_t* w, const float* b, bf16_t* y,
                         hipStream_t st) {
-    const int ks = (s.Cin + 15) / 16;
-    if (ks <= 4) return launch_pw<MB, 4, STAGED>(s, x, w, b, y, st);
-    if (ks <= 8) return launch_pw<MB, 8, STAGED>(s, x, w, b, y, st);
-    if (ks <= 12) return launch_pw<MB, 12, STAGED>(s, x, w, b, y, st);
-    if constexpr (MB <= 2 && !STAGED) return launch_pw<MB, 16, STAGED>(s, x, w, b, y, st);
+    const int ks = (a.cin + 15) / 16;
+    if (ks <= 4) return launch_pw<MB, 4, STAGED, SHUF>(a, x, w, b, y, st);
+    if (ks <= 8) return launch_pw<MB, 8, STAGED, SHUF>(a, x, w, b, y, st);
+    if (ks <= 12) return launch_pw<MB, 12, STAGED, SHUF>(a, x, w, b, y, st);
+    if constexpr (MB <= 2 && !STAGED) return launch_pw<MB, 16, STAGED, SHUF>(a, x, w, b, y, st);
     return hipErrorInvalidValue;  // more than 192 input channels: at most two blocks, not staged
 }
 
 template <int MB>
-hipError_t launch_pw_mb(const Shape& s, const bf16_t* x, const bf16_t* w, const float* b, bf16_t* y,
+hipError_t launch_pw_mb(const PwArgs& a, const bf16_t* x, const bf16_t* w, const float* b, bf16_t* y,
                         hipStream_t st) {
-    if (pw_staged(s.Cin, s.Cout)) return launch_pw_ks<MB, true>(s, x, w, b, y, st);
-    return launch_pw_ks<MB, false>(s, x, w, b, y, st);
+    if (pw_staged(a.cin, a.cout)) return launch_pw_ks<MB, true, false>(a, x, w, b, y, st);
+    return launch_pw_ks<MB, false, false>(a, x, w, b, y, st);
 }
 
 }  // namespace
@@ -312,9 +370,55 @@ hipError_t launch_pointwise(const Shape& s, const void* x, const void* w_packed,
     const bf16_t* wt = static_cast<const bf16_t*>(w_packed);
     bf16_t* yt = static_cast<bf16_t*>(y);
     const int mb = pw_blocks(s.Cin, s.Cout);
-    if (mb == 1) return launch_pw_mb<1>(s, xt, wt, bias, yt, st);
-    if (mb == 2) return launch_pw_mb<2>(s, xt, wt, bias, yt, st);
-    return launch_pw_mb<4>(s, xt, wt, bias, yt, st);
+    PwArgs a{};
+    a.npix = s.N * s.Ho * s.Wo;
+    a.cin = s.Cin;
+    a.cout = s.Cout;
+    a.epilogue = s.epilogue;
+    a.scale = s.scale;
+    a.shift = s.shift;
+    if (mb == 1) return launch_pw_mb<1>(a, xt, wt, bias, yt, st);
+    if (mb == 2) return launch_pw_mb<2>(a, xt, wt, bias, yt, st);
+    return launch_pw_mb<4>(a, xt, wt, bias, yt, st);
+}
+
+// Pixel-shuffle transposed convolution: kernel = stride, no padding, no
+// output padding, dilation 1, one group; Cout % 32 == 0 so a 32-row block
+// never straddles two taps; Cout*Kh*Kw GEMM rows within the staged-weight
+// budget.  Activations straight into operand registers (the weights alone
+// take up to 72 KB of LDS).
+bool pw_shuffle_supports(const Shape& s) {
+    const long long rows = (long long)s.Cout * s.Kh * s.Kw;
+    const long long npix = (long long)s.N * s.H * s.W;
+    return s.dtype == CONV2D_BF16 && s.groups == 1 && s.Kh == s.stride && s.Kw == s.stride && s.stride > 1 &&
+           s.pad == 0 && s.out_pad == 0 && s.dil == 1 && s.Cin % 8 == 0 && s.Cin <= 256 && s.Cout % 32 == 0 &&
+           rows <= kPwMaxCout && rows * pw_pitch(s.Cin) * 16 <= kPwMaxLdsShuf &&
+           pw_lds_bytes(s.Cin, (int)rows, false) + kPwMaxCout * 4 <= 163840 && npix * s.Cin * 2 < 0x7fff0000LL &&
+           (long long)s.N * s.Ho * s.Wo * s.Cout * 2 < 0x7fff0000LL;
+}
+
+hipError_t launch_pw_shuffle(const Shape& s, const void* x, const void* w_packed, const float* bias, void* y,
+                             hipStream_t st) {
+    (void)hipGetLastError();  // report only this launch's error
+    if (!pw_shuffle_supports(s)) return hipErrorInvalidValue;
+    const bf16_t* xt = static_cast<const bf16_t*>(x);
+    const bf16_t* wt = static_cast<const bf16_t*>(w_packed);
+    bf16_t* yt = static_cast<bf16_t*>(y);
+    PwArgs a{};
+    a.npix = s.N * s.H * s.W;
+    a.cin = s.Cin;
+    a.cout = s.Cout * s.Kh * s.Kw;
+    a.epilogue = s.epilogue;
+    a.scale = nullptr;
+    a.shift = nullptr;
+    a.sh = PwShuf{s.Cout, s.Kh * s.Kw, s.Kw, s.stride, s.H, s.W, s.Ho, s.Wo};
+    const int mb = pw_blocks(a.cin, a.cout);
+    constexpr bool kStaged = PW_SHUF_STAGED != 0;
+    if (pw_lds_bytes(a.cin, (a.cout + 127) / 128 * 128, kStaged) + kPwMaxCout * 4 > 163840)
+        return hipErrorInvalidValue;
+    if (mb == 1) return launch_pw_ks<1, kStaged, true>(a, xt, wt, bias, yt, st);
+    if (mb == 2) return launch_pw_ks<2, kStaged, true>(a, xt, wt, bias, yt, st);
+    return launch_pw_ks<4, kStaged, true>(a, xt, wt, bias, yt, st);
 }
 
 }  // namespace conv2d

@@ -225,12 +225,17 @@ int conv2d_fwd_winograd_nhwc(const void* x, const void* w_wino, const float* bia
  *   w_packed conv2d_transpose_pack_weights of w: [Cout][Kh][Kw][Cin/G]
  *   y        [N][Ho][Wo][Cout]  (NHWC)
  *
- * Paths: CONV2D_PATH_IGEMM_GATHER (bf16, Cin/G % 8 == 0, Cout/G % 4 == 0)
- * splits the output into its S x S phases (rows and columns of one residue
- * mod S); each phase is an implicit GEMM on MFMA over only the taps that
- * reach it.  CONV2D_PATH_DIRECT serves every other shape and dtype.
- * conv2d_set_path_override applies (CONV2D_PATH_IGEMM means the phase GEMM;
- * any other forced path returns CONV2D_ERR_UNSUPPORTED).  Alignment, stream
+ * Paths: CONV2D_PATH_GEMM1X1 when the kernel equals the stride (Kh == Kw ==
+ * S > 1, no padding, no output padding, dilation 1, groups 1, bf16,
+ * Cin % 8 == 0, Cin <= 256, Cout % 32 == 0, Cout*Kh*Kw <= 256): the windows do
+ * not overlap, so Y = W^T X is one GEMM of Cout*Kh*Kw rows over the input
+ * pixels whose rows land in distinct output pixels.  CONV2D_PATH_IGEMM_GATHER
+ * (bf16, Cin/G % 8 == 0, Cout/G % 4 == 0) splits the output into its S x S
+ * phases (rows and columns of one residue mod S); each phase is an implicit
+ * GEMM on MFMA over only the taps that reach it.  CONV2D_PATH_DIRECT serves
+ * every other shape and dtype.  conv2d_set_path_override applies
+ * (CONV2D_PATH_IGEMM means the phase GEMM; a forced path that cannot run the
+ * shape, or any other forced path, returns CONV2D_ERR_UNSUPPORTED).  Alignment, stream
  * and error behaviour as for conv2d_fwd / conv2d_fwd_nhwc_packed; an output
  * padding out of range returns CONV2D_ERR_ARG.
  */

@@ -92,6 +92,36 @@ def test_transposed_sweep(path, mode):
             _check(y, x, w, b, S, P, OP, D, G, ci.BF16, epi, mode, f"{path} case {k} epi {epi}")
 
 
+# kernel == stride, no padding: (N, Cin, H, W, Cout, K=S)
+SHUFFLE = [
+    (2, 32, 9, 11, 64, 2),     # 256 GEMM rows, ragged last pixel tile
+    (1, 16, 5, 7, 32, 2),      # 128 rows
+    (1, 8, 4, 4, 32, 2),       # one 16-byte vector of input channels
+    (2, 192, 4, 3, 32, 2),     # 12 channel slices
+    (1, 64, 3, 5, 32, 4),      # stride 4: 16 taps, 512 rows > 256 -> not eligible (checked)
+]
+
+
+@pytest.mark.parametrize("mode", ["random", "int"])
+def test_transposed_pixel_shuffle(mode):
+    """The pointwise GEMM with pixel-shuffled output (forced), against the
+    oracle; a shape it cannot take is refused when forced."""
+    c2.conv2d_set_path_override(c2.PATH_GEMM1X1)
+    ran = 0
+    for k, (N, Cin, H, W, Cout, K) in enumerate(SHUFFLE):
+        if Cout * K * K > 256:
+            with pytest.raises(c2.Conv2dError):
+                c2.conv2d_transpose_select_path(N, Cin, H, W, Cout, K, K, K, 0, 0, 1, 1, c2.BF16)
+            continue
+        for epi in (0, 3):
+            x, w, b = _tensors(950 + k, N, Cin, H, W, Cout, K, 1, ci.BF16, mode, bias=bool(epi & 1))
+            say(f"[tconv] pixel shuffle {mode} case {k} {(N, Cin, H, W, Cout, K)} epi {epi}")
+            y = run_tnhwc(x, w, b, K, 0, 0, 1, 1, ci.BF16, epi)
+            _check(y, x, w, b, K, 0, 0, 1, 1, ci.BF16, epi, mode, f"shuffle case {k} epi {epi}")
+            ran += 1
+    assert ran == 8
+
+
 @pytest.mark.parametrize("mode", ["random", "int"])
 def test_transposed_fp32_direct(mode):
     for k, (N, Cin, H, W, Cout, K, S, P, OP, D, G) in enumerate(SWEEP[:8]):
@@ -124,12 +154,25 @@ def test_workload_layer_reduced(cid, li, mode):
     ly = ci.layer(cid, li)
     x, w, b = ci.layer_tensors(cid, li, N=2, H=ly.H // 2 + 1, W=ly.W // 2 - 1, mode=mode)
     say(f"[tconv] {ly.name} reduced {mode} x{x.shape}")
+    want = c2.PATH_GEMM1X1 if ly.Kh == ly.stride and ly.pad == 0 else c2.PATH_IGEMM_GATHER
     assert c2.conv2d_transpose_select_path(2, ly.Cin, x.shape[2], x.shape[3], ly.Cout, ly.Kh, ly.Kw, ly.stride,
-                                           ly.pad, ly.out_pad, ly.dilation, ly.groups, c2.BF16) \
-        == c2.PATH_IGEMM_GATHER
+                                           ly.pad, ly.out_pad, ly.dilation, ly.groups, c2.BF16) == want
     y = run_tnhwc(x, w, b, ly.stride, ly.pad, ly.out_pad, ly.dilation, ly.groups, ly.dtype, ly.epilogue)
     _check(y, x, w, b, ly.stride, ly.pad, ly.out_pad, ly.dilation, ly.groups, ly.dtype, ly.epilogue, mode,
            f"{ly.name} reduced {mode}")
+
+
+@pytest.mark.parametrize("mode", ["random", "int"])
+def test_workload_kernel_equals_stride_layer_on_phase_gemm(mode):
+    """The 2x2 stride-2 decoder layer forced onto the phase-split gather GEMM
+    (its automatic path is the pixel-shuffle GEMM)."""
+    ly = ci.layer(6, 1)
+    x, w, b = ci.layer_tensors(6, 1, N=2, H=15, W=13, mode=mode)
+    c2.conv2d_set_path_override(c2.PATH_IGEMM_GATHER)
+    say(f"[tconv] {ly.name} on the phase GEMM {mode}")
+    y = run_tnhwc(x, w, b, ly.stride, ly.pad, ly.out_pad, ly.dilation, ly.groups, ly.dtype, ly.epilogue)
+    _check(y, x, w, b, ly.stride, ly.pad, ly.out_pad, ly.dilation, ly.groups, ly.dtype, ly.epilogue, mode,
+           f"{ly.name} phase GEMM {mode}")
 
 
 def _sample_indices(shape, rng, n_random=4096):
