@@ -106,6 +106,19 @@ int blocks_per_cu(int nt, int dev) {
     return b;
 }
 
+// Allow a kernel more than the default 64 KB of dynamic LDS (up to `bytes`),
+// once per kernel and device.
+template <auto Kernel>
+hipError_t ensure_dynamic_lds(int bytes, int dev) {
+    static int done[64] = {};   // largest size set per device
+    if (dev < 0 || dev >= 64) dev = 0;
+    if (__atomic_load_n(&done[dev], __ATOMIC_RELAXED) >= bytes) return hipSuccess;
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(Kernel),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess) __atomic_store_n(&done[dev], bytes, __ATOMIC_RELAXED);
+    return e;
+}
+
 // Host-side launchers (each defined in its kernel's source file).  They
 // return hipSuccess or the launch error.
 hipError_t launch_direct(const Shape& s, const void* x, int xl, const void* w, int wl,

@@ -298,14 +298,8 @@ hipError_t launch_pw(const PwArgs& a, const bf16_t* x, const bf16_t* w, const fl
     int dev = 0;
     (void)hipGetDevice(&dev);
     if (lds > 64 * 1024) {
-        // above the default dynamic-LDS limit: raise it once per kernel
-        static bool raised = false;
-        if (!raised) {
-            const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-            if (e != hipSuccess) return e;
-            raised = true;
-        }
+        const hipError_t ea = ensure_dynamic_lds<pw_kernel<MB, KS, STAGED, SHUF>>((int)lds, dev);
+        if (ea != hipSuccess) return ea;
     }
     const int by_regs = blocks_per_cu<pw_kernel<MB, KS, STAGED, SHUF>>(kPwThreads, dev);
     const int by_lds = (int)(163840 / (lds + kPwMaxCout * 4));

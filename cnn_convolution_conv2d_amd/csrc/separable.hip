@@ -341,13 +341,8 @@ hipError_t launch_sep(const SepPlan& pl, const bf16_t* x, const bf16_t* wdw, con
     auto kern = sep_kernel<S, sep_rows(S), DWR>;
     int dev = 0;
     (void)hipGetDevice(&dev);
-    static bool attr_set[64] = {};
-    if (dev >= 0 && dev < 64 && !attr_set[dev]) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, kSepLds);
-        if (e != hipSuccess) return e;
-        attr_set[dev] = true;
-    }
+    const hipError_t ea = ensure_dynamic_lds<sep_kernel<S, sep_rows(S), DWR>>(kSepLds, dev);
+    if (ea != hipSuccess) return ea;
     const int by_regs = blocks_per_cu<sep_kernel<S, sep_rows(S), DWR>>(kSepThreads, dev);
     const int by_lds = (int)(163840 / (pl.lds + kSepMaxCout * 4));
     const int bpc = by_lds < by_regs ? (by_lds < 1 ? 1 : by_lds) : by_regs;

@@ -338,13 +338,10 @@ WinoGrid wino_grid(const Shape& s) {
 
 template <bool BIAS, bool RELU>
 hipError_t launch_w(const WinoGrid& g, const bf16_t* x, const bf16_t* v, const float* b, bf16_t* y, hipStream_t st) {
-    static bool attr = false;   // dynamic LDS above 64 KB needs the kernel attribute once per process
-    if (!attr) {
-        const hipError_t e = hipFuncSetAttribute((const void*)wino_kernel<BIAS, RELU>,
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, kWLds);
-        if (e != hipSuccess) return e;
-        attr = true;
-    }
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    const hipError_t ea = ensure_dynamic_lds<wino_kernel<BIAS, RELU>>(kWLds, dev);
+    if (ea != hipSuccess) return ea;
     const long long blocks = (long long)g.N * g.nbr * g.nbc * g.ncb;
     hipLaunchKernelGGL((wino_kernel<BIAS, RELU>), dim3((unsigned)blocks), dim3(kWThreads), kWLds, st, x, v, b, y, g);
     return hipGetLastError();
