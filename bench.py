@@ -59,7 +59,7 @@ KERNEL_SOURCES = {"direct": ["direct.hip"], "depthwise": ["depthwise.hip", "dwro
                   "gemm1x1": ["pointwise.hip", "igemm.hip"], "igemm_gather": ["igemm.hip"],
                   "igemm_halo": ["igemm_halo.hip"], "separable": ["separable.hip", "dwrow.hpp"],
                   "transposed_igemm_gather": ["igemm.hip"], "transposed_direct": ["transposed.hip"],
-                  "transposed_gemm1x1": ["pointwise.hip"],
+                  "transposed_gemm1x1": ["pointwise.hip"], "transposed_igemm_halo": ["transposed.hip"],
                   "winograd": ["winograd.hip"]}
 
 

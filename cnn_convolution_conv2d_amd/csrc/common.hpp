@@ -148,6 +148,10 @@ hipError_t launch_tconv_direct(const Shape& s, const void* x, int xl, const void
 hipError_t launch_igemm_transposed(const Shape& s, const void* x, const void* w_packed, const float* bias,
                                    void* y, hipStream_t st);
 bool igemm_transposed_supports(const Shape& s);
+// stride 2, 4x4: all phases on one staged input window
+bool tconv_halo_supports(const Shape& s);
+hipError_t launch_tconv_halo(const Shape& s, const void* x, const void* w_packed, const float* bias, void* y,
+                             hipStream_t st);
 // kernel == stride, no padding: the pointwise GEMM with pixel-shuffled output
 bool pw_shuffle_supports(const Shape& s);
 hipError_t launch_pw_shuffle(const Shape& s, const void* x, const void* w_packed, const float* bias, void* y,

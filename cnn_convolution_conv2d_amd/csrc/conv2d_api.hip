@@ -295,19 +295,23 @@ int validate_transposed(const void* x, const void* w, const float* bias, const v
 }
 
 // Transposed paths: kernel == stride without padding -> the pointwise GEMM
-// with pixel-shuffled output (reported as the 1x1 path); other
-// channel-aligned bf16 -> the phase-split implicit GEMM (reported as the
-// gather path); the direct loop otherwise.
+// with pixel-shuffled output (reported as the 1x1 path); stride 2 with a 4x4
+// kernel -> all phases on one staged input window (reported as the halo
+// path); other channel-aligned bf16 -> the phase-split implicit GEMM
+// (reported as the gather path); the direct loop otherwise.
 int choose_tpath(const Shape& s) {
     const bool mfma = s.dtype == CONV2D_BF16 && igemm_transposed_supports(s);
     const bool shuf = pw_shuffle_supports(s);
+    const bool halo = tconv_halo_supports(s);
     const int forced = __atomic_load_n(&g_path_override, __ATOMIC_RELAXED);
     if (forced == CONV2D_PATH_AUTO)
-        return shuf ? CONV2D_PATH_GEMM1X1 : mfma ? CONV2D_PATH_IGEMM_GATHER : CONV2D_PATH_DIRECT;
+        return shuf ? CONV2D_PATH_GEMM1X1 : halo ? CONV2D_PATH_IGEMM_HALO
+                                                 : mfma ? CONV2D_PATH_IGEMM_GATHER : CONV2D_PATH_DIRECT;
     if (forced == CONV2D_PATH_DIRECT) return CONV2D_PATH_DIRECT;
     if ((forced == CONV2D_PATH_IGEMM || forced == CONV2D_PATH_IGEMM_GATHER) && mfma)
         return CONV2D_PATH_IGEMM_GATHER;
     if (forced == CONV2D_PATH_GEMM1X1 && shuf) return CONV2D_PATH_GEMM1X1;
+    if (forced == CONV2D_PATH_IGEMM_HALO && halo) return CONV2D_PATH_IGEMM_HALO;
     return set_error(CONV2D_ERR_UNSUPPORTED, "forced path %d cannot run this transposed convolution", forced);
 }
 
@@ -319,8 +323,9 @@ int run_tnhwc(int path, const Shape& s, const void* x, const void* wp, const flo
     } else {
         if (!(aligned16(x) && aligned16(wp) && aligned16(y)))
             return set_error(CONV2D_ERR_ALIGN, "x, w_packed and y must be 16-byte aligned for path %d", path);
-        e = path == CONV2D_PATH_GEMM1X1 ? launch_pw_shuffle(s, x, wp, bias, y, st)
-                                        : launch_igemm_transposed(s, x, wp, bias, y, st);
+        e = path == CONV2D_PATH_GEMM1X1     ? launch_pw_shuffle(s, x, wp, bias, y, st)
+            : path == CONV2D_PATH_IGEMM_HALO ? launch_tconv_halo(s, x, wp, bias, y, st)
+                                             : launch_igemm_transposed(s, x, wp, bias, y, st);
     }
     return e == hipSuccess ? CONV2D_OK : hip_fail(e, "transposed kernel launch");
 }

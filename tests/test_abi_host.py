@@ -244,7 +244,7 @@ def test_transpose_entries_reject_bad_args_before_any_gpu_work():
 
 def test_transpose_path_selection():
     sel = c2.conv2d_transpose_select_path
-    for li, want in ((0, c2.PATH_IGEMM_GATHER), (1, c2.PATH_GEMM1X1)):
+    for li, want in ((0, c2.PATH_IGEMM_HALO), (1, c2.PATH_GEMM1X1)):
         ly = ci.layer(6, li)
         assert sel(ly.N, ly.Cin, ly.H, ly.W, ly.Cout, ly.Kh, ly.Kw, ly.stride, ly.pad, ly.out_pad, ly.dilation,
                    ly.groups, c2.BF16) == want
@@ -254,6 +254,10 @@ def test_transpose_path_selection():
     assert sel(1, 16, 8, 8, 32, 4, 4, 4, 0, 0, 1, 1, c2.BF16) == c2.PATH_IGEMM_GATHER
     assert sel(1, 16, 8, 8, 48, 2, 2, 2, 0, 0, 1, 1, c2.BF16) == c2.PATH_IGEMM_GATHER   # Cout % 32
     assert sel(1, 12, 8, 8, 16, 4, 4, 2, 1, 0, 1, 1, c2.BF16) == c2.PATH_DIRECT   # Cin % 8 != 0
+    assert sel(1, 16, 8, 8, 16, 4, 4, 2, 1, 0, 1, 1, c2.BF16) == c2.PATH_IGEMM_GATHER   # Cin % 32 != 0
+    assert sel(1, 32, 8, 8, 16, 4, 4, 2, 1, 0, 1, 1, c2.BF16) == c2.PATH_IGEMM_HALO
+    assert sel(1, 32, 8, 8, 16, 4, 4, 2, 1, 0, 2, 1, c2.BF16) == c2.PATH_IGEMM_GATHER   # dilation 2
+    assert sel(1, 32, 8, 8, 16, 3, 3, 2, 1, 0, 1, 1, c2.BF16) == c2.PATH_IGEMM_GATHER   # 3x3
     assert sel(1, 16, 8, 8, 16, 4, 4, 2, 1, 0, 1, 1, c2.F32) == c2.PATH_DIRECT
     prev = c2.conv2d_set_path_override(c2.PATH_DEPTHWISE)
     try:
@@ -263,6 +267,10 @@ def test_transpose_path_selection():
         assert sel(1, 16, 8, 8, 16, 4, 4, 2, 1, 0, 1, 1, c2.BF16) == c2.PATH_DIRECT
         c2.conv2d_set_path_override(c2.PATH_IGEMM)
         assert sel(1, 16, 8, 8, 16, 4, 4, 2, 1, 0, 1, 1, c2.BF16) == c2.PATH_IGEMM_GATHER
+        c2.conv2d_set_path_override(c2.PATH_IGEMM_HALO)
+        assert sel(1, 32, 8, 8, 16, 4, 4, 2, 1, 0, 1, 1, c2.BF16) == c2.PATH_IGEMM_HALO
+        with pytest.raises(c2.Conv2dError):
+            sel(1, 16, 8, 8, 16, 4, 4, 2, 1, 0, 1, 1, c2.BF16)
     finally:
         c2.conv2d_set_path_override(prev)
 

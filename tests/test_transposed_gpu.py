@@ -122,6 +122,32 @@ def test_transposed_pixel_shuffle(mode):
     assert ran == 8
 
 
+# stride 2, 4x4 kernel: (N, Cin, H, W, Cout, pad, out_pad)
+HALO = [
+    (2, 32, 9, 11, 48, 1, 0),     # several tiles' worth of rows, ragged columns, a partial channel group
+    (1, 64, 17, 40, 32, 1, 1),    # two column tiles, output padding
+    (1, 32, 5, 6, 36, 0, 0),      # padding 0: output 2H + 2
+    (1, 32, 6, 5, 40, 2, 1),      # padding 2
+    (2, 96, 4, 3, 8, 3, 0),       # padding 3, three channel chunks
+    (1, 32, 1, 1, 4, 1, 0),       # a single input pixel
+]
+
+
+@pytest.mark.parametrize("mode", ["random", "int"])
+def test_transposed_halo_window(mode):
+    """All phases from one staged input window (forced), against the oracle;
+    a shape it cannot take is refused when forced."""
+    c2.conv2d_set_path_override(c2.PATH_IGEMM_HALO)
+    for k, (N, Cin, H, W, Cout, P, OP) in enumerate(HALO):
+        for epi in (0, 3):
+            x, w, b = _tensors(980 + k, N, Cin, H, W, Cout, 4, 1, ci.BF16, mode, bias=bool(epi & 1))
+            say(f"[tconv] halo window {mode} case {k} {(N, Cin, H, W, Cout, P, OP)} epi {epi}")
+            y = run_tnhwc(x, w, b, 2, P, OP, 1, 1, ci.BF16, epi)
+            _check(y, x, w, b, 2, P, OP, 1, 1, ci.BF16, epi, mode, f"halo case {k} epi {epi}")
+    with pytest.raises(c2.Conv2dError):   # Cin not a multiple of 32
+        c2.conv2d_transpose_select_path(1, 24, 8, 8, 16, 4, 4, 2, 1, 0, 1, 1, c2.BF16)
+
+
 @pytest.mark.parametrize("mode", ["random", "int"])
 def test_transposed_fp32_direct(mode):
     for k, (N, Cin, H, W, Cout, K, S, P, OP, D, G) in enumerate(SWEEP[:8]):
@@ -154,7 +180,7 @@ def test_workload_layer_reduced(cid, li, mode):
     ly = ci.layer(cid, li)
     x, w, b = ci.layer_tensors(cid, li, N=2, H=ly.H // 2 + 1, W=ly.W // 2 - 1, mode=mode)
     say(f"[tconv] {ly.name} reduced {mode} x{x.shape}")
-    want = c2.PATH_GEMM1X1 if ly.Kh == ly.stride and ly.pad == 0 else c2.PATH_IGEMM_GATHER
+    want = c2.PATH_GEMM1X1 if ly.Kh == ly.stride and ly.pad == 0 else c2.PATH_IGEMM_HALO
     assert c2.conv2d_transpose_select_path(2, ly.Cin, x.shape[2], x.shape[3], ly.Cout, ly.Kh, ly.Kw, ly.stride,
                                            ly.pad, ly.out_pad, ly.dilation, ly.groups, c2.BF16) == want
     y = run_tnhwc(x, w, b, ly.stride, ly.pad, ly.out_pad, ly.dilation, ly.groups, ly.dtype, ly.epilogue)
@@ -163,11 +189,12 @@ def test_workload_layer_reduced(cid, li, mode):
 
 
 @pytest.mark.parametrize("mode", ["random", "int"])
-def test_workload_kernel_equals_stride_layer_on_phase_gemm(mode):
-    """The 2x2 stride-2 decoder layer forced onto the phase-split gather GEMM
-    (its automatic path is the pixel-shuffle GEMM)."""
-    ly = ci.layer(6, 1)
-    x, w, b = ci.layer_tensors(6, 1, N=2, H=15, W=13, mode=mode)
+@pytest.mark.parametrize("li", [0, 1])
+def test_workload_layer_on_phase_gemm(li, mode):
+    """Each decoder layer forced onto the phase-split gather GEMM (their
+    automatic paths are the halo window and the pixel-shuffle GEMM)."""
+    ly = ci.layer(6, li)
+    x, w, b = ci.layer_tensors(6, li, N=2, H=15, W=13, mode=mode)
     c2.conv2d_set_path_override(c2.PATH_IGEMM_GATHER)
     say(f"[tconv] {ly.name} on the phase GEMM {mode}")
     y = run_tnhwc(x, w, b, ly.stride, ly.pad, ly.out_pad, ly.dilation, ly.groups, ly.dtype, ly.epilogue)
