@@ -8,8 +8,8 @@ Tolerances, element by element, S = sum |x w| over the valid taps:
   bf16 random data  |y - yref| <= 1e-2 S + 1e-3
   exact-integer mode (x in {-2..2}, w in {-1,0,1}, integer bias): the
   transformed input holds integers up to 8 and the transformed filter
-  multiples of 1/4 up to 9/4 -- all exact in bf16 -- and every sum is a
-  multiple of 1/16 far below 2^20, exact in fp32, so the output equals
+  multiples of 1/4 up to 9/4 -- all exact in bf16 -- so every product and sum
+  is a multiple of 1/4 far below 2^20, exact in fp32, and the output equals
   round-to-nearest-even(yref) bit for bit.
 """
 import sys
