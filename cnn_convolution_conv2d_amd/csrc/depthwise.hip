@@ -60,22 +60,29 @@ __device__ __forceinline__ V8 finish(const float acc[8], const float b[8], const
     return o;
 }
 
-// 3x3, stride 1, dilation 1, any padding: the row arithmetic of dwrow.hpp,
-// with two input rows of loads in flight ahead of it (the loop is unrolled by
-// two so that no register with a pending load is ever moved).
-template <int TH, bool BIAS, bool RELU>
+// 3x3, stride 1, dilation 1, any padding: the row arithmetic of dwrow.hpp.
+// The thread's TH + 2 input rows are loaded PF rows ahead of their use (the
+// row loop is unrolled at compile time, so every row has registers of its
+// own and no register with a pending load is ever moved).  Work items are
+// (image, strip of TH rows, 256-vector slice of a row), numbered so that each
+// XCD takes one contiguous run of them: the strips of an image that share
+// halo rows then read them through one L2.
+template <int TH, int PF, bool BIAS, bool RELU>
 __global__ __launch_bounds__(kThreads) void dw3x3s1_kernel(const bf16_t* __restrict__ x,
                                                            const bf16_t* __restrict__ w,   // [3][3][C]
                                                            const float* __restrict__ bias,
                                                            bf16_t* __restrict__ y, Shape s) {
-    static_assert(TH % 2 == 0, "rows per thread come in pairs");
+    static_assert(PF >= 1 && PF <= TH + 2, "rows in flight");
     const int CV = s.Cin >> 3;                       // 16-byte vectors per pixel
-    const int v = blockIdx.x * kThreads + threadIdx.x;
-    if (v >= s.Wo * CV) return;
+    const int gx = (s.Wo * CV + kThreads - 1) / kThreads, gy = (s.Ho + TH - 1) / TH;
+    const int item = xcd_tile_index();
+    const int bx = item % gx, t = item / gx;
+    const int by = t % gy, n = t / gy;
+    const int v = bx * kThreads + threadIdx.x;
+    if (n >= s.N || v >= s.Wo * CV) return;
     const int wo = v / CV;
     const int c0 = (v - wo * CV) << 3;
-    const int n = blockIdx.z;
-    const int ho0 = blockIdx.y * TH;
+    const int ho0 = by * TH;
     const int ho1 = min(ho0 + TH, s.Ho);
 
     // weights: per filter row, the (kw0, kw1) pair of each channel and kw2 in fp32
@@ -96,13 +103,15 @@ __global__ __launch_bounds__(kThreads) void dw3x3s1_kernel(const bf16_t* __restr
     for (int k = 0; k < 3; ++k)
         coff[k] = ((unsigned)(wi0 + k) < (unsigned)s.W) ? (img + (wi0 + k) * s.Cin) * 2 : kOOB;
     const int rstride = s.W * s.Cin * 2;
-    auto row_off = [&](int hi_, int k) {
-        return ((unsigned)hi_ < (unsigned)s.H && coff[k] != kOOB) ? coff[k] + hi_ * rstride : kOOB;
+    const int hb = ho0 - s.pad;  // input row of filter row 0 for output row ho0
+    V8 raw[TH + 2][3];
+    auto load_row = [&](int r) {
+        const int hi_ = hb + r;
+#pragma unroll
+        for (int k = 0; k < 3; ++k)
+            raw[r][k] = load_v8(xr, ((unsigned)hi_ < (unsigned)s.H && coff[k] != kOOB) ? coff[k] + hi_ * rstride
+                                                                                        : kOOB);
     };
-#define DW_LOAD(RAW, HI)                                                                     \
-    do {                                                                                     \
-        _Pragma("unroll") for (int k = 0; k < 3; ++k) RAW[k] = load_v8(xr, row_off((HI), k)); \
-    } while (0)
 
     bf16_t* yrow = y + ((size_t)n * s.Ho * s.Wo + wo) * s.Cout + c0;
     auto emit = [&](int ho, const RowX& r0, const RowX& r1, const RowX& r2) {
@@ -122,30 +131,15 @@ __global__ __launch_bounds__(kThreads) void dw3x3s1_kernel(const bf16_t* __restr
         if (ho < ho1) *reinterpret_cast<V8*>(yrow + (size_t)ho * s.Wo * s.Cout) = o;
     };
 
-    const int hb = ho0 - s.pad;  // input row of filter row 0 for output row ho0
-    V8 rawA[3], rawB[3];
-    RowX R0, R1, R2;
-    DW_LOAD(rawA, hb);
-    DW_LOAD(rawB, hb + 1);
-    prep_row(rawA[0], rawA[1], rawA[2], R0);
-    DW_LOAD(rawA, hb + 2);
-    prep_row(rawB[0], rawB[1], rawB[2], R1);
-    DW_LOAD(rawB, hb + 3);
-    prep_row(rawA[0], rawA[1], rawA[2], R2);
-    // invariant at the top of each half-iteration: R0..R2 hold input rows
-    // ho-pad .. ho-pad+2; rawB holds row ho-pad+3 (arriving)
 #pragma unroll
-    for (int ho = ho0; ho < ho0 + TH; ho += 2) {
-        DW_LOAD(rawA, hb + (ho - ho0) + 4);
-        emit(ho, R0, R1, R2);
-        prep_row(rawB[0], rawB[1], rawB[2], R0);  // R0 <- row ho-pad+3
-        DW_LOAD(rawB, hb + (ho - ho0) + 5);
-        emit(ho + 1, R1, R2, R0);
-        prep_row(rawA[0], rawA[1], rawA[2], R1);  // R1 <- row ho-pad+4
-        // rotate names for the next pair: rows now R2, R0, R1
-        RowX t = R0; R0 = R2; R2 = R1; R1 = t;
+    for (int r = 0; r < PF; ++r) load_row(r);
+    RowX R[TH + 2];
+#pragma unroll
+    for (int r = 0; r < TH + 2; ++r) {
+        if (r + PF < TH + 2) load_row(r + PF);
+        prep_row(raw[r][0], raw[r][1], raw[r][2], R[r]);
+        if (r >= 2) emit(ho0 + r - 2, R[r - 2], R[r - 1], R[r]);
     }
-#undef DW_LOAD
 }
 
 // Any Kh, Kw, stride, padding, dilation.
@@ -190,6 +184,9 @@ __global__ __launch_bounds__(kThreads) void dw_generic_kernel(const bf16_t* __re
 #ifndef DW_ROWS_PER_THREAD
 #define DW_ROWS_PER_THREAD 14
 #endif
+#ifndef DW_ROWS_IN_FLIGHT
+#define DW_ROWS_IN_FLIGHT 2
+#endif
 static_assert(DW_ROWS_PER_THREAD % 2 == 0, "rows per thread come in pairs");
 constexpr int kTH = DW_ROWS_PER_THREAD;  // output rows per thread
 
@@ -199,7 +196,8 @@ hipError_t launch_epi(const Shape& s, const bf16_t* x, const bf16_t* w, const fl
     const int CV = s.Cin / 8;
     dim3 grid((s.Wo * CV + kThreads - 1) / kThreads, (s.Ho + kTH - 1) / kTH, s.N);
     if (s.Kh == 3 && s.Kw == 3 && s.stride == 1 && s.dil == 1)
-        hipLaunchKernelGGL((dw3x3s1_kernel<kTH, BIAS, RELU>), grid, dim3(kThreads), 0, st, x, w, b, y, s);
+        hipLaunchKernelGGL((dw3x3s1_kernel<kTH, DW_ROWS_IN_FLIGHT, BIAS, RELU>), dim3(grid.x * grid.y * grid.z),
+                           dim3(kThreads), 0, st, x, w, b, y, s);
     else
         hipLaunchKernelGGL((dw_generic_kernel<kTH, BIAS, RELU>), grid, dim3(kThreads), 0, st, x, w, b, y, s);
     return hipGetLastError();
@@ -208,8 +206,10 @@ hipError_t launch_epi(const Shape& s, const bf16_t* x, const bf16_t* w, const fl
 }  // namespace
 
 bool depthwise_supports(const Shape& s) {
-    // 16-byte channel vectors; the grid's y/z extents within launch limits
-    return s.Cin % 8 == 0 && s.N <= 65535 && (s.Ho + kTH - 1) / kTH <= 65535;
+    // 16-byte channel vectors; the grid's y/z extents (and, for 3x3 stride 1,
+    // their product with x) within launch limits
+    const long long items = (long long)((s.Wo * (s.Cin / 8) + kThreads - 1) / kThreads) * ((s.Ho + kTH - 1) / kTH) * s.N;
+    return s.Cin % 8 == 0 && s.N <= 65535 && (s.Ho + kTH - 1) / kTH <= 65535 && items < 0x7fffffffLL;
 }
 
 hipError_t launch_depthwise(const Shape& s, const void* x, const void* w_dw, const float* bias,

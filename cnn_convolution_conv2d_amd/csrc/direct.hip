@@ -79,6 +79,95 @@ __global__ __launch_bounds__(kThreads) void direct_kernel(const T* __restrict__ 
     }
 }
 
+// 3x3 filters over few input channels per group (CI <= 4: a stem layer on an
+// RGB image is the common case).  The K dimension is only CI*9, so the
+// generic loop above is one dependent global load per tap; here the taps are
+// unrolled, every input value of the window is requested at once (one memory
+// latency instead of CI*9), and the block's weights sit in LDS as
+// [tap][COB], read as broadcasts.
+template <typename T, int XL, int WL, int YL, int CI, int COB, bool BIAS, bool RELU>
+__global__ __launch_bounds__(kThreads) void direct3x3_small_kernel(const T* __restrict__ x,
+                                                                   const T* __restrict__ w,
+                                                                   const float* __restrict__ bias,
+                                                                   T* __restrict__ y, Shape s) {
+    constexpr int NT = CI * 9;  // taps per output
+    __shared__ __align__(16) float ws[NT][COB];
+    const int ncob = (s.cout_g + COB - 1) / COB;
+    const int g = blockIdx.y / ncob;
+    const int cb = blockIdx.y - g * ncob;
+    const int co_base = g * s.cout_g + cb * COB;
+    const int nco = min(COB, s.cout_g - cb * COB);
+    for (int i = threadIdx.x; i < NT * COB; i += kThreads) {
+        const int tap = i / COB, j = i - tap * COB;
+        const int ci = tap / 9, kh = (tap / 3) % 3, kw = tap % 3;
+        const int co = co_base + j;
+        const int wi_ = (WL == W_OIHW) ? ((co * CI + ci) * 3 + kh) * 3 + kw : ((co * 3 + kh) * 3 + kw) * CI + ci;
+        ws[tap][j] = j < nco ? load_f32<T>(w, wi_) : 0.0f;
+    }
+    __syncthreads();
+    const int npix = s.N * s.Ho * s.Wo;
+    const int p = blockIdx.x * kThreads + threadIdx.x;
+    if (p >= npix) return;
+    const int wo = p % s.Wo;
+    const int t = p / s.Wo;
+    const int ho = t % s.Ho;
+    const int n = t / s.Ho;
+
+    float xv[NT];
+#pragma unroll
+    for (int ci = 0; ci < CI; ++ci) {
+        const int c = g * CI + ci;
+#pragma unroll
+        for (int kh = 0; kh < 3; ++kh) {
+            const int hi = ho * s.stride + kh * s.dil - s.pad;
+#pragma unroll
+            for (int kw = 0; kw < 3; ++kw) {
+                const int wi = wo * s.stride + kw * s.dil - s.pad;
+                const bool ok = (unsigned)hi < (unsigned)s.H && (unsigned)wi < (unsigned)s.W;
+                const int xi = (XL == NCHW) ? ((n * s.Cin + c) * s.H + hi) * s.W + wi
+                                            : ((n * s.H + hi) * s.W + wi) * s.Cin + c;
+                xv[(ci * 3 + kh) * 3 + kw] = ok ? load_f32<T>(x, xi) : 0.0f;
+            }
+        }
+    }
+    float acc[COB];
+#pragma unroll
+    for (int j = 0; j < COB; ++j) acc[j] = 0.0f;
+#pragma unroll
+    for (int tap = 0; tap < NT; ++tap)
+#pragma unroll
+        for (int j = 0; j < COB; ++j) acc[j] = fmaf(xv[tap], ws[tap][j], acc[j]);
+#pragma unroll
+    for (int j = 0; j < COB; ++j) {
+        if (j < nco) {
+            const int co = co_base + j;
+            const float v = epilogue<BIAS, RELU>(acc[j], bias, s.scale, s.shift, co);
+            const int yi = (YL == NCHW) ? ((n * s.Cout + co) * s.Ho + ho) * s.Wo + wo
+                                        : ((n * s.Ho + ho) * s.Wo + wo) * s.Cout + co;
+            store_f32<T>(y, yi, v);
+        }
+    }
+}
+
+template <typename T, int XL, int WL, int YL, int CI>
+hipError_t launch_small(const Shape& s, const T* x, const T* w, const float* b, T* y, hipStream_t st) {
+    constexpr int COB = 8;
+    const int npix = s.N * s.Ho * s.Wo;
+    const int ncob = (s.cout_g + COB - 1) / COB;
+    if ((long long)s.groups * ncob > 65535) return hipErrorInvalidConfiguration;
+    dim3 grid((npix + kThreads - 1) / kThreads, s.groups * ncob);
+    const bool bias = s.epilogue & CONV2D_EPI_BIAS, relu = s.epilogue & CONV2D_EPI_RELU;
+#define SMALL_LAUNCH(B_, R_)                                                                 \
+    hipLaunchKernelGGL((direct3x3_small_kernel<T, XL, WL, YL, CI, COB, B_, R_>), grid, dim3(kThreads), 0, st, x, w, \
+                       b, y, s)
+    if (bias && relu) SMALL_LAUNCH(true, true);
+    else if (bias) SMALL_LAUNCH(true, false);
+    else if (relu) SMALL_LAUNCH(false, true);
+    else SMALL_LAUNCH(false, false);
+#undef SMALL_LAUNCH
+    return hipGetLastError();
+}
+
 template <typename T, int XL, int WL, int YL, int COB>
 hipError_t launch_t(const Shape& s, const T* x, const T* w, const float* b, T* y, hipStream_t st) {
     const int npix = s.N * s.Ho * s.Wo;
@@ -102,6 +191,14 @@ hipError_t launch_cob(const Shape& s, const void* x, const void* w, const float*
     const T* xt = static_cast<const T*>(x);
     const T* wt = static_cast<const T*>(w);
     T* yt = static_cast<T*>(y);
+    // 3x3 over at most 4 input channels per group, at least 8 outputs per
+    // group: the unrolled small-K kernel.
+    if (WL != W_DW && s.Kh == 3 && s.Kw == 3 && s.cout_g >= 8 && s.cin_g <= 4) {
+        if (s.cin_g == 1) return launch_small<T, XL, WL, YL, 1>(s, xt, wt, b, yt, st);
+        if (s.cin_g == 2) return launch_small<T, XL, WL, YL, 2>(s, xt, wt, b, yt, st);
+        if (s.cin_g == 3) return launch_small<T, XL, WL, YL, 3>(s, xt, wt, b, yt, st);
+        return launch_small<T, XL, WL, YL, 4>(s, xt, wt, b, yt, st);
+    }
     // Few output channels per group (depthwise, small layers): 1 or 4 per
     // thread; otherwise 8, or 16 when the pixel grid alone would not fill the
     // chip.

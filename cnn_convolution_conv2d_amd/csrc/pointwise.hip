@@ -43,6 +43,10 @@ constexpr int kPwMaxLdsShuf = 72 * 1024;  // staged weights in pixel-shuffle mod
 // Pixel-shuffle mode: activations through LDS (one workgroup per CU: 72 KB
 // of weights plus the tiles) or straight into operand registers; overridable
 // at build time for tuning.
+// The first tile's activation loads are issued before the weight staging.
+#ifndef PW_EARLY
+#define PW_EARLY 1
+#endif
 #ifndef PW_SHUF_STAGED
 #define PW_SHUF_STAGED 0
 #endif
@@ -77,38 +81,7 @@ __global__ __launch_bounds__(kPwThreads, 2) void pw_kernel(const bf16_t* __restr
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int P = pw_pitch(cin);
     uint4* const wl = pw_lds;
-
-    // stage the weights (rows past Cout and channels past Cin are zero) and
-    // the bias
-    const int rows = nmh * MB * 32;
-    {
-        // all loads first (zero for padding units), then the LDS stores, so
-        // the staging costs one memory latency
-        constexpr int kUnits = ((SHUF ? kPwMaxLdsShuf : kPwMaxLds) / 16 + kPwThreads - 1) / kPwThreads;
-        const __amdgpu_buffer_rsrc_t wr = make_rsrc(wp, (uint32_t)cout * (uint32_t)cin * 2u);
-        uint4 v[kUnits];
-#pragma unroll
-        for (int k = 0; k < kUnits; ++k) {
-            const int u = tid + k * kPwThreads;
-            const int r = u / P, c = u - r * P;
-            // pixel shuffle: LDS row (tap, co) is packed row co*kk + tap
-            const int gr = SHUF ? (r % sh.cout) * sh.kk + r / sh.cout : r;
-            v[k] = load16(wr, (u < rows * P && r < cout && c * 8 < cin) ? (gr * cin + c * 8) * 2 : kOOB);
-        }
-#pragma unroll
-        for (int k = 0; k < kUnits; ++k) {
-            const int u = tid + k * kPwThreads;
-            if (u < rows * P) wl[u] = v[k];
-        }
-    }
-    for (int i = tid; i < rows; i += kPwThreads)
-        sb[i] = (has_bias && i < cout) ? bias[SHUF ? i % sh.cout : i] : 0.0f;
-    // pad units of every pixel row of the activation tiles (never written
-    // by the staging) are zero
-    if (STAGED)
-        for (int u = tid; u < kPwWaves * 32 * P; u += kPwThreads)
-            if ((u % P) * 8 >= cin) wl[rows * P + u] = make_uint4(0, 0, 0, 0);
-    __syncthreads();
+    const int rows = nmh * MB * 32;  // staged weight rows
 
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, (uint32_t)npix * (uint32_t)cin * 2u);
     const __amdgpu_buffer_rsrc_t yr = make_rsrc(y, (uint32_t)npix * (uint32_t)cout * 2u);
@@ -165,6 +138,42 @@ __global__ __launch_bounds__(kPwThreads, 2) void pw_kernel(const bf16_t* __restr
             }                                                                                \
         }                                                                                    \
     } while (0)
+
+#if PW_EARLY
+    // the first tile's activations go out before the weight staging, so the
+    // two memory latencies overlap
+    PW_LOAD(b0, w0);
+#endif
+    // stage the weights (rows past Cout and channels past Cin are zero) and
+    // the bias
+    {
+        // all loads first (zero for padding units), then the LDS stores, so
+        // the staging costs one memory latency
+        constexpr int kUnits = ((SHUF ? kPwMaxLdsShuf : kPwMaxLds) / 16 + kPwThreads - 1) / kPwThreads;
+        const __amdgpu_buffer_rsrc_t wr = make_rsrc(wp, (uint32_t)cout * (uint32_t)cin * 2u);
+        uint4 v[kUnits];
+#pragma unroll
+        for (int k = 0; k < kUnits; ++k) {
+            const int u = tid + k * kPwThreads;
+            const int r = u / P, c = u - r * P;
+            // pixel shuffle: LDS row (tap, co) is packed row co*kk + tap
+            const int gr = SHUF ? (r % sh.cout) * sh.kk + r / sh.cout : r;
+            v[k] = load16(wr, (u < rows * P && r < cout && c * 8 < cin) ? (gr * cin + c * 8) * 2 : kOOB);
+        }
+#pragma unroll
+        for (int k = 0; k < kUnits; ++k) {
+            const int u = tid + k * kPwThreads;
+            if (u < rows * P) wl[u] = v[k];
+        }
+    }
+    for (int i = tid; i < rows; i += kPwThreads)
+        sb[i] = (has_bias && i < cout) ? bias[SHUF ? i % sh.cout : i] : 0.0f;
+    // pad units of every pixel row of the activation tiles (never written
+    // by the staging) are zero
+    if (STAGED)
+        for (int u = tid; u < kPwWaves * 32 * P; u += kPwThreads)
+            if ((u % P) * 8 >= cin) wl[rows * P + u] = make_uint4(0, 0, 0, 0);
+    __syncthreads();
 
     // one tile: bias-initialised accumulators, KS x MB matrix ops, epilogue
 #define PW_TILE(B, I)                                                                        \
@@ -251,7 +260,9 @@ __global__ __launch_bounds__(kPwThreads, 2) void pw_kernel(const bf16_t* __restr
     // Two tiles per iteration so the two register sets alternate statically;
     // the loads of the tile after next go out before a tile is computed.
     int it = w0;
+#if !PW_EARLY
     PW_LOAD(b0, it);
+#endif
     for (; it < nitems; it += 2 * nw) {
         PW_LOAD(b1, it + nw);
         __builtin_amdgcn_sched_barrier(0);

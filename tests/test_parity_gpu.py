@@ -259,6 +259,34 @@ def test_direct_fp32_sweep(mode):
             check_f32(y, yref, s, np.abs(b)[None, :, None, None].astype(np.float64), f"fp32 case {k}")
 
 
+# 3x3 over at most four input channels per group (the unrolled small-K
+# direct kernel): (N, Cin, H, W, Cout, S, P, D, G), ragged pixel counts,
+# output channels not a multiple of the 8-channel block.
+SMALL_K_CASES = [(1, 3, 17, 23, 32, 2, 1, 1, 1), (2, 1, 9, 8, 8, 1, 1, 1, 1), (1, 2, 12, 7, 20, 1, 0, 2, 1),
+                 (1, 4, 15, 15, 16, 3, 2, 1, 1), (2, 4, 10, 11, 24, 1, 1, 1, 2), (1, 8, 9, 9, 16, 2, 1, 2, 4),
+                 (1, 3, 1, 1, 12, 1, 1, 1, 1), (3, 3, 33, 31, 8, 2, 1, 1, 1)]
+
+
+@pytest.mark.parametrize("dtype", [ci.F32, ci.BF16])
+@pytest.mark.parametrize("mode", ["random", "int"])
+def test_direct_small_k_sweep(dtype, mode):
+    """The small-K direct kernel through both entries (NHWC packed, NCHW)."""
+    c2.conv2d_set_path_override(c2.PATH_DIRECT)
+    for k, (N, Cin, H, W, Cout, S, P, D, G) in enumerate(SMALL_K_CASES):
+        for epi in (0, 1, 3):
+            x, w, b = ci.random_tensors(700 + k, N, Cin, H, W, Cout, 3, 3, G, dtype=dtype, mode=mode,
+                                        bias=epi & 1)
+            yref, s = oracle.conv2d(x, w, b, S, P, D, G, relu=bool(epi & 2))
+            for entry, run in (("nhwc", run_nhwc), ("nchw", run_nchw)):
+                say(f"[sweep] small-K direct {entry} {dtype} {mode} case {k} epi {epi}")
+                y = run(x, w, b, S, P, D, G, dtype, epi)
+                if mode == "int":
+                    want = yref if dtype == ci.F32 else oracle.round_to_bf16(yref)
+                    np.testing.assert_array_equal(y, want)
+                else:
+                    _compare(y, yref, s, b, dtype, f"small-K {entry} case {k}")
+
+
 # ------------------------------------------------------------------ NCHW entry
 
 @pytest.mark.parametrize("cid,li", [(1, 0), (2, 0), (3, 0), (3, 1), (4, 0), (5, 3)])
