@@ -11,7 +11,7 @@
 // Grid: x = blocks of 256 output pixels (n, ho, wo); y = group * channel
 // blocks.  All threads of a block share (group, channel block), so the weight
 // reads are wave-uniform and go through the scalar cache.
-#include "common.hpp"
+#include "mfma.hpp"
 #include "../../include/conv2d.h"
 
 namespace conv2d {
@@ -84,7 +84,10 @@ __global__ __launch_bounds__(kThreads) void direct_kernel(const T* __restrict__ 
 // generic loop above is one dependent global load per tap; here the taps are
 // unrolled, every input value of the window is requested at once (one memory
 // latency instead of CI*9), and the block's weights sit in LDS as
-// [tap][COB], read as broadcasts.
+// [tap][COB], read as broadcasts.  Work items are (pixel block, group and
+// channel block) with the channel blocks of one pixel block consecutive, and
+// each XCD takes one contiguous run of items, so the channel blocks that
+// share an input window read it through one L2.
 template <typename T, int XL, int WL, int YL, int CI, int COB, bool BIAS, bool RELU>
 __global__ __launch_bounds__(kThreads) void direct3x3_small_kernel(const T* __restrict__ x,
                                                                    const T* __restrict__ w,
@@ -93,8 +96,10 @@ __global__ __launch_bounds__(kThreads) void direct3x3_small_kernel(const T* __re
     constexpr int NT = CI * 9;  // taps per output
     __shared__ __align__(16) float ws[NT][COB];
     const int ncob = (s.cout_g + COB - 1) / COB;
-    const int g = blockIdx.y / ncob;
-    const int cb = blockIdx.y - g * ncob;
+    const int item = xcd_tile_index();
+    const int pb = item / (s.groups * ncob), gc = item - pb * (s.groups * ncob);
+    const int g = gc / ncob;
+    const int cb = gc - g * ncob;
     const int co_base = g * s.cout_g + cb * COB;
     const int nco = min(COB, s.cout_g - cb * COB);
     for (int i = threadIdx.x; i < NT * COB; i += kThreads) {
@@ -106,7 +111,7 @@ __global__ __launch_bounds__(kThreads) void direct3x3_small_kernel(const T* __re
     }
     __syncthreads();
     const int npix = s.N * s.Ho * s.Wo;
-    const int p = blockIdx.x * kThreads + threadIdx.x;
+    const int p = pb * kThreads + threadIdx.x;
     if (p >= npix) return;
     const int wo = p % s.Wo;
     const int t = p / s.Wo;
@@ -149,13 +154,18 @@ __global__ __launch_bounds__(kThreads) void direct3x3_small_kernel(const T* __re
     }
 }
 
+#ifndef DIRECT_SMALL_COB
+#define DIRECT_SMALL_COB 4
+#endif
+
 template <typename T, int XL, int WL, int YL, int CI>
 hipError_t launch_small(const Shape& s, const T* x, const T* w, const float* b, T* y, hipStream_t st) {
-    constexpr int COB = 8;
+    constexpr int COB = DIRECT_SMALL_COB;  // output channels per thread
     const int npix = s.N * s.Ho * s.Wo;
     const int ncob = (s.cout_g + COB - 1) / COB;
-    if ((long long)s.groups * ncob > 65535) return hipErrorInvalidConfiguration;
-    dim3 grid((npix + kThreads - 1) / kThreads, s.groups * ncob);
+    const long long items = (long long)((npix + kThreads - 1) / kThreads) * s.groups * ncob;
+    if (items > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    const dim3 grid((unsigned)items);
     const bool bias = s.epilogue & CONV2D_EPI_BIAS, relu = s.epilogue & CONV2D_EPI_RELU;
 #define SMALL_LAUNCH(B_, R_)                                                                 \
     hipLaunchKernelGGL((direct3x3_small_kernel<T, XL, WL, YL, CI, COB, B_, R_>), grid, dim3(kThreads), 0, st, x, w, \

@@ -43,10 +43,6 @@ constexpr int kPwMaxLdsShuf = 72 * 1024;  // staged weights in pixel-shuffle mod
 // Pixel-shuffle mode: activations through LDS (one workgroup per CU: 72 KB
 // of weights plus the tiles) or straight into operand registers; overridable
 // at build time for tuning.
-// The first tile's activation loads are issued before the weight staging.
-#ifndef PW_EARLY
-#define PW_EARLY 1
-#endif
 #ifndef PW_SHUF_STAGED
 #define PW_SHUF_STAGED 0
 #endif
@@ -61,6 +57,24 @@ struct PwShuf {
 // bank conflicts), and at least two units per 16-channel slice, so the last
 // slice's second half is a zero pad unit inside the row when Cin % 16 == 8.
 __host__ __device__ constexpr int pw_pitch(int cin) { return (2 * ((cin + 15) / 16)) | 1; }
+
+// Work items in flight per wave: register sets of KS 16-byte units each, as
+// many as fit beside the accumulators (overridable at build time for tuning).
+#ifndef PW_DEPTH4
+#define PW_DEPTH4 6
+#endif
+#ifndef PW_DEPTH8
+#define PW_DEPTH8 2
+#endif
+#ifndef PW_DEPTH12
+#define PW_DEPTH12 2
+#endif
+#ifndef PW_DEPTH16
+#define PW_DEPTH16 2
+#endif
+constexpr int pw_depth(int ks) {
+    return ks <= 4 ? PW_DEPTH4 : ks <= 8 ? PW_DEPTH8 : ks <= 12 ? PW_DEPTH12 : PW_DEPTH16;
+}
 
 // MB: 32-row blocks of output channels per work item; KS: 16-channel slices
 // of the input (Cin <= 16*KS).  A work item is one 32-pixel tile and one
@@ -101,8 +115,10 @@ __global__ __launch_bounds__(kPwThreads, 2) void pw_kernel(const bf16_t* __restr
     const int nw = gridDim.x * (kPwThreads / 64);
     const int w0 = blockIdx.x * (kPwThreads / 64) + wave;
     const int nitems = ntiles * nmh;
+    constexpr int PD = pw_depth(KS);
+    static_assert(PD >= 2, "at least one item ahead");
 
-    uint4 b0[KS], b1[KS];
+    uint4 bs[PD][KS];  // register sets of the items in flight
     f32x16 acc[MB];
 
     // STAGED: activations of item I's tile as units u = 64 k + lane of the
@@ -139,11 +155,10 @@ __global__ __launch_bounds__(kPwThreads, 2) void pw_kernel(const bf16_t* __restr
         }                                                                                    \
     } while (0)
 
-#if PW_EARLY
-    // the first tile's activations go out before the weight staging, so the
-    // two memory latencies overlap
-    PW_LOAD(b0, w0);
-#endif
+    // the first PD-1 items' activations go out before the weight staging, so
+    // the two memory latencies overlap
+#pragma unroll
+    for (int d = 0; d + 1 < PD; ++d) PW_LOAD(bs[d], w0 + d * nw);
     // stage the weights (rows past Cout and channels past Cin are zero) and
     // the bias
     {
@@ -257,20 +272,18 @@ __global__ __launch_bounds__(kPwThreads, 2) void pw_kernel(const bf16_t* __restr
         }                                                                                    \
     } while (0)
 
-    // Two tiles per iteration so the two register sets alternate statically;
-    // the loads of the tile after next go out before a tile is computed.
-    int it = w0;
-#if !PW_EARLY
-    PW_LOAD(b0, it);
-#endif
-    for (; it < nitems; it += 2 * nw) {
-        PW_LOAD(b1, it + nw);
-        __builtin_amdgcn_sched_barrier(0);
-        PW_TILE(b0, it);
-        if (it + nw >= nitems) break;
-        PW_LOAD(b0, it + 2 * nw);
-        __builtin_amdgcn_sched_barrier(0);
-        PW_TILE(b1, it + nw);
+    // PD items per iteration so the register sets rotate statically: before
+    // an item is computed, the loads of the item PD-1 steps later go out into
+    // the set the previous item has just freed.
+    for (int it = w0; it < nitems; it += PD * nw) {
+#pragma unroll
+        for (int d = 0; d < PD; ++d) {
+            const int cur = it + d * nw;
+            if (cur >= nitems) break;
+            PW_LOAD(bs[(d + PD - 1) % PD], cur + (PD - 1) * nw);
+            __builtin_amdgcn_sched_barrier(0);
+            PW_TILE(bs[d], cur);
+        }
     }
 #undef PW_LOAD
 #undef PW_STAGE
