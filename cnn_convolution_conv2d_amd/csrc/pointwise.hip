@@ -39,7 +39,10 @@ constexpr int kPwThreads = 256;
 constexpr int kPwWaves = kPwThreads / 64;
 constexpr int kPwMaxLds = 64 * 1024;  // bytes of staged weights
 constexpr int kPwMaxCout = 256;
-constexpr int kPwMaxLdsShuf = 72 * 1024;  // staged weights in pixel-shuffle mode (256 rows x 17 units)
+constexpr int kPwMaxLdsShuf = 72 * 1024;
+// How a wave's activations reach the matrix ops: straight into operand
+// registers, through a whole tile in LDS, or through half tiles in LDS.
+constexpr int kPwDirect = 0, kPwStaged = 1, kPwHalf = 2;  // staged weights in pixel-shuffle mode (256 rows x 17 units)
 // Pixel-shuffle mode: activations through LDS (one workgroup per CU: 72 KB
 // of weights plus the tiles) or straight into operand registers; overridable
 // at build time for tuning.
@@ -80,7 +83,7 @@ constexpr int pw_depth(int ks) {
 // of the input (Cin <= 16*KS).  A work item is one 32-pixel tile and one
 // group of MB*32 output channels (nmh groups cover Cout); the items of one
 // tile are consecutive, so the later ones find its activations in cache.
-template <int MB, int KS, bool STAGED, bool SHUF>
+template <int MB, int KS, int STG, bool SHUF>
 __global__ __launch_bounds__(kPwThreads, 2) void pw_kernel(const bf16_t* __restrict__ x,
                                                        const bf16_t* __restrict__ wp,
                                                        const float* __restrict__ bias,
@@ -92,8 +95,12 @@ __global__ __launch_bounds__(kPwThreads, 2) void pw_kernel(const bf16_t* __restr
     // [32 pixels][P units] per wave
     extern __shared__ uint4 pw_lds[];
     __shared__ __align__(16) float sb[kPwMaxCout];
+    constexpr bool STAGED = STG == kPwStaged, HALF = STG == kPwHalf;
+    static_assert(!HALF || KS % 2 == 0, "half tiles of whole 16-channel slices");
+    constexpr int PH = KS + 1;  // HALF: pitch of a half-tile pixel row (odd)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int P = pw_pitch(cin);
+    const int XP = HALF ? PH : P;  // pitch of the wave's activation tile
     uint4* const wl = pw_lds;
     const int rows = nmh * MB * 32;  // staged weight rows
 
@@ -103,8 +110,8 @@ __global__ __launch_bounds__(kPwThreads, 2) void pw_kernel(const bf16_t* __restr
     // weight operand: row frow of block mb, 16-byte chunk 2s + h
     const char* const a_base = reinterpret_cast<const char*>(wl) + (frow * P + h) * 16;
     // this wave's activation tile; operand of slice s: pixel frow, chunk 2s + h
-    char* const xt = reinterpret_cast<char*>(wl + rows * P + wave * 32 * P);
-    const char* const b_base = xt + (frow * P + h) * 16;
+    char* const xt = reinterpret_cast<char*>(wl + rows * P + wave * 32 * XP);
+    const char* const b_base = xt + (frow * XP + h) * 16;
     const int cin8 = cin / 8, tunits = 32 * cin8;  // 16-byte units of one tile
     // epilogue: this lane's 16-byte piece holds channels cl .. cl+7 of a
     // 32-channel block, of pixel 16*e + lane % 16 (e = 0, 1) of the tile
@@ -123,9 +130,12 @@ __global__ __launch_bounds__(kPwThreads, 2) void pw_kernel(const bf16_t* __restr
 
     // STAGED: activations of item I's tile as units u = 64 k + lane of the
     // tile's contiguous run (coalesced), later written to the wave's tile in
-    // LDS.  Otherwise: straight into operand layout, k = slice, lane l holding
-    // channels 16k + 8 (l / 32) .. +7 of pixel l % 32.  Zero past the image or
-    // past Cin.
+    // LDS.  HALF (Cin = 16 KS): loads k < KS/2 cover the first KS units
+    // (Cin/2 channels) of every pixel of the tile, the others the second KS
+    // units, 64 consecutive units of such half rows per load (whole 128-byte
+    // lines).  Otherwise: straight into operand layout, k = slice, lane l
+    // holding channels 16k + 8 (l / 32) .. +7 of pixel l % 32.  Zero past the
+    // image or past Cin.
 #define PW_LOAD(B, I)                                                                        \
     do {                                                                                     \
         const int p0_ = ((I) / nmh) * 32;                                                    \
@@ -136,6 +146,11 @@ __global__ __launch_bounds__(kPwThreads, 2) void pw_kernel(const bf16_t* __restr
                 const int pl_ = (u_ * cin8_magic) >> 16;                                     \
                 const bool ok_ = tin_ && u_ < tunits && p0_ + pl_ < npix;                    \
                 (B)[k] = load16(xr, ok_ ? (p0_ * cin + u_ * 8) * 2 : kOOB);                  \
+            } else if (HALF) {                                                               \
+                const int hf_ = k / (KS / 2), uh_ = (k - hf_ * (KS / 2)) * 64 + lane;        \
+                const int pl_ = uh_ / KS, c_ = uh_ - pl_ * KS + hf_ * KS;                    \
+                const bool ok_ = tin_ && p0_ + pl_ < npix;                                   \
+                (B)[k] = load16(xr, ok_ ? ((p0_ + pl_) * cin + c_ * 8) * 2 : kOOB);          \
             } else {                                                                         \
                 const bool ok_ = tin_ && p0_ + frow < npix && k * 16 + 8 * h < cin;          \
                 (B)[k] = load16(xr, ok_ ? ((p0_ + frow) * cin + k * 16 + 8 * h) * 2 : kOOB); \
@@ -152,6 +167,18 @@ __global__ __launch_bounds__(kPwThreads, 2) void pw_kernel(const bf16_t* __restr
                 if (u_ < tunits)                                                             \
                     *reinterpret_cast<uint4*>(xt + (pl_ * P + u_ - pl_ * cin8) * 16) = (B)[k]; \
             }                                                                                \
+        }                                                                                    \
+    } while (0)
+
+    // HALF: half HF of the loaded units into the wave's tile (pixel rows of KS
+    // units at the odd pitch PH); in-order LDS access within the wave lets it
+    // overwrite the other half once that half's operands have been read
+#define PW_STAGE_HALF(B, HF)                                                                 \
+    do {                                                                                     \
+        _Pragma("unroll") for (int k = 0; k < KS / 2; ++k) {                                 \
+            const int uh_ = k * 64 + lane;                                                   \
+            const int pl_ = uh_ / KS;                                                        \
+            *reinterpret_cast<uint4*>(xt + (pl_ * PH + uh_ - pl_ * KS) * 16) = (B)[(HF) * (KS / 2) + k]; \
         }                                                                                    \
     } while (0)
 
@@ -206,7 +233,9 @@ __global__ __launch_bounds__(kPwThreads, 2) void pw_kernel(const bf16_t* __restr
         /* slices past Cin are skipped: their weight reads would run past a row */          \
         _Pragma("unroll") for (int s = 0; s < KS; ++s) {                                     \
             if (s * 16 < cin) {                                                              \
+                if (HALF && s % (KS / 2) == 0) PW_STAGE_HALF(B, s / (KS / 2));               \
                 const bf16x8 b_ = STAGED ? *reinterpret_cast<const bf16x8*>(b_base + 2 * s * 16) \
+                                  : HALF ? *reinterpret_cast<const bf16x8*>(b_base + 2 * (s % (KS / 2)) * 16) \
                                          : __builtin_bit_cast(bf16x8, (B)[s]);               \
                 _Pragma("unroll") for (int mb = 0; mb < MB; ++mb) {                          \
                     const bf16x8 a_ = *reinterpret_cast<const bf16x8*>(a_base + ((c0_ + mb * 32) * P + 2 * s) * 16); \
@@ -287,18 +316,31 @@ __global__ __launch_bounds__(kPwThreads, 2) void pw_kernel(const bf16_t* __restr
     }
 #undef PW_LOAD
 #undef PW_STAGE
+#undef PW_STAGE_HALF
 #undef PW_TILE
 }
 
-// LDS bytes of one workgroup: weights plus one activation tile per wave.
-long long pw_lds_bytes(int cin, int rows, bool staged) {
-    return (long long)(rows + (staged ? kPwWaves * 32 : 0)) * pw_pitch(cin) * 16;
+// LDS bytes of one workgroup: weights plus one activation tile (or half
+// tile) per wave.
+long long pw_lds_bytes(int cin, int rows, int stg) {
+    const long long w = (long long)rows * pw_pitch(cin) * 16;
+    if (stg == kPwStaged) return w + (long long)kPwWaves * 32 * pw_pitch(cin) * 16;
+    if (stg == kPwHalf) return w + (long long)kPwWaves * 32 * (cin / 16 + 1) * 16;
+    return w;
 }
 
 // Activations through LDS (coalesced 1 KB loads) for narrow inputs and wide
-// outputs, where it was measured faster; straight into operand registers
-// otherwise (wide inputs keep two workgroups per CU that way).
-bool pw_staged(int cin, int cout) { return cin <= 128 && cout >= 128; }
+// outputs, where it was measured faster; for 192 or 256 input channels in
+// half tiles (whole-line loads, and the LDS of half a tile keeps two
+// workgroups per CU); straight into operand registers otherwise.
+#ifndef PW_HALF
+#define PW_HALF 1
+#endif
+int pw_stage_mode(int cin, int cout) {
+    if (cin <= 128 && cout >= 128) return kPwStaged;
+    if (PW_HALF && (cin == 192 || cin == 256)) return kPwHalf;
+    return kPwDirect;
+}
 
 // One launch: npix rows of the activation matrix, cin channels, cout GEMM
 // rows (output channels, or (tap, channel) rows in pixel-shuffle mode).
@@ -309,23 +351,23 @@ struct PwArgs {
     PwShuf sh;
 };
 
-template <int MB, int KS, bool STAGED, bool SHUF>
+template <int MB, int KS, int STG, bool SHUF>
 hipError_t launch_pw(const PwArgs& a, const bf16_t* x, const bf16_t* w, const float* b, bf16_t* y,
                      hipStream_t st) {
-    auto kern = pw_kernel<MB, KS, STAGED, SHUF>;
+    auto kern = pw_kernel<MB, KS, STG, SHUF>;
     const int npix = a.npix;
     const int ntiles = (npix + 31) / 32;
     const int nmh = (a.cout + MB * 32 - 1) / (MB * 32);
-    const long long lds = pw_lds_bytes(a.cin, nmh * MB * 32, STAGED);
+    const long long lds = pw_lds_bytes(a.cin, nmh * MB * 32, STG);
     // unit -> pixel of a tile: (u * magic) >> 16 == u / (Cin/8) for u < 32*Cin/8
     const int cin8 = a.cin / 8, magic = (65536 + cin8 - 1) / cin8;
     int dev = 0;
     (void)hipGetDevice(&dev);
     if (lds > 64 * 1024) {
-        const hipError_t ea = ensure_dynamic_lds<pw_kernel<MB, KS, STAGED, SHUF>>((int)lds, dev);
+        const hipError_t ea = ensure_dynamic_lds<pw_kernel<MB, KS, STG, SHUF>>((int)lds, dev);
         if (ea != hipSuccess) return ea;
     }
-    const int by_regs = blocks_per_cu<pw_kernel<MB, KS, STAGED, SHUF>>(kPwThreads, dev);
+    const int by_regs = blocks_per_cu<pw_kernel<MB, KS, STG, SHUF>>(kPwThreads, dev);
     const int by_lds = (int)(163840 / (lds + kPwMaxCout * 4));
     const int bpc = by_lds < by_regs ? (by_lds < 1 ? 1 : by_lds) : by_regs;
     // at most two workgroups per CU: with more, the waves' activation streams
@@ -340,22 +382,32 @@ hipError_t launch_pw(const PwArgs& a, const bf16_t* x, const bf16_t* w, const fl
     return hipGetLastError();
 }
 
-template <int MB, bool STAGED, bool SHUF>
+template <int MB, int STG, bool SHUF>
 hipError_t launch_pw_ks(const PwArgs& a, const bf16_t* x, const bf16_t* w, const float* b, bf16_t* y,
                         hipStream_t st) {
     const int ks = (a.cin + 15) / 16;
-    if (ks <= 4) return launch_pw<MB, 4, STAGED, SHUF>(a, x, w, b, y, st);
-    if (ks <= 8) return launch_pw<MB, 8, STAGED, SHUF>(a, x, w, b, y, st);
-    if (ks <= 12) return launch_pw<MB, 12, STAGED, SHUF>(a, x, w, b, y, st);
-    if constexpr (MB <= 2 && !STAGED) return launch_pw<MB, 16, STAGED, SHUF>(a, x, w, b, y, st);
-    return hipErrorInvalidValue;  // more than 192 input channels: at most two blocks, not staged
+    if constexpr (STG == kPwHalf) {
+        // half tiles: Cin exactly 16 KS with KS even
+        if (a.cin == 192) return launch_pw<MB, 12, STG, SHUF>(a, x, w, b, y, st);
+        if constexpr (MB <= 2)
+            if (a.cin == 256) return launch_pw<MB, 16, STG, SHUF>(a, x, w, b, y, st);
+        return hipErrorInvalidValue;
+    } else {
+        if (ks <= 4) return launch_pw<MB, 4, STG, SHUF>(a, x, w, b, y, st);
+        if (ks <= 8) return launch_pw<MB, 8, STG, SHUF>(a, x, w, b, y, st);
+        if (ks <= 12) return launch_pw<MB, 12, STG, SHUF>(a, x, w, b, y, st);
+        if constexpr (MB <= 2 && STG == kPwDirect) return launch_pw<MB, 16, STG, SHUF>(a, x, w, b, y, st);
+        return hipErrorInvalidValue;  // more than 192 input channels: at most two blocks, not staged
+    }
 }
 
 template <int MB>
 hipError_t launch_pw_mb(const PwArgs& a, const bf16_t* x, const bf16_t* w, const float* b, bf16_t* y,
                         hipStream_t st) {
-    if (pw_staged(a.cin, a.cout)) return launch_pw_ks<MB, true, false>(a, x, w, b, y, st);
-    return launch_pw_ks<MB, false, false>(a, x, w, b, y, st);
+    const int stg = pw_stage_mode(a.cin, a.cout);
+    if (stg == kPwStaged) return launch_pw_ks<MB, kPwStaged, false>(a, x, w, b, y, st);
+    if (stg == kPwHalf) return launch_pw_ks<MB, kPwHalf, false>(a, x, w, b, y, st);
+    return launch_pw_ks<MB, kPwDirect, false>(a, x, w, b, y, st);
 }
 
 }  // namespace
@@ -376,7 +428,7 @@ bool pointwise_supports(const Shape& s) {
     return s.Kh == 1 && s.Kw == 1 && s.stride == 1 && s.pad == 0 && s.groups == 1 && s.dtype == CONV2D_BF16 &&
            s.Cin % 8 == 0 && s.Cin <= 256 && s.Cout % 4 == 0 && s.Cout <= kPwMaxCout &&
            rows * pw_pitch(s.Cin) * 16 <= kPwMaxLds &&
-           pw_lds_bytes(s.Cin, (int)rows, pw_staged(s.Cin, s.Cout)) + kPwMaxCout * 4 <= 163840 &&
+           pw_lds_bytes(s.Cin, (int)rows, pw_stage_mode(s.Cin, s.Cout)) + kPwMaxCout * 4 <= 163840 &&
            npix * s.Cin * 2 < 0x7fff0000LL && npix * s.Cout * 2 < 0x7fff0000LL;
 }
 
@@ -411,7 +463,7 @@ bool pw_shuffle_supports(const Shape& s) {
     return s.dtype == CONV2D_BF16 && s.groups == 1 && s.Kh == s.stride && s.Kw == s.stride && s.stride > 1 &&
            s.pad == 0 && s.out_pad == 0 && s.dil == 1 && s.Cin % 8 == 0 && s.Cin <= 256 && s.Cout % 32 == 0 &&
            rows <= kPwMaxCout && rows * pw_pitch(s.Cin) * 16 <= kPwMaxLdsShuf &&
-           pw_lds_bytes(s.Cin, (int)rows, false) + kPwMaxCout * 4 <= 163840 && npix * s.Cin * 2 < 0x7fff0000LL &&
+           pw_lds_bytes(s.Cin, (int)rows, kPwDirect) + kPwMaxCout * 4 <= 163840 && npix * s.Cin * 2 < 0x7fff0000LL &&
            (long long)s.N * s.Ho * s.Wo * s.Cout * 2 < 0x7fff0000LL;
 }
 
@@ -431,7 +483,7 @@ hipError_t launch_pw_shuffle(const Shape& s, const void* x, const void* w_packed
     a.shift = nullptr;
     a.sh = PwShuf{s.Cout, s.Kh * s.Kw, s.Kw, s.stride, s.H, s.W, s.Ho, s.Wo};
     const int mb = pw_blocks(a.cin, a.cout);
-    constexpr bool kStaged = PW_SHUF_STAGED != 0;
+    constexpr int kStaged = PW_SHUF_STAGED != 0 ? kPwStaged : kPwDirect;
     if (pw_lds_bytes(a.cin, (a.cout + 127) / 128 * 128, kStaged) + kPwMaxCout * 4 > 163840)
         return hipErrorInvalidValue;
     if (mb == 1) return launch_pw_ks<1, kStaged, true>(a, xt, wt, bias, yt, st);

@@ -187,6 +187,9 @@ def _sweep():
         (1, 144, 7, 9, 24, 1, 1, 1, 0, 1, 1), (1, 32, 5, 5, 20, 1, 1, 1, 0, 1, 1),
         (16, 16, 64, 70, 16, 1, 1, 1, 0, 1, 1), (1, 264, 3, 5, 16, 1, 1, 1, 0, 1, 1),
         (1, 16, 4, 6, 272, 1, 1, 1, 0, 1, 1), (2, 40, 9, 7, 136, 1, 1, 1, 0, 1, 1),
+        # 192 and 256 input channels: activations through half tiles in LDS
+        (1, 192, 7, 13, 96, 1, 1, 1, 0, 1, 1), (2, 256, 5, 7, 40, 1, 1, 1, 0, 1, 1),
+        (1, 192, 3, 11, 256, 1, 1, 1, 0, 1, 1),
     ]
     return cases
 
