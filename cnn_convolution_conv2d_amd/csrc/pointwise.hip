@@ -329,16 +329,19 @@ long long pw_lds_bytes(int cin, int rows, int stg) {
     return w;
 }
 
-// Activations through LDS (coalesced 1 KB loads) for narrow inputs and wide
-// outputs, where it was measured faster; for 192 or 256 input channels in
-// half tiles (whole-line loads, and the LDS of half a tile keeps two
-// workgroups per CU); straight into operand registers otherwise.
-#ifndef PW_HALF
-#define PW_HALF 1
-#endif
+// How the activations reach the matrix ops (each choice measured against
+// the others on the workload layers):
+//  * whole tiles through LDS (coalesced 1 KB loads) for narrow inputs with
+//    wide outputs, and for 129..191 input channels with at most 64 outputs
+//    (the 144 -> 24 layer: the weights are small, so two workgroups per CU
+//    still fit);
+//  * half tiles through LDS for 192 or 256 input channels (whole-line loads;
+//    half a tile keeps two workgroups per CU beside the weights);
+//  * straight into operand registers otherwise.
 int pw_stage_mode(int cin, int cout) {
     if (cin <= 128 && cout >= 128) return kPwStaged;
-    if (PW_HALF && (cin == 192 || cin == 256)) return kPwHalf;
+    if (cin == 192 || cin == 256) return kPwHalf;
+    if (cin > 128 && cin < 192 && cout <= 64) return kPwStaged;
     return kPwDirect;
 }
 
