@@ -437,8 +437,8 @@ def main(argv=None):
     a = ap.parse_args(argv)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {a.gpus}, WORLD_SIZE "
-              f"{world}); a multi-GPU split of the batch is not built.",
+        print(f"bench.py: the library and this benchmark use one GPU (asked for --gpus {a.gpus}, "
+              f"WORLD_SIZE {world}); a multi-GPU split of the batch is not implemented.",
               file=sys.stderr)
         return 2
     import torch

@@ -543,8 +543,8 @@ __device__ __forceinline__ void tile_epilogue(f32x16 (&acc)[TM][TN], const char*
             for (int h = 0; h < 2; ++h) {
                 const int off = (pix[j][h] + tc.g * s.cout_g + co) * 2;
                 if (vec16) {
-                    store16(yr, pix[j][h] >= 0 && co < s.cout_g ? off : kOOB,
-                            make_uint4(out[h][0], out[h][1], out[h][2], out[h][3]));
+                    store16<kStoreStream>(yr, pix[j][h] >= 0 && co < s.cout_g ? off : kOOB,
+                                          make_uint4(out[h][0], out[h][1], out[h][2], out[h][3]));
                 } else {
                     store8(yr, pix[j][h] >= 0 && co < s.cout_g ? off : kOOB, make_uint2(out[h][0], out[h][1]));
                     store8(yr, pix[j][h] >= 0 && co + 4 < s.cout_g ? off + 8 : kOOB, make_uint2(out[h][2], out[h][3]));

@@ -31,15 +31,24 @@ __device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, int byte_off, 
 }
 
 // Buffer stores: an offset past the descriptor's size drops the store, so
-// out-of-range pixels and channels need no branch.
+// out-of-range pixels and channels need no branch.  POLICY is the
+// instruction's cache-policy field: 0, or kStoreStream for output written
+// once and not read again by the kernel (the nt bit: the lines do not
+// displace the inputs the kernel re-reads from L2).  Streaming measured
+// faster for epilogues that write 64 contiguous bytes per pixel per
+// instruction and much slower for scattered 8-byte pieces.
+constexpr int kStoreStream = 2;
+
+template <int POLICY = 0>
 __device__ __forceinline__ void store16(__amdgpu_buffer_rsrc_t r, int byte_off, uint4 v) {
     typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, byte_off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, byte_off, 0, POLICY);
 }
 
+template <int POLICY = 0>
 __device__ __forceinline__ void store8(__amdgpu_buffer_rsrc_t r, int byte_off, uint2 v) {
     typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, byte_off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, byte_off, 0, POLICY);
 }
 
 // The folded batch-normalisation step of an epilogue: v = v * scale[c] +

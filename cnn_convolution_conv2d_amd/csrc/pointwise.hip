@@ -117,6 +117,11 @@ __global__ __launch_bounds__(kPwThreads, 2) void pw_kernel(const bf16_t* __restr
     // 32-channel block, of pixel 16*e + lane % 16 (e = 0, 1) of the tile
     const int cl = ((lane >> 4) & 1) * 16 + h * 8;
     const bool vec16 = cout % 8 == 0;
+    // streaming stores (measured): faster for the pixel-shuffle epilogue and
+    // for outputs narrower than 64 channels, slower for the plain 64- and
+    // 256-channel layers, where the lines written by two store instructions
+    // then leave L2 as separate partial writes
+    const bool stream = SHUF || cout < 64;
     const Affine4 aff(scale, shift, cout);  // folded batch normalisation, when scale is given
 
     const int nw = gridDim.x * (kPwThreads / 64);
@@ -290,8 +295,10 @@ __global__ __launch_bounds__(kPwThreads, 2) void pw_kernel(const bf16_t* __restr
             _Pragma("unroll") for (int e = 0; e < 2; ++e) {                                  \
                 const int off_ = SHUF ? ((pix_[e] + tapoff_) * sh.cout + cc_) * 2 : (pix_[e] + co_) * 2; \
                 if (vec16) {                                                                 \
-                    store16(yr, pix_[e] >= 0 && co_ < cout ? off_ : kOOB,                    \
-                            make_uint4(o_[e][0], o_[e][1], o_[e][2], o_[e][3]));             \
+                    const int so_ = pix_[e] >= 0 && co_ < cout ? off_ : kOOB;                \
+                    const uint4 ov_ = make_uint4(o_[e][0], o_[e][1], o_[e][2], o_[e][3]);    \
+                    if (stream) store16<kStoreStream>(yr, so_, ov_);                         \
+                    else store16(yr, so_, ov_);                                              \
                 } else {                                                                     \
                     store8(yr, pix_[e] >= 0 && co_ < cout ? off_ : kOOB, make_uint2(o_[e][0], o_[e][1])); \
                     store8(yr, pix_[e] >= 0 && co_ + 4 < cout ? off_ + 8 : kOOB,             \
