@@ -358,7 +358,11 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(const bf16_t* __restric
         }
         bf16_t* dst = y + (size_t)opix * s.Cout + g * s.cout_g + co;
         if (vec16 && co + 8 <= s.cout_g) {
-            *reinterpret_cast<uint4*>(dst) = v;
+            // streaming (nt) store: written once, never read here; keeps the
+            // L2 for the input rows neighbouring tiles re-read (measured
+            // 34.5 -> 33.3 us on the 3x3 stride-2 128->128 layer)
+            typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+            __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, v), reinterpret_cast<u32x4_t*>(dst));
         } else {
             *reinterpret_cast<uint2*>(dst) = make_uint2(v.x, v.y);
             if (co + 8 <= s.cout_g) *reinterpret_cast<uint2*>(dst + 4) = make_uint2(v.z, v.w);
