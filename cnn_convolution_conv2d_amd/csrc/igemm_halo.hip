@@ -730,6 +730,11 @@ void halo3_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ wp, c
 #pragma unroll
         for (int j = 0; j < TN; ++j) bf0[j] = *reinterpret_cast<const bf16x8*>(bb + j * JSTRIDE);
     }
+    // Nothing of the prologue stays in flight into the tile loop: the
+    // compiler merges the loop's entry and back-edge states, and a prologue
+    // load still pending at the entry made it wait at every tile start for
+    // all but the last few epilogue stores of the previous tile.
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
 
     // One tap T (a literal 0..8) of the current chunk.
 #define TAPOFF(T) ((((T) / 3) * DIL * HWd + ((T) % 3) * DIL) * (kHP * 16))
