@@ -513,7 +513,7 @@ __device__ __forceinline__ void tile_epilogue(f32x16 (&acc)[TM][TN], const char*
             for (int q = 0; q < 4; ++q) {
                 float v[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * q + r] + (&b4[q].x)[r];
+                for (int r = 0; r < 4; ++r) v[r] = BIAS ? acc[i][j][4 * q + r] + (&b4[q].x)[r] : acc[i][j][4 * q + r];
                 if (s.scale) aff.apply(v, cga + i * 32 + 8 * q + 4 * half);
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
