@@ -353,17 +353,71 @@ __global__ __launch_bounds__(kThThreads, 1) void tconv_halo_kernel(const bf16_t*
     // epilogue: lane holds position (r, lane % 32), output channels
     // 8q + 4*(lane/32) + (0..3) in acc[r][4q + 0..3]
     const __amdgpu_buffer_rsrc_t br = make_rsrc(bias, BIAS ? (uint32_t)g.Cout * 4u : 0u);
+    float4 b4[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int co = co0 + 8 * q + 4 * (lane >> 5);
+        b4[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (BIAS) b4[q] = __builtin_bit_cast(float4, load16(br, co < g.Cout ? co * 4 : kOOB));
+    }
+    if (g.Cout % 8 == 0) {
+        // Two lane swaps regroup a row's 32 x 32 block so that each lane holds
+        // 8 consecutive channels (16 bytes) of one position: channels
+        // co0 + cl .. +7 of position 16*h + lane % 16 (h = 0, 1), and one
+        // store instruction writes 64 contiguous bytes of each of 16 pixels,
+        // with the streaming (nt) policy (measured 46.1 -> 39.7 us on the
+        // 4x4 stride-2 256->128 layer against 8-byte stores).
+        const int cl = ((lane >> 4) & 1) * 16 + (lane >> 5) * 8;
+#pragma unroll
+        for (int r = 0; r < kThRows; ++r) {
+            const int oh = 2 * (u0 + r0 + r) + ph_h;
+            uint32_t pk[4][2];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float v[4] = {acc[r][4 * q] + b4[q].x, acc[r][4 * q + 1] + b4[q].y, acc[r][4 * q + 2] + b4[q].z,
+                              acc[r][4 * q + 3] + b4[q].w};
+                if (RELU)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) v[i] = fmaxf(v[i], 0.0f);
+                pk[q][0] = pack_bf16x2(v[0], v[1]);
+                pk[q][1] = pack_bf16x2(v[2], v[3]);
+            }
+            uint32_t r8[2][4];
+#pragma unroll
+            for (int pr = 0; pr < 2; ++pr)
+#pragma unroll
+                for (int w = 0; w < 2; ++w) {
+                    const auto sw = __builtin_amdgcn_permlane32_swap(pk[2 * pr][w], pk[2 * pr + 1][w], false, false);
+                    r8[pr][w] = sw[0];
+                    r8[pr][2 + w] = sw[1];
+                }
+            uint32_t out[2][4];
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const auto sw = __builtin_amdgcn_permlane16_swap(r8[0][d], r8[1][d], false, false);
+                out[0][d] = sw[0];
+                out[1][d] = sw[1];
+            }
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int ow = 2 * (v0 + 16 * h + (lane & 15)) + ph_w;
+                const int co = co0 + cl;
+                const bool ok = oh < g.Ho && ow < g.Wo && co < g.Cout;
+                store16<kStoreStream>(yr, ok ? (((n * g.Ho + oh) * g.Wo + ow) * g.Cout + co) * 2 : kOOB,
+                                      make_uint4(out[h][0], out[h][1], out[h][2], out[h][3]));
+            }
+        }
+        return;
+    }
     const int ow = 2 * (v0 + (lane & 31)) + ph_w;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int co = co0 + 8 * q + 4 * (lane >> 5);
-        float4 b4 = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (BIAS) b4 = __builtin_bit_cast(float4, load16(br, co < g.Cout ? co * 4 : kOOB));
 #pragma unroll
         for (int r = 0; r < kThRows; ++r) {
             const int oh = 2 * (u0 + r0 + r) + ph_h;
-            float v[4] = {acc[r][4 * q] + b4.x, acc[r][4 * q + 1] + b4.y, acc[r][4 * q + 2] + b4.z,
-                          acc[r][4 * q + 3] + b4.w};
+            float v[4] = {acc[r][4 * q] + b4[q].x, acc[r][4 * q + 1] + b4[q].y, acc[r][4 * q + 2] + b4[q].z,
+                          acc[r][4 * q + 3] + b4[q].w};
             if (RELU)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) v[i] = fmaxf(v[i], 0.0f);
