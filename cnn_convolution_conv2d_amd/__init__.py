@@ -37,7 +37,7 @@ EXPORTS = ("conv2d_fwd", "conv2d_fwd_nhwc_packed", "conv2d_fwd_bn", "conv2d_fwd_
            "conv2d_packed_weight_bytes",
            "conv2d_pack_weights", "conv2d_nchw_to_nhwc", "conv2d_nhwc_to_nchw",
            "conv2d_out_dim", "conv2d_check_args", "conv2d_select_path",
-           "conv2d_set_path_override", "conv2d_release_scratch", "conv2d_strerror",
+           "conv2d_set_path_override", "conv2d_set_grid_limit", "conv2d_release_scratch", "conv2d_strerror",
            "conv2d_last_error")
 
 
@@ -91,6 +91,7 @@ def _load() -> ctypes.CDLL:
     lib.conv2d_check_args.argtypes, lib.conv2d_check_args.restype = [P, P, P, P] + [I] * 13, I
     lib.conv2d_select_path.argtypes, lib.conv2d_select_path.restype = [I] * 12, I
     lib.conv2d_set_path_override.argtypes, lib.conv2d_set_path_override.restype = [I], I
+    lib.conv2d_set_grid_limit.argtypes, lib.conv2d_set_grid_limit.restype = [I], I
     lib.conv2d_release_scratch.argtypes, lib.conv2d_release_scratch.restype = [], None
     lib.conv2d_strerror.argtypes, lib.conv2d_strerror.restype = [I], ctypes.c_char_p
     lib.conv2d_last_error.argtypes, lib.conv2d_last_error.restype = [], ctypes.c_char_p
@@ -267,6 +268,10 @@ def conv2d_select_path(N, Cin, H, W, Cout, Kh, Kw, stride, pad, dilation, groups
 
 def conv2d_set_path_override(path: int) -> int:
     return _check(int(lib.conv2d_set_path_override(path)), "conv2d_set_path_override")
+
+
+def conv2d_set_grid_limit(max_workgroups: int) -> int:
+    return _check(int(lib.conv2d_set_grid_limit(max_workgroups)), "conv2d_set_grid_limit")
 
 
 def conv2d_release_scratch() -> None:

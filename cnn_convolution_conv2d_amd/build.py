@@ -72,5 +72,30 @@ def build(verbose: bool = True) -> str:
     return OUT
 
 
+def sources() -> list[str]:
+    """Every file the library is built from: the HIP sources, their headers and
+    the public header."""
+    pats = ("*.hip", "*.hpp", "*.h")
+    found = [p for pat in pats for p in glob.glob(os.path.join(CSRC, pat))]
+    found += glob.glob(os.path.join(ROOT, "include", "*.h"))
+    found.append(os.path.abspath(__file__))
+    return sorted(found)
+
+
+def stale() -> bool:
+    """True when libconv2d.so is missing or older than any file it is built from."""
+    if not os.path.exists(OUT):
+        return True
+    built = os.path.getmtime(OUT)
+    return any(os.path.getmtime(p) > built for p in sources())
+
+
+def ensure_built(verbose: bool = False) -> str:
+    """Build libconv2d.so if it is missing or stale; returns its path."""
+    if stale():
+        build(verbose=verbose)
+    return OUT
+
+
 if __name__ == "__main__":
     build()

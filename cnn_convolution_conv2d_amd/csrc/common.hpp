@@ -106,6 +106,30 @@ int blocks_per_cu(int nt, int dev) {
     return b;
 }
 
+// The MFMA and depthwise kernels read and write through buffer resources whose
+// out-of-range offset (0x7ffffff0) stands for a zero tap or a dropped store;
+// that only works while x, y and the packed weights stay below it.  Larger
+// tensors go to the direct kernel.  (Transposed shapes: H, W are the input
+// extent and Ho, Wo the output's, so the same byte counts apply.)
+inline bool buffer_addressable(const Shape& s) {
+    const long long eb = s.dtype == 0 /* CONV2D_F32 */ ? 4 : 2;
+    const long long xb = (long long)s.N * s.H * s.W * s.Cin * eb;
+    const long long yb = (long long)s.N * s.Ho * s.Wo * s.Cout * eb;
+    const long long wb = (long long)s.Cout * s.cin_g * s.Kh * s.Kw * eb;
+    return xb < 0x7fff0000LL && yb < 0x7fff0000LL && wb < 0x7fff0000LL;
+}
+
+// Process-wide cap on the workgroups of one persistent launch (0: none), set
+// by conv2d_set_grid_limit.  The persistent kernels (halo tiles, streaming
+// 1x1, fused separable) launch min(work items, resident slots, this cap)
+// workgroups and walk their items in a grid-stride loop, so any cap >= 1 is
+// valid; a small one makes every workgroup walk several items.
+int grid_limit();
+inline long long persistent_slots(long long resident) {
+    const int lim = grid_limit();
+    return (lim > 0 && lim < resident) ? lim : resident;
+}
+
 // Allow a kernel more than the default 64 KB of dynamic LDS (up to `bytes`),
 // once per kernel and device.
 template <auto Kernel>

@@ -5,6 +5,7 @@
 #include <climits>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 
@@ -30,6 +31,37 @@ int hip_fail(hipError_t e, const char* what) {
 }
 
 int g_path_override = CONV2D_PATH_AUTO;
+int g_grid_limit = 0;
+
+// CONV2D_LOG (environment, read once): when set and not "0", every forward
+// entry prints the kernel path it chose to stderr, one line per call, so a
+// caller can check which kernel served a layer.
+bool log_enabled() {
+    static const bool on = [] {
+        const char* v = getenv("CONV2D_LOG");
+        return v && *v && strcmp(v, "0") != 0;
+    }();
+    return on;
+}
+
+const char* path_name(int path) {
+    switch (path) {
+    case CONV2D_PATH_DIRECT: return "direct";
+    case CONV2D_PATH_DEPTHWISE: return "depthwise";
+    case CONV2D_PATH_GEMM1X1: return "gemm1x1";
+    case CONV2D_PATH_IGEMM_GATHER: return "igemm_gather";
+    case CONV2D_PATH_IGEMM_HALO: return "igemm_halo";
+    default: return "?";
+    }
+}
+
+void log_path(const char* entry, const Shape& s, int path) {
+    if (!log_enabled()) return;
+    fprintf(stderr,
+            "conv2d: %s N=%d Cin=%d H=%d W=%d Cout=%d K=%dx%d S=%d P=%d D=%d G=%d dtype=%s epi=%d -> %s\n",
+            entry, s.N, s.Cin, s.H, s.W, s.Cout, s.Kh, s.Kw, s.stride, s.pad, s.dil, s.groups,
+            s.dtype == CONV2D_F32 ? "f32" : "bf16", s.epilogue, path_name(path));
+}
 
 // Output extent: floor((in + 2p - d(k-1) - 1)/s) + 1 (floor division of a
 // possibly negative numerator).
@@ -155,13 +187,22 @@ std::mutex g_scratch_mu;
 void* g_scratch[kMaxDevices] = {};
 size_t g_scratch_bytes[kMaxDevices] = {};
 
-int get_scratch(size_t bytes, void** out) {
+int get_scratch(size_t bytes, hipStream_t stream, void** out) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
     if (dev < 0 || dev >= kMaxDevices) return set_error(CONV2D_ERR_UNSUPPORTED, "device id %d", dev);
     std::lock_guard<std::mutex> lk(g_scratch_mu);
     if (g_scratch_bytes[dev] < bytes) {
+        // Growing synchronises the device and allocates, neither of which a
+        // stream capture allows.
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        e = hipStreamIsCapturing(stream, &cs);
+        if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+        if (cs != hipStreamCaptureStatusNone)
+            return set_error(CONV2D_ERR_UNSUPPORTED,
+                             "the NCHW entry's scratch must grow to %zu bytes, which cannot happen during a stream "
+                             "capture: call it once before capturing, or use conv2d_fwd_nhwc_packed", bytes);
         if (g_scratch[dev]) {
             // Earlier work on any stream may still read the old block.
             e = hipDeviceSynchronize();
@@ -207,6 +248,7 @@ int fwd_nhwc_packed(const void* x, const void* w_packed, const float* bias, cons
     if (rc) return rc;
     int path = choose_path(s);
     if (path < 0) return path;
+    log_path(with_bn ? "conv2d_fwd_nhwc_packed_bn" : "conv2d_fwd_nhwc_packed", s, path);
     return run_nhwc(path, s, x, w_packed, bias, y, stream);
 }
 
@@ -219,6 +261,7 @@ int fwd_nchw(const void* x, const void* w, const float* bias, const float* scale
     if (rc) return rc;
     int path = choose_path(s);
     if (path < 0) return path;
+    log_path(with_bn ? "conv2d_fwd_bn" : "conv2d_fwd", s, path);
     if (path == CONV2D_PATH_DIRECT) {
         // The direct loop reads the pages' layouts as they are: no repack.
         hipError_t e = launch_direct(s, x, NCHW, w, W_OIHW, bias, y, NCHW, stream);
@@ -229,7 +272,7 @@ int fwd_nchw(const void* x, const void* w, const float* bias, const float* scale
     const size_t xb = round_up((size_t)N * Cin * H * W * eb, 256);
     const size_t yb = round_up((size_t)N * Cout * s.Ho * s.Wo * eb, 256);
     void* scratch = nullptr;
-    rc = get_scratch(wb + xb + yb, &scratch);
+    rc = get_scratch(wb + xb + yb, stream, &scratch);
     if (rc) return rc;
     char* base = static_cast<char*>(scratch);
     void* wp = base;
@@ -332,7 +375,14 @@ int run_tnhwc(int path, const Shape& s, const void* x, const void* wp, const flo
 
 }  // namespace
 
+int conv2d::grid_limit() { return __atomic_load_n(&g_grid_limit, __ATOMIC_RELAXED); }
+
 extern "C" {
+
+int conv2d_set_grid_limit(int max_workgroups) {
+    if (max_workgroups < 0) return set_error(CONV2D_ERR_ARG, "grid limit %d must be >= 0", max_workgroups);
+    return __atomic_exchange_n(&g_grid_limit, max_workgroups, __ATOMIC_RELAXED);
+}
 
 int conv2d_out_dim(int in, int k, int stride, int pad, int dilation) {
     if (stride < 1 || dilation < 1 || k < 1 || pad < 0 || in < 1) return CONV2D_ERR_ARG;
@@ -558,6 +608,7 @@ int conv2d_transpose_fwd_nhwc_packed(const void* x, const void* w_packed, const 
     if (rc) return rc;
     const int path = choose_tpath(s);
     if (path < 0) return path;
+    log_path("conv2d_transpose_fwd_nhwc_packed", s, path);
     return run_tnhwc(path, s, x, w_packed, bias, y, stream);
 }
 
@@ -570,6 +621,7 @@ int conv2d_transpose_fwd(const void* x, const void* w, const float* bias, void* 
     if (rc) return rc;
     const int path = choose_tpath(s);
     if (path < 0) return path;
+    log_path("conv2d_transpose_fwd", s, path);
     if (path == CONV2D_PATH_DIRECT) {
         // the direct loop reads the pages' layouts as they are
         const hipError_t e = launch_tconv_direct(s, x, NCHW, w, W_IOHW, bias, y, NCHW, stream);
@@ -580,7 +632,7 @@ int conv2d_transpose_fwd(const void* x, const void* w, const float* bias, void* 
     const size_t xb = round_up((size_t)N * Cin * H * W * eb, 256);
     const size_t yb = round_up((size_t)N * Cout * s.Ho * s.Wo * eb, 256);
     void* scratch = nullptr;
-    rc = get_scratch(wb + xb + yb, &scratch);
+    rc = get_scratch(wb + xb + yb, stream, &scratch);
     if (rc) return rc;
     char* base = static_cast<char*>(scratch);
     void* wp = base;

@@ -215,7 +215,8 @@ bool depthwise_supports(const Shape& s) {
     // 16-byte channel vectors; the grid's y/z extents (and, for 3x3 stride 1,
     // their product with x) within launch limits
     const long long items = (long long)((s.Wo * (s.Cin / 8) + kThreads - 1) / kThreads) * ((s.Ho + kTH - 1) / kTH) * s.N;
-    return s.Cin % 8 == 0 && s.N <= 65535 && (s.Ho + kTH - 1) / kTH <= 65535 && items < 0x7fffffffLL;
+    return s.Cin % 8 == 0 && s.N <= 65535 && (s.Ho + kTH - 1) / kTH <= 65535 && items < 0x7fffffffLL &&
+           buffer_addressable(s);
 }
 
 hipError_t launch_depthwise(const Shape& s, const void* x, const void* w_dw, const float* bias,

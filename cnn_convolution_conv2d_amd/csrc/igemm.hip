@@ -410,8 +410,9 @@ hipError_t launch_any(const Shape& s, const void* x, const void* w, const float*
 }
 
 bool mfma_channels_ok(const Shape& s) {
-    // 16-byte K vectors and 4-channel output stores
-    return s.cin_g % 8 == 0 && s.cout_g % 4 == 0;
+    // 16-byte K vectors and 4-channel output stores; zero taps and dropped
+    // stores through the out-of-range buffer offset
+    return s.cin_g % 8 == 0 && s.cout_g % 4 == 0 && buffer_addressable(s);
 }
 
 }  // namespace

@@ -907,7 +907,8 @@ hipError_t launch_k(const Shape& s, const HaloGrid& hg, const bf16_t* x, const b
     auto kern = halo_kernel<NT, MINB, BM, TH, TW, WGM, WGN, KE, CFULL, BIAS, RELU>;
     int dev = 0;
     (void)hipGetDevice(&dev);
-    const long long resident = (long long)cu_count(dev) * blocks_per_cu<halo_kernel<NT, MINB, BM, TH, TW, WGM, WGN, KE, CFULL, BIAS, RELU>>(NT, dev);
+    const long long resident = persistent_slots(
+        (long long)cu_count(dev) * blocks_per_cu<halo_kernel<NT, MINB, BM, TH, TW, WGM, WGN, KE, CFULL, BIAS, RELU>>(NT, dev));
     const int grid = (int)(hg.ntiles < resident ? hg.ntiles : resident);
     hipLaunchKernelGGL(kern, dim3(grid), dim3(NT), 0, st, x, w, b, y, s, hg);
     return hipGetLastError();
@@ -942,7 +943,7 @@ hipError_t launch3_k(const Shape& s, const HaloGrid& hg, const bf16_t* x, const 
     int dev = 0;
     (void)hipGetDevice(&dev);
     const int bpc = blocks_per_cu<halo3_kernel<NT, MINB, BM, TH, TW, WGM, WGN, DIL, CFULL, BIAS, RELU>>(NT, dev);
-    const long long resident = (long long)cu_count(dev) * bpc;
+    const long long resident = persistent_slots((long long)cu_count(dev) * bpc);
     const int grid = (int)(hg.ntiles < resident ? hg.ntiles : resident);
     // Workgroups go round-robin over the 8 XCDs and, within one, fill every
     // CU once before any CU takes a second: the last round's tiles go to

@@ -383,7 +383,7 @@ hipError_t launch_pw(const PwArgs& a, const bf16_t* x, const bf16_t* w, const fl
     // at most two workgroups per CU: with more, the waves' activation streams
     // evict each other's lines from L1 between the slices that share them
     // (measured slower)
-    const long long resident = (long long)cu_count(dev) * (bpc < 2 ? bpc : 2);
+    const long long resident = persistent_slots((long long)cu_count(dev) * (bpc < 2 ? bpc : 2));
     const long long want = ((long long)ntiles * nmh + kPwWaves - 1) / kPwWaves;
     const int grid = (int)(want < resident ? want : resident);
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kPwThreads), (unsigned)lds, st, x, w, b, y, npix, a.cin, a.cout,

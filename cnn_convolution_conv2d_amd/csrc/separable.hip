@@ -346,7 +346,7 @@ hipError_t launch_sep(const SepPlan& pl, const bf16_t* x, const bf16_t* wdw, con
     const int by_regs = blocks_per_cu<sep_kernel<S, sep_rows(S), DWR>>(kSepThreads, dev);
     const int by_lds = (int)(163840 / (pl.lds + kSepMaxCout * 4));
     const int bpc = by_lds < by_regs ? (by_lds < 1 ? 1 : by_lds) : by_regs;
-    const long long resident = (long long)cu_count(dev) * bpc;
+    const long long resident = persistent_slots((long long)cu_count(dev) * bpc);
     const int grid = (int)(pl.g.nitems < resident ? pl.g.nitems : resident);
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kSepThreads), (unsigned)pl.lds, st, x, wdw, bdw, wpw, bpw, y, pl.g);
     return hipGetLastError();

@@ -96,7 +96,9 @@ enum {
  * (lincklin.cn sections 29-30), using a per-device scratch block that the
  * library grows on demand with hipMalloc (so this entry may allocate and may
  * block while it does) and frees in conv2d_release_scratch().  Calls that
- * share a device share that scratch: issue them on one stream.
+ * share a device share that scratch: issue them on one stream.  A call that
+ * would have to grow the scratch while its stream is being captured into a
+ * graph returns CONV2D_ERR_UNSUPPORTED instead (nothing is enqueued).
  */
 int conv2d_fwd(const void* x, const void* w, const float* bias, void* y,
                int N, int Cin, int H, int W, int Cout, int Kh, int Kw,
@@ -314,6 +316,22 @@ int conv2d_select_path(int N, int Cin, int H, int W, int Cout, int Kh, int Kw,
  * CONV2D_ERR_UNSUPPORTED.  Process-wide; returns the previous setting, or
  * CONV2D_ERR_ARG for an unknown path.  Meant for tests and A/B timing. */
 int conv2d_set_path_override(int path);
+
+/* Cap the workgroups of every persistent launch (the halo-tile implicit
+ * GEMMs, the streaming 1x1 kernel and the fused separable kernel) at
+ * max_workgroups; 0 (the default) launches as many as fit on the device.
+ * These kernels walk their output tiles in a grid-stride loop, so results do
+ * not depend on the cap: a small cap makes every workgroup walk several tiles
+ * (tests reach the cross-tile hand-over on small problems that way), and a
+ * caller sharing the GPU with concurrent work can bound the footprint of one
+ * call.  Process-wide; returns the previous cap, or CONV2D_ERR_ARG if
+ * max_workgroups < 0.  Host only. */
+int conv2d_set_grid_limit(int max_workgroups);
+
+/* Diagnostics: with the environment variable CONV2D_LOG set (and not "0")
+ * when the library first checks it, every conv2d_fwd*, conv2d_transpose_fwd*
+ * call prints one line to stderr naming its shape and the kernel path it
+ * chose (lpnh.cn section 6.3: check that the intended kernel ran). */
 
 /* Free the conv2d_fwd scratch of every device (after synchronising them). */
 void conv2d_release_scratch(void);

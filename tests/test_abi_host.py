@@ -187,6 +187,30 @@ def test_path_selection_fallbacks_and_override():
     assert c2.lib.conv2d_set_path_override(9) == c2.ERR_ARG
 
 
+def test_tensors_past_the_buffer_offset_limit_take_the_direct_path():
+    """The MFMA and depthwise kernels stand for a zero tap or a dropped store
+    with the out-of-range buffer offset 0x7ffffff0; an activation of 2 GiB or
+    more (valid: below 2**31 elements) would put real data at that offset, so
+    such shapes must go to the direct kernel."""
+    big = 4100  # 64 channels x 4100 x 4100 bf16 = 2.15 GB, 1.08e9 elements
+    assert 64 * big * big * 2 >= 0x7fff0000 and 64 * big * big < 2**31 - 1
+    # padded 3x3 (halo and gather), stride-2 3x3 (gather), 1x1 (GEMM), depthwise
+    for args in ((1, 64, big, big, 64, 3, 3, 1, 1, 1, 1), (1, 64, big, big, 64, 3, 3, 2, 1, 1, 1),
+                 (1, 64, big, big, 64, 1, 1, 1, 0, 1, 1), (1, 64, big, big, 64, 3, 3, 1, 1, 1, 64)):
+        assert c2.conv2d_select_path(*args, c2.BF16) == c2.PATH_DIRECT, args
+    # the output alone past the limit (a 1x1 widening 8 -> 128 channels)
+    assert c2.conv2d_select_path(1, 8, 3000, 3000, 128, 1, 1, 1, 0, 1, 1, c2.BF16) == c2.PATH_DIRECT
+    # just below the limit the MFMA paths still serve it
+    assert c2.conv2d_select_path(1, 64, 4000, 4000, 64, 3, 3, 2, 1, 1, 1, c2.BF16) == c2.PATH_IGEMM_GATHER
+    assert c2.conv2d_transpose_select_path(1, 64, big, big, 64, 3, 3, 1, 1, 0, 1, 1, c2.BF16) == c2.PATH_DIRECT
+
+
+def test_grid_limit_is_validated_and_returns_previous():
+    assert c2.lib.conv2d_set_grid_limit(-1) == c2.ERR_ARG
+    assert c2.conv2d_set_grid_limit(7) == 0
+    assert c2.conv2d_set_grid_limit(0) == 7
+
+
 # ------------------------------------------------------------------ transposed convolution
 
 def test_transpose_out_dim_agrees_with_oracle():
