@@ -23,10 +23,9 @@ def builder():
 
 
 def ensure_built():
-    """Build libconv2d.so if it is missing (tests load what is built)."""
-    b = builder()
-    if not os.path.exists(b.OUT):
-        b.build(verbose=False)
+    """Build libconv2d.so if it is missing or older than any of its sources
+    (tests load what is built; a stale library must not pass silently)."""
+    builder().ensure_built(verbose=False)
 
 
 def gpu_available() -> bool:
@@ -232,3 +231,30 @@ def run_winograd(x_nchw, w, bias, pad, epilogue, return_dev=False):
     if return_dev:
         return yd
     return ci.nhwc_to_nchw(yd.float().cpu().numpy()).astype(np.float64)
+
+
+def compare_full(yd, x_nchw, w, bias, stride, pad, dil, groups, relu, dtype, mode, what,
+                 outputs_per_chunk=1 << 22):
+    """Every element of the device NHWC output ``yd`` against the fp64 oracle,
+    a few images at a time (the oracle's memory stays bounded at full size).
+    Random data: the fp32 or bf16 tolerance element by element; exact-integer
+    mode: bit for bit (bf16: the round-to-nearest-even of the exact value).
+    Returns the worst err/tol (0 in exact-integer mode)."""
+    import oracle
+    N, Ho, Wo, Cout = yd.shape
+    step = max(1, outputs_per_chunk // max(1, Ho * Wo * Cout))
+    worst = 0.0
+    for n0 in range(0, N, step):
+        n1 = min(N, n0 + step)
+        y = ci.nhwc_to_nchw(yd[n0:n1].float().cpu().numpy()).astype(np.float64)
+        yref, s = oracle.conv2d(x_nchw[n0:n1], w, bias, stride, pad, dil, groups, relu=relu)
+        tag = f"{what} images {n0}..{n1 - 1}"
+        if mode == "int":
+            want = yref if dtype == ci.F32 else oracle.round_to_bf16(yref)
+            np.testing.assert_array_equal(y, want, err_msg=tag)
+        elif dtype == ci.F32:
+            bb = 0.0 if bias is None else np.abs(np.asarray(bias, np.float64))[None, :, None, None]
+            worst = max(worst, check_f32(y, yref, s, bb, tag))
+        else:
+            worst = max(worst, check_bf16(y, yref, s, tag))
+    return worst
