@@ -29,7 +29,7 @@ ERR_ARG, ERR_GROUPS, ERR_EMPTY_OUTPUT, ERR_UNSUPPORTED, ERR_HIP = -1, -2, -3, -4
 ERR_NULL, ERR_DTYPE, ERR_EPILOGUE, ERR_ALIGN = -6, -7, -8, -9
 
 # Every symbol include/conv2d.h declares.
-EXPORTS = ("conv2d_fwd", "conv2d_fwd_nhwc_packed", "conv2d_fwd_bn", "conv2d_fwd_nhwc_packed_bn",
+EXPORTS = ("conv2d_fwd", "conv2d_fwd_noalloc", "conv2d_fwd_nhwc_packed", "conv2d_fwd_bn", "conv2d_fwd_nhwc_packed_bn",
            "conv2d_fwd_separable_nhwc",
            "conv2d_winograd_weight_bytes", "conv2d_winograd_transform_weights", "conv2d_fwd_winograd_nhwc",
            "conv2d_transpose_fwd", "conv2d_transpose_fwd_nhwc_packed", "conv2d_transpose_pack_weights",
@@ -57,7 +57,7 @@ def _load() -> ctypes.CDLL:
     lib = ctypes.CDLL(LIB_PATH)
     P, I = ctypes.c_void_p, ctypes.c_int
     conv_args = [P, P, P, P] + [I] * 11 + [I, I, P]
-    for name in ("conv2d_fwd", "conv2d_fwd_nhwc_packed"):
+    for name in ("conv2d_fwd", "conv2d_fwd_noalloc", "conv2d_fwd_nhwc_packed"):
         f = getattr(lib, name)
         f.argtypes, f.restype = conv_args, I
     for name in ("conv2d_fwd_bn", "conv2d_fwd_nhwc_packed_bn"):
@@ -138,6 +138,15 @@ def conv2d_fwd(x, w, bias, y, N, Cin, H, W, Cout, Kh, Kw, stride, pad, dilation,
     _check(lib.conv2d_fwd(_ptr(x), _ptr(w), _ptr(bias), _ptr(y), N, Cin, H, W, Cout, Kh, Kw,
                           stride, pad, dilation, groups, dtype, epilogue, _stream(stream)),
            "conv2d_fwd")
+
+
+def conv2d_fwd_noalloc(x, w, bias, y, N, Cin, H, W, Cout, Kh, Kw, stride, pad, dilation, groups,
+                       dtype, epilogue, stream=None) -> None:
+    """conv2d_fwd staging through the library's static 64 MiB device array
+    (no allocation; calls on one GPU must not overlap)."""
+    _check(lib.conv2d_fwd_noalloc(_ptr(x), _ptr(w), _ptr(bias), _ptr(y), N, Cin, H, W, Cout, Kh, Kw,
+                                  stride, pad, dilation, groups, dtype, epilogue, _stream(stream)),
+           "conv2d_fwd_noalloc")
 
 
 def conv2d_fwd_nhwc_packed(x, w_packed, bias, y, N, Cin, H, W, Cout, Kh, Kw, stride, pad,

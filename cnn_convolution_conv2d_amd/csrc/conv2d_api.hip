@@ -252,6 +252,40 @@ int fwd_nhwc_packed(const void* x, const void* w_packed, const float* bias, cons
     return run_nhwc(path, s, x, w_packed, bias, y, stream);
 }
 
+// Staging of the NCHW entry's channels-last path: packed weights, the NHWC
+// copy of x and the NHWC result, each 256-byte aligned, in one block.
+struct Staging {
+    size_t wb, xb, yb;
+    size_t total() const { return wb + xb + yb; }
+};
+
+Staging staging_of(const Shape& s) {
+    const size_t eb = elem_bytes(s.dtype);
+    Staging g;
+    g.wb = round_up(conv2d_packed_weight_bytes(s.Cout, s.Cin, s.Kh, s.Kw, s.groups, s.dtype), 256);
+    g.xb = round_up((size_t)s.N * s.Cin * s.H * s.W * eb, 256);
+    g.yb = round_up((size_t)s.N * s.Cout * s.Ho * s.Wo * eb, 256);
+    return g;
+}
+
+// Repack w and x into the block at `base`, run the kernel of `path` on the
+// channels-last copies and write y back as NCHW (lincklin.cn lesson 9,
+// sections 29-30).  Every byte of the block that is read was written earlier
+// in the same call, on the same stream.
+int run_staged(int path, const Shape& s, const Staging& g, char* base, const void* x, const void* w,
+               const float* bias, void* y, hipStream_t stream) {
+    void* wp = base;
+    void* xn = base + g.wb;
+    void* yn = base + g.wb + g.xb;
+    int rc = conv2d_pack_weights(w, wp, s.Cout, s.Cin, s.Kh, s.Kw, s.groups, s.dtype, stream);
+    if (rc) return rc;
+    rc = conv2d_nchw_to_nhwc(x, xn, s.N, s.Cin, s.H, s.W, s.dtype, stream);
+    if (rc) return rc;
+    rc = run_nhwc(path, s, xn, wp, bias, yn, stream);
+    if (rc) return rc;
+    return conv2d_nhwc_to_nchw(yn, y, s.N, s.Cout, s.Ho, s.Wo, s.dtype, stream);
+}
+
 int fwd_nchw(const void* x, const void* w, const float* bias, const float* scale, const float* shift, void* y,
              int N, int Cin, int H, int W, int Cout, int Kh, int Kw, int stride, int pad, int dilation, int groups,
              int dtype, int epilogue, hipStream_t stream, bool with_bn) {
@@ -267,24 +301,42 @@ int fwd_nchw(const void* x, const void* w, const float* bias, const float* scale
         hipError_t e = launch_direct(s, x, NCHW, w, W_OIHW, bias, y, NCHW, stream);
         return e == hipSuccess ? CONV2D_OK : hip_fail(e, "direct launch");
     }
-    const size_t eb = elem_bytes(dtype);
-    const size_t wb = round_up(conv2d_packed_weight_bytes(Cout, Cin, Kh, Kw, groups, dtype), 256);
-    const size_t xb = round_up((size_t)N * Cin * H * W * eb, 256);
-    const size_t yb = round_up((size_t)N * Cout * s.Ho * s.Wo * eb, 256);
+    const Staging g = staging_of(s);
     void* scratch = nullptr;
-    rc = get_scratch(wb + xb + yb, stream, &scratch);
+    rc = get_scratch(g.total(), stream, &scratch);
     if (rc) return rc;
-    char* base = static_cast<char*>(scratch);
-    void* wp = base;
-    void* xn = base + wb;
-    void* yn = base + wb + xb;
-    rc = conv2d_pack_weights(w, wp, Cout, Cin, Kh, Kw, groups, dtype, stream);
-    if (rc) return rc;
-    rc = conv2d_nchw_to_nhwc(x, xn, N, Cin, H, W, dtype, stream);
-    if (rc) return rc;
-    rc = run_nhwc(path, s, xn, wp, bias, yn, stream);
-    if (rc) return rc;
-    return conv2d_nhwc_to_nchw(yn, y, N, Cout, s.Ho, s.Wo, dtype, stream);
+    return run_staged(path, s, g, static_cast<char*>(scratch), x, w, bias, y, stream);
+}
+
+// ---- the allocation-free NCHW entry
+//
+// Its staging lives in one statically sized device array per GPU, reserved
+// when the code object is loaded and kept until the process ends.  In host
+// code `scratch` names a host-side stand-in, not device memory: the array's
+// address on each device comes from hipGetSymbolAddress, taken once per
+// device with that device current, and only that address is handed to
+// kernels.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+std::mutex g_noalloc_mu;
+void* g_noalloc_ptr[kMaxDevices] = {};
+
+int noalloc_scratch(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return set_error(CONV2D_ERR_UNSUPPORTED, "device id %d", dev);
+    std::lock_guard<std::mutex> lk(g_noalloc_mu);
+    if (!g_noalloc_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol,
+                                                  "hipGetSymbolAddress(scratch)");
+        g_noalloc_ptr[dev] = p;
+    }
+    *out = g_noalloc_ptr[dev];
+    return CONV2D_OK;
 }
 
 // ---- transposed convolution
@@ -481,6 +533,33 @@ int conv2d_fwd(const void* x, const void* w, const float* bias, void* y,
                int dtype, int epilogue, hipStream_t stream) {
     return fwd_nchw(x, w, bias, nullptr, nullptr, y, N, Cin, H, W, Cout, Kh, Kw, stride, pad, dilation, groups,
                     dtype, epilogue, stream, false);
+}
+
+int conv2d_fwd_noalloc(const void* x, const void* w, const float* bias, void* y,
+                       int N, int Cin, int H, int W, int Cout, int Kh, int Kw,
+                       int stride, int pad, int dilation, int groups,
+                       int dtype, int epilogue, hipStream_t stream) {
+    Shape s;
+    int rc = validate(x, w, bias, y, N, Cin, H, W, Cout, Kh, Kw, stride, pad, dilation, groups, dtype, epilogue,
+                      &s);
+    if (rc) return rc;
+    const int path = choose_path(s);
+    if (path < 0) return path;
+    log_path("conv2d_fwd_noalloc", s, path);
+    if (path == CONV2D_PATH_DIRECT) {
+        const hipError_t e = launch_direct(s, x, NCHW, w, W_OIHW, bias, y, NCHW, stream);
+        return e == hipSuccess ? CONV2D_OK : hip_fail(e, "direct launch");
+    }
+    const Staging g = staging_of(s);
+    if (g.total() > kNoAllocScratchBytes)
+        return set_error(CONV2D_ERR_UNSUPPORTED,
+                         "conv2d_fwd_noalloc needs %zu bytes of staging (packed weights, NHWC x and y) but its "
+                         "static scratch holds %zu; use conv2d_fwd or conv2d_fwd_nhwc_packed",
+                         g.total(), kNoAllocScratchBytes);
+    void* base = nullptr;
+    rc = noalloc_scratch(&base);
+    if (rc) return rc;
+    return run_staged(path, s, g, static_cast<char*>(base), x, w, bias, y, stream);
 }
 
 int conv2d_fwd_bn(const void* x, const void* w, const float* bias, const float* scale, const float* shift,

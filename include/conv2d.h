@@ -106,6 +106,26 @@ int conv2d_fwd(const void* x, const void* w, const float* bias, void* y,
                int dtype, int epilogue, hipStream_t stream);
 
 /*
+ * conv2d_fwd_noalloc -- conv2d_fwd for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, layouts, paths, results and errors as
+ * conv2d_fwd, but the bf16 staging (packed weights, NHWC x, NHWC y) goes to a
+ * static device array of 64 MiB per GPU, reserved when the library's code
+ * object is loaded on that GPU and held until the process ends; the call
+ * never calls hipMalloc or hipFree and never synchronises.  A bf16 call whose
+ * staging needs more than 64 MiB returns CONV2D_ERR_UNSUPPORTED before
+ * enqueuing anything.  fp32 calls run the direct kernel in place and use no
+ * staging.  Every call on one GPU shares that GPU's array and leaves its
+ * contents behind; each call writes every staging byte it reads, so nothing
+ * needs clearing, but calls that overlap in time on one GPU (different
+ * streams, or host threads) race on the array: serialise them.
+ */
+int conv2d_fwd_noalloc(const void* x, const void* w, const float* bias, void* y,
+                       int N, int Cin, int H, int W, int Cout, int Kh, int Kw,
+                       int stride, int pad, int dilation, int groups,
+                       int dtype, int epilogue, hipStream_t stream);
+
+/*
  * conv2d_fwd_nhwc_packed -- the same operation on channels-last data
  * (lincklin.cn section 29; lnrq.cn section 5.3); allocates nothing.
  *   x        [N][H][W][Cin]        (NHWC)
