@@ -202,42 +202,27 @@ def test_workload_layer_on_phase_gemm(li, mode):
            f"{ly.name} phase GEMM {mode}")
 
 
-def _sample_indices(shape, rng, n_random=4096):
-    N, C, Ho, Wo = shape
-    idx = [rng.integers(0, N * C * Ho * Wo, size=n_random)]
-    for _ in range(2):  # the whole border of two output planes
-        n, c = int(rng.integers(0, N)), int(rng.integers(0, C))
-        base = (n * C + c) * Ho * Wo
-        hh, ww = np.meshgrid(np.arange(Ho), np.arange(Wo), indexing="ij")
-        border = (hh == 0) | (ww == 0) | (hh == Ho - 1) | (ww == Wo - 1)
-        idx.append(base + (hh * Wo + ww)[border])
-    idx.append(np.array([0, N * C * Ho * Wo - 1]))
-    return np.concatenate(idx).astype(np.int64)
-
-
 @pytest.mark.parametrize("mode", ["random", "int"])
 @pytest.mark.parametrize("cid,li", LAYERS, ids=[ci.layer(c, l).name for c, l in LAYERS])
-def test_workload_layer_full_size_sampled(cid, li, mode):
-    """Full size, the entry and launch the benchmark times; sampled outputs
-    against the oracle's gather-form point evaluator."""
+def test_workload_layer_full_size(cid, li, mode):
+    """Full size, the entry and launch the benchmark times; every output
+    element against the oracle's scatter form, a few images at a time."""
     ly = ci.layer(cid, li)
     x, w, b = ci.layer_tensors(cid, li, mode=mode)
     say(f"[tconv] {ly.name} full {mode} x{x.shape}")
     yd = run_tnhwc(x, w, b, ly.stride, ly.pad, ly.out_pad, ly.dilation, ly.groups, ly.dtype, ly.epilogue,
                    return_dev=True)
-    N, Ho, Wo, Cout = yd.shape
-    idx = _sample_indices((N, Cout, Ho, Wo), np.random.default_rng(60 + li))
-    wo, ho = idx % Wo, (idx // Wo) % Ho
-    co, n = (idx // (Wo * Ho)) % Cout, idx // (Wo * Ho * Cout)
-    nhwc = torch.from_numpy(((n * Ho + ho) * Wo + wo) * Cout + co).cuda()
-    y = yd.reshape(-1)[nhwc].float().cpu().numpy().astype(np.float64)
-    yref, s = oracle.conv_transpose2d_points(x, w, idx, b, ly.stride, ly.pad, ly.out_pad, ly.dilation, ly.groups,
-                                             relu=bool(ly.epilogue & ci.EPI_RELU))
-    if mode == "int":
-        np.testing.assert_array_equal(y, oracle.round_to_bf16(yref))
-    else:
-        check_bf16(y, yref, s, f"{ly.name} full")
     assert not torch.isnan(yd.float()).any().item()
+    N = yd.shape[0]
+    step = 4
+    for n0 in range(0, N, step):
+        y = ci.nhwc_to_nchw(yd[n0:n0 + step].float().cpu().numpy()).astype(np.float64)
+        yref, s = oracle.conv_transpose2d(x[n0:n0 + step], w, b, ly.stride, ly.pad, ly.out_pad, ly.dilation,
+                                          ly.groups, relu=bool(ly.epilogue & ci.EPI_RELU))
+        if mode == "int":
+            np.testing.assert_array_equal(y, oracle.round_to_bf16(yref), err_msg=f"images {n0}..")
+        else:
+            check_bf16(y, yref, s, f"{ly.name} full, images {n0}..")
 
 
 def test_transposed_forced_path_that_cannot_run_is_an_error():

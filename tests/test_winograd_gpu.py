@@ -19,7 +19,7 @@ import pytest
 
 import conv_inputs as ci
 import oracle
-from helpers import check_bf16, ensure_built, gpu_available, run_winograd
+from helpers import check_bf16, compare_full, ensure_built, gpu_available, run_winograd
 
 pytestmark = pytest.mark.gpu
 
@@ -67,37 +67,15 @@ def test_winograd_matches_oracle(case, mode):
         say(f"[wino]   worst |err| / tolerance = {worst:.3f}")
 
 
-def _sample_indices(shape, rng, n_random=4096):
-    N, C, Ho, Wo = shape
-    idx = [rng.integers(0, N * C * Ho * Wo, size=n_random)]
-    for _ in range(2):
-        n, c = int(rng.integers(0, N)), int(rng.integers(0, C))
-        base = (n * C + c) * Ho * Wo
-        hh, ww = np.meshgrid(np.arange(Ho), np.arange(Wo), indexing="ij")
-        border = (hh == 0) | (ww == 0) | (hh == Ho - 1) | (ww == Wo - 1)
-        idx.append(base + (hh * Wo + ww)[border])
-    idx.append(np.array([0, N * C * Ho * Wo - 1]))
-    return np.concatenate(idx).astype(np.int64)
-
-
 @pytest.mark.parametrize("mode", ["random", "int"])
-def test_winograd_full_workload_sampled(mode):
+def test_winograd_full_workload(mode):
     """The 3x3 workload layer (N=32, 128x112x112 -> 256, pad 1, bias+ReLU) at
-    full size through the launch the benchmark times; sampled outputs."""
+    full size through the launch the benchmark times; every output element
+    against the direct-loop oracle."""
     ly = ci.layer(2, 0)
     x, w, b = ci.layer_tensors(2, 0, mode=mode)
     say(f"[wino] full workload {mode}")
     yd = run_winograd(x, w, b, ly.pad, ly.epilogue, return_dev=True)
-    N, Ho, Wo, Cout = yd.shape
-    idx = _sample_indices((N, Cout, Ho, Wo), np.random.default_rng(77))
-    wo, ho = idx % Wo, (idx // Wo) % Ho
-    co, n = (idx // (Wo * Ho)) % Cout, idx // (Wo * Ho * Cout)
-    nhwc = torch.from_numpy(((n * Ho + ho) * Wo + wo) * Cout + co).cuda()
-    y = yd.reshape(-1)[nhwc].float().cpu().numpy().astype(np.float64)
-    yref, s = oracle.conv2d_points(x, w, idx, b, 1, ly.pad, 1, 1, relu=True)
-    if mode == "int":
-        np.testing.assert_array_equal(y, oracle.round_to_bf16(yref))
-    else:
-        worst = check_bf16(y, yref, s, "winograd full")
-        say(f"[wino]   worst |err| / tolerance = {worst:.3f}")
     assert not torch.isnan(yd.float()).any().item()
+    worst = compare_full(yd, x, w, b, 1, ly.pad, 1, 1, True, ci.BF16, mode, "winograd full")
+    say(f"[wino]   worst |err| / tolerance = {worst:.3f}")
