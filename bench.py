@@ -28,9 +28,19 @@ duration; peak = MI355X dense bf16 MFMA 2516.6 TFLOP/s (256 CU x 2.4 GHz x
 HBM byte count measured with rocprofv3 counters for this kernel source, read
 from profiles/traffic.json, or null when the kernel source changed since.
 
+The roofline block also gives the launch durations' mean and p10/p50/p90.
+Beside the timed entry, ``nchw_entry`` times ``conv2d_fwd`` on the pages'
+own layouts (weight repack and both layout passes per call; never the
+headline value); ``--no-nchw`` skips it.
+
 cpu_baseline: the fp64 oracle (test infrastructure) on a bounded sample of the
 same workload -- whole images, all channels -- run on the host cores until
-about --cpu-seconds have passed, scaled to the metric's unit.
+about --cpu-seconds have passed, scaled to the metric's unit.  The first line
+also carries ``single_thread``: the oracle on one host thread over the whole
+fp32 first layer and the whole depthwise-separable pair.
+
+``--hbm-ceiling`` only times a plain device copy that moves each HBM-bound
+layer's total bytes (context for their HBM fractions).
 """
 from __future__ import annotations
 
@@ -145,6 +155,54 @@ def host_cpu():
     return "unknown"
 
 
+def launch_stats(launch_ms):
+    """Mean and p10/p50/p90 of the per-launch HIP-event durations, in us."""
+    us = np.asarray(launch_ms) * 1e3
+    p10, p50, p90 = np.percentile(us, [10, 50, 90])
+    return {"kernel_mean_us": round(float(us.mean()), 3), "kernel_median_us": round(float(p50), 3),
+            "kernel_p10_us": round(float(p10), 3), "kernel_p90_us": round(float(p90), 3)}
+
+
+_SINGLE_THREAD_CHILD = r"""
+import json, sys, time
+sys.path.insert(0, sys.argv[1])
+import conv_inputs as ci
+import oracle
+out = {}
+for cid, li in ((1, 0), (3, 0), (3, 1)):
+    ly = ci.layer(cid, li)
+    x, w, b = ci.layer_tensors(cid, li)
+    relu = bool(ly.epilogue & ci.EPI_RELU)
+    oracle.conv2d(x[:1], w, b, ly.stride, ly.pad, ly.dilation, ly.groups, relu=relu, with_scale=False)
+    t0 = time.perf_counter()
+    oracle.conv2d(x, w, b, ly.stride, ly.pad, ly.dilation, ly.groups, relu=relu, with_scale=False)
+    out[f"cfg{cid}:{ly.name}"] = time.perf_counter() - t0
+out["threads"] = oracle.num_threads()
+print(json.dumps(out))
+"""
+
+
+def oracle_single_thread():
+    """The oracle on one host thread over the whole fp32 first layer and the
+    whole depthwise-separable pair (each layer separately), in a child
+    process started with OMP_NUM_THREADS=1; seconds and GFLOP/s per layer."""
+    import subprocess
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    r = subprocess.run([sys.executable, "-c", _SINGLE_THREAD_CHILD, ROOT], env=env, capture_output=True,
+                       text=True, timeout=300)
+    if r.returncode != 0:
+        return {"error": (r.stderr or "")[-300:]}
+    t = json.loads(r.stdout.strip().splitlines()[-1])
+    res = {"threads": t.pop("threads")}
+    for key, sec in t.items():
+        cid, name = key[3:].split(":", 1)
+        ly = ci.layer(int(cid), name)
+        flops, nbytes = algorithmic(ly)
+        res[key] = {"seconds": round(sec, 4), "gflop_per_s": round(flops / sec / 1e9, 4),
+                    "gb_per_s": round(nbytes / sec / 1e9, 4), "sample": f"all {ly.N} images"}
+    return res
+
+
 def cpu_baseline(cid, li, x, w, b, target_s, unit):
     """The fp64 oracle on whole images of the workload until target_s elapses."""
     import oracle
@@ -170,7 +228,38 @@ def cpu_baseline(cid, li, x, w, b, target_s, unit):
             "host_cpu": host_cpu()}
 
 
-def bench_layer(cid, li, steps, warmup, cpu_seconds, with_cpu, winograd=False):
+def time_nchw_entry(c2, ly, x, w, b, ho, wo, tdt, dt_lib, dev, stream, steps, flops, nbytes, unit):
+    """conv2d_fwd end to end on the pages' layouts (NCHW x and y, OIHW w):
+    for bf16 this is the weight repack, the NCHW -> NHWC pass, the kernel and
+    the NHWC -> NCHW pass per call, the conversion cost that can cancel a
+    kernel's gain (lincklin.cn lesson 9, section 30).  One buffer set; the
+    library's scratch is grown by the warm-up call.  Reported beside the
+    timed entry, never as the headline value."""
+    import torch
+    xn = torch.from_numpy(x).to(dev).to(tdt)
+    wn = torch.from_numpy(w).to(dev).to(tdt)
+    bn = torch.from_numpy(b).to(dev) if b is not None else None
+    yn = torch.empty((ly.N, ly.Cout, ho, wo), dtype=tdt, device=dev)
+
+    def call():
+        c2.conv2d_fwd(xn, wn, bn, yn, ly.N, ly.Cin, ly.H, ly.W, ly.Cout, ly.Kh, ly.Kw, ly.stride, ly.pad,
+                      ly.dilation, ly.groups, dt_lib, ly.epilogue, stream)
+
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    value = flops / (ms * 1e-3) / 1e12 if unit == "TFLOP/s" else nbytes / (ms * 1e-3) / 1e9
+    del xn, wn, yn
+    return {"entry": "conv2d_fwd (NCHW in and out, weights repacked per call)", "steps": steps,
+            "ms_per_call": round(ms, 5), "value": round(value, 3), "unit": unit, "buffer_sets": 1}
+
+
+def bench_layer(cid, li, steps, warmup, cpu_seconds, with_cpu, winograd=False, with_nchw=True):
     import torch
     import cnn_convolution_conv2d_amd as c2
 
@@ -258,6 +347,10 @@ def bench_layer(cid, li, steps, warmup, cpu_seconds, with_cpu, winograd=False):
         peak = PEAK_HBM_GBS
     key = f"cfg{cid}:{ly.name}" + (":winograd" if winograd else "")
     traffic = measured_traffic(key, pname)
+    nchw = None
+    if with_nchw and not winograd and not ly.transposed:
+        nchw = time_nchw_entry(c2, ly, x, w, b, ho, wo, tdt, dt_lib, dev, stream, max(5, min(steps, 20)),
+                               flops, nbytes, unit)
     line = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -286,10 +379,11 @@ def bench_layer(cid, li, steps, warmup, cpu_seconds, with_cpu, winograd=False):
             "bound": bound, "achieved": round(achieved, 3), "peak": peak,
             "unit": "TFLOP/s" if unit == "TFLOP/s" else "GB/s",
             "frac": round(achieved / peak, 4), "traffic": traffic,
-            "kernel_mean_us": round(mean_ms * 1e3, 3),
-            "kernel_median_us": round(float(np.median(launch_ms)) * 1e3, 3),
+            **launch_stats(launch_ms),
         },
     }
+    if nchw is not None:
+        line["nchw_entry"] = nchw
     if winograd:
         # FLOP/s above count the convolution's own multiply-adds; the matrix
         # cores execute 16/36 of them (F(2x2,3x3)) on the transformed data
@@ -409,13 +503,48 @@ def bench_separable(steps, warmup, cpu_seconds, with_cpu):
             "bound": "hbm", "achieved": round(achieved, 3), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
             "traffic": measured_traffic("cfg3:separable", "separable"),
-            "kernel_mean_us": round(mean_ms * 1e3, 3),
-            "kernel_median_us": round(float(np.median(launch_ms)) * 1e3, 3),
+            **launch_stats(launch_ms),
         },
     }
     if with_cpu:
         line["cpu_baseline"] = separable_cpu_baseline(x, wdw, bdw, wpw, bpw, cpu_seconds)
     return line
+
+
+def hbm_ceiling(steps):
+    """What a plain device copy (torch's copy kernel) reaches when it moves
+    the same total bytes as each HBM-bound layer (x read + y written, bf16):
+    a copy of (R + W) / 2 bytes into another buffer.  Buffer sets rotate as in
+    the layer timing.  Context for the HBM roofline fractions: a streaming
+    kernel with no arithmetic at the layer's size, not a bound on it."""
+    import torch
+    dev = torch.device("cuda", torch.cuda.current_device())
+    lines = []
+    for cid, li in ((3, 0), (3, 1), (5, 0), (5, 2), (6, 1)):
+        ly = ci.layer(cid, li)
+        ho, wo = out_hw(ly)
+        rb, wb = 2 * ly.N * ly.H * ly.W * ly.Cin, 2 * ly.N * ho * wo * ly.Cout
+        half = (rb + wb) // 4  # bf16 elements of each side of the copy
+        R = max(2, min(16, math.ceil(ROTATE_BYTES / (rb + wb))))
+        xs = [torch.randn(half, device=dev).to(torch.bfloat16) for _ in range(R)]
+        ys = [torch.empty(half, dtype=torch.bfloat16, device=dev) for _ in range(R)]
+        for i in range(5):
+            ys[i % R].copy_(xs[i % R])
+        torch.cuda.synchronize()
+        a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(steps):
+            ys[i % R].copy_(xs[i % R])
+        e.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(e) * 1e3 / steps
+        moved = 4 * half
+        lines.append({"workload": f"cfg{cid} {ly.name}", "layer_read_mb": round(rb / 1e6, 2),
+                      "layer_write_mb": round(wb / 1e6, 2), "copy_mb_each_way": round(2 * half / 1e6, 2),
+                      "us": round(us, 2), "gb_per_s": round(moved / us / 1e3, 1),
+                      "frac_of_8tb": round(moved / us / 1e3 / PEAK_HBM_GBS, 4), "buffer_sets": R})
+        del xs, ys
+    return lines
 
 
 def main(argv=None):
@@ -431,6 +560,10 @@ def main(argv=None):
                     help="time the 3x3 layer through the Winograd F(2x2,3x3) entry")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-nchw", action="store_true",
+                    help="skip timing the NCHW entry conv2d_fwd beside the timed entry")
+    ap.add_argument("--hbm-ceiling", action="store_true",
+                    help="only time a plain device copy moving each HBM-bound layer's total bytes")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 5 plain device copies of 256 MiB (known HBM traffic), for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
@@ -456,9 +589,11 @@ def main(argv=None):
         print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
                           "dispatches": 5}))
         return 0
-    b = _builder()
-    if not os.path.exists(b.OUT):
-        b.build()
+    if a.hbm_ceiling:
+        for ln in hbm_ceiling(a.steps):
+            print(json.dumps(ln), flush=True)
+        return 0
+    _builder().ensure_built()  # rebuilds a missing or stale library
     if a.winograd and not a.all:
         cid, li = (int(v) for v in a.layer.split(":"))
         print(json.dumps(bench_layer(cid, li, a.steps, a.warmup, a.cpu_seconds, with_cpu=not a.no_cpu_baseline,
@@ -472,7 +607,9 @@ def main(argv=None):
         if a.all else [tuple(int(v) for v in a.layer.split(":"))]
     for cid, li in layers:
         line = bench_layer(cid, li, a.steps, a.warmup, a.cpu_seconds,
-                           with_cpu=not a.no_cpu_baseline)
+                           with_cpu=not a.no_cpu_baseline, with_nchw=not a.no_nchw)
+        if not a.no_cpu_baseline and (cid, li) == layers[0]:
+            line["cpu_baseline"]["single_thread"] = oracle_single_thread()
         print(json.dumps(line), flush=True)
         if a.all and cid == 2:
             print(json.dumps(bench_layer(cid, li, a.steps, a.warmup, a.cpu_seconds,
