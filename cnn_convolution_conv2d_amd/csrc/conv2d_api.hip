@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <climits>
+#include <initializer_list>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -63,6 +64,15 @@ void log_path(const char* entry, const Shape& s, int path) {
             s.dtype == CONV2D_F32 ? "f32" : "bf16", s.epilogue, path_name(path));
 }
 
+// Product of non-negative sizes, saturated at LLONG_MAX instead of
+// overflowing (the size checks compare it with 2^31).
+long long sat_mul(std::initializer_list<long long> f) {
+    long long r = 1;
+    for (long long v : f)
+        if (__builtin_mul_overflow(r, v, &r)) return LLONG_MAX;
+    return r;
+}
+
 // Output extent: floor((in + 2p - d(k-1) - 1)/s) + 1 (floor division of a
 // possibly negative numerator).
 long long out_extent(long long in, long long k, long long s, long long p, long long d) {
@@ -95,9 +105,9 @@ int validate(const void* x, const void* w, const float* bias, const void* y,
     long long Wo = out_extent(W, Kw, stride, pad, dilation);
     if (Ho < 1 || Wo < 1)
         return set_error(CONV2D_ERR_EMPTY_OUTPUT, "empty output (Ho=%lld Wo=%lld)", Ho, Wo);
-    long long xe = (long long)N * Cin * H * W;
-    long long ye = (long long)N * Cout * Ho * Wo;
-    long long we = (long long)Cout * (Cin / groups) * Kh * Kw;
+    const long long xe = sat_mul({N, Cin, H, W});
+    const long long ye = sat_mul({N, Cout, Ho, Wo});
+    const long long we = sat_mul({Cout, Cin / groups, Kh, Kw});
     if (xe >= INT_MAX || ye >= INT_MAX || we >= INT_MAX || (long long)H + 2LL * pad >= INT_MAX / 2)
         return set_error(CONV2D_ERR_UNSUPPORTED, "tensor too large for 32-bit element offsets");
     if (out) {
@@ -370,8 +380,8 @@ int validate_transposed(const void* x, const void* w, const float* bias, const v
     const long long Ho = tout_extent(H, Kh, stride, pad, dilation, out_pad);
     const long long Wo = tout_extent(W, Kw, stride, pad, dilation, out_pad);
     if (Ho < 1 || Wo < 1) return set_error(CONV2D_ERR_EMPTY_OUTPUT, "empty output (Ho=%lld Wo=%lld)", Ho, Wo);
-    const long long xe = (long long)N * Cin * H * W, ye = (long long)N * Cout * Ho * Wo;
-    const long long we = (long long)Cout * (Cin / groups) * Kh * Kw;
+    const long long xe = sat_mul({N, Cin, H, W}), ye = sat_mul({N, Cout, Ho, Wo});
+    const long long we = sat_mul({Cout, Cin / groups, Kh, Kw});
     if (xe >= INT_MAX || ye >= INT_MAX || we >= INT_MAX || Ho >= INT_MAX / 2 || Wo >= INT_MAX / 2 ||
         (long long)pad + (long long)dilation * Kh >= INT_MAX / 2 || (long long)dilation * Kw >= INT_MAX / 2)
         return set_error(CONV2D_ERR_UNSUPPORTED, "tensor too large for 32-bit element offsets");
@@ -469,7 +479,8 @@ size_t conv2d_packed_weight_bytes(int Cout, int Cin, int Kh, int Kw, int groups,
     if (Cout < 1 || Cin < 1 || Kh < 1 || Kw < 1 || groups < 1 || Cin % groups || Cout % groups)
         return 0;
     if (dtype != CONV2D_F32 && dtype != CONV2D_BF16) return 0;
-    return (size_t)Cout * (Cin / groups) * Kh * Kw * elem_bytes(dtype);
+    const long long bytes = sat_mul({Cout, Cin / groups, Kh, Kw, (long long)elem_bytes(dtype)});
+    return bytes == LLONG_MAX ? 0 : (size_t)bytes;
 }
 
 int conv2d_pack_weights(const void* w, void* w_packed, int Cout, int Cin, int Kh, int Kw,
@@ -479,7 +490,7 @@ int conv2d_pack_weights(const void* w, void* w_packed, int Cout, int Cin, int Kh
         return set_error(CONV2D_ERR_ARG, "sizes must be >= 1");
     if (Cin % groups || Cout % groups) return set_error(CONV2D_ERR_GROUPS, "channels not divisible by groups");
     if (!w || !w_packed) return set_error(CONV2D_ERR_NULL, "w and w_packed must be non-NULL");
-    if ((long long)Cout * (Cin / groups) * Kh * Kw >= INT_MAX)
+    if (sat_mul({Cout, Cin / groups, Kh, Kw}) >= INT_MAX)
         return set_error(CONV2D_ERR_UNSUPPORTED, "weight too large");
     int dw = (groups == Cin && Cout == Cin) ? 1 : 0;
     hipError_t e = launch_pack_weights(w, w_packed, Cout, Cin / groups, Kh, Kw, dw,
@@ -491,7 +502,7 @@ static int transpose_args(const void* src, void* dst, int N, int C, int H, int W
     if (dtype != CONV2D_F32 && dtype != CONV2D_BF16) return set_error(CONV2D_ERR_DTYPE, "unknown dtype %d", dtype);
     if (N < 1 || C < 1 || H < 1 || W < 1) return set_error(CONV2D_ERR_ARG, "sizes must be >= 1");
     if (!src || !dst) return set_error(CONV2D_ERR_NULL, "src and dst must be non-NULL");
-    if ((long long)N * C * H * W >= INT_MAX) return set_error(CONV2D_ERR_UNSUPPORTED, "tensor too large");
+    if (sat_mul({N, C, H, W}) >= INT_MAX) return set_error(CONV2D_ERR_UNSUPPORTED, "tensor too large");
     return CONV2D_OK;
 }
 
@@ -589,7 +600,7 @@ int conv2d_fwd_separable_nhwc(const void* x, const void* w_dw, const float* bias
     if ((long long)H + 2LL * pad >= INT_MAX / 2) return set_error(CONV2D_ERR_UNSUPPORTED, "padding too large");
     const long long Ho = out_extent(H, 3, stride, pad, 1), Wo = out_extent(W, 3, stride, pad, 1);
     if (Ho < 1 || Wo < 1) return set_error(CONV2D_ERR_EMPTY_OUTPUT, "empty output (Ho=%lld Wo=%lld)", Ho, Wo);
-    if ((long long)N * C * H * W >= INT_MAX || (long long)N * Cout * Ho * Wo >= INT_MAX)
+    if (sat_mul({N, C, H, W}) >= INT_MAX || sat_mul({N, Cout, Ho, Wo}) >= INT_MAX)
         return set_error(CONV2D_ERR_UNSUPPORTED, "tensor too large for 32-bit element offsets");
     if (dtype != CONV2D_BF16)
         return set_error(CONV2D_ERR_UNSUPPORTED, "the fused depthwise-separable kernel runs bf16 only");
@@ -608,7 +619,7 @@ int conv2d_fwd_separable_nhwc(const void* x, const void* w_dw, const float* bias
 
 size_t conv2d_winograd_weight_bytes(int Cout, int Cin, int dtype) {
     if (Cout < 1 || Cin < 1 || Cin % 8 || dtype != CONV2D_BF16) return 0;
-    if (16LL * Cout * Cin * 2 >= INT_MAX) return 0;
+    if (sat_mul({16, Cout, Cin, 2}) >= INT_MAX) return 0;
     return (size_t)16 * Cout * Cin * 2;
 }
 
@@ -616,7 +627,7 @@ int conv2d_winograd_transform_weights(const void* w, void* w_wino, int Cout, int
     if (dtype != CONV2D_F32 && dtype != CONV2D_BF16) return set_error(CONV2D_ERR_DTYPE, "unknown dtype %d", dtype);
     if (Cout < 1 || Cin < 1) return set_error(CONV2D_ERR_ARG, "sizes must be >= 1");
     if (!w || !w_wino) return set_error(CONV2D_ERR_NULL, "w and w_wino must be non-NULL");
-    if (dtype != CONV2D_BF16 || Cin % 8 || 16LL * Cout * Cin * 2 >= INT_MAX)
+    if (dtype != CONV2D_BF16 || Cin % 8 || sat_mul({16, Cout, Cin, 2}) >= INT_MAX)
         return set_error(CONV2D_ERR_UNSUPPORTED, "Winograd weights need bf16, Cin %% 8 == 0 (got Cin=%d)", Cin);
     const hipError_t e = launch_winograd_weights(w, w_wino, Cout, Cin, stream);
     return e == hipSuccess ? CONV2D_OK : hip_fail(e, "winograd weight transform launch");
@@ -670,7 +681,7 @@ int conv2d_transpose_pack_weights(const void* w, void* w_packed, int Cin, int Co
         return set_error(CONV2D_ERR_ARG, "sizes must be >= 1");
     if (Cin % groups || Cout % groups) return set_error(CONV2D_ERR_GROUPS, "channels not divisible by groups");
     if (!w || !w_packed) return set_error(CONV2D_ERR_NULL, "w and w_packed must be non-NULL");
-    if ((long long)Cout * (Cin / groups) * Kh * Kw >= INT_MAX)
+    if (sat_mul({Cout, Cin / groups, Kh, Kw}) >= INT_MAX)
         return set_error(CONV2D_ERR_UNSUPPORTED, "weight too large");
     hipError_t e = launch_tpack_weights(w, w_packed, Cin, Cout / groups, groups, Kh, Kw, (int)elem_bytes(dtype),
                                         stream);
