@@ -554,6 +554,20 @@ __device__ __forceinline__ void tile_epilogue(f32x16 (&acc)[TM][TN], const char*
     }
 }
 
+// LDS address space for the destination of buffer-to-LDS copies.
+typedef __attribute__((address_space(3))) void* halo_lds_t;
+
+// This wave's LDS operations complete, then the workgroup barrier.  Unlike
+// __syncthreads, it does not wait for buffer-to-LDS copies still in flight
+// (those into the next chunk's halo buffer); the kernel waits for them
+// explicitly before the barrier after which they are read.
+__device__ __forceinline__ void halo_barrier() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt at their maxima (no wait)
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // 3x3 filters with dilation DIL (1 or 2): the same schedule as halo_kernel,
 // with the nine taps of a chunk unrolled at compile time.  Ring slots, tap
 // offsets and every LDS operand address are immediates; load offsets are
@@ -561,13 +575,24 @@ __device__ __forceinline__ void tile_epilogue(f32x16 (&acc)[TM][TN], const char*
 // LDS reads, matrix ops and LDS stores.  Per step (tap t of a chunk):
 //  * weights of step + 3 are loaded into register set t % 3 and stored one
 //    step later into ring slot (t + 2) % 3 (the slot read three steps later),
-//  * at taps 0 .. NPS-1 two 16-byte pieces per thread of the next chunk's
-//    halo window are loaded (stored one step later); at tap NPS of a tile's
-//    last chunk, the next tile's bias,
+//  * at taps 0 .. NPS-1 two 64-unit copies per wave of the next chunk's halo
+//    window go straight from memory into the other halo buffer (buffer loads
+//    to LDS: no registers, no LDS store instruction); they have until the
+//    barrier that closes tap 7 to land, four to seven steps later.  At tap
+//    NPS of a tile's last chunk, the next tile's bias is loaded (stored one
+//    step later),
 //  * the second slice's operands are read, the first slice's matrix ops
 //    issue, the next step's first-slice operands are read, the second
 //    slice's matrix ops issue,
 //  * one barrier.
+// The nine steps of a chunk run in a function whose LDS buffers (ring, the
+// current and the next halo buffer, bias) are distinct restrict arguments:
+// the compiler can then tell the copies in flight into the next buffer from
+// this chunk's operand reads and does not wait for them before each read.
+// Each wave waits for its own copies before the barrier that closes tap 7
+// (loads complete in order, so waiting until only tap 7's weight loads are
+// outstanding covers them); the next chunk's first operands are read after
+// that barrier.
 template <int NT, int MINB, int BM, int TH, int TW, int WGM, int WGN, int DIL, bool CFULL, bool BIAS, bool RELU>
 __global__ __launch_bounds__(NT, waves_per_simd(NT, MINB, halo_lds_bytes(BM, TH, TW, 2 * DIL + 1, BIAS)))
 void halo3_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ wp, const float* __restrict__ bias,
@@ -579,15 +604,19 @@ void halo3_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ wp, c
     static_assert(TM * 32 == WTM && TN * 32 == WTN, "32x32 MFMA tiles");
     static_assert(32 % TW == 0 || TW % 32 == 0, "32-pixel MFMA tiles cover whole block rows");
     constexpr int HWd = TW + 2 * DIL, HH = TH + 2 * DIL;  // halo window
-    constexpr int HUNITS = HH * HWd * 4;                   // its 16-byte units per chunk
     constexpr int A_BYTES = BM * kBK * 2;
-    constexpr int H_BYTES = HH * HWd * kHP * 16;
+    constexpr int HU5 = HH * HWd * kHP;                    // 16-byte units of a halo buffer (padding included)
+    constexpr int H_BYTES = HU5 * 16;
     constexpr int B_BYTES = BIAS ? BM * 4 : 0;
     constexpr int AV = BM * 4 / NT;
-    static_assert(AV * NT == BM * 4 && AV >= 1, "weight slice splits evenly");
-    constexpr int PPS = 2;                                 // halo pieces per loading step
-    constexpr int NPS = ((HUNITS + NT - 1) / NT + PPS - 1) / PPS;  // steps that load halo pieces
-    static_assert(NPS + 1 <= 7, "halo pieces land two taps before the chunk's last");
+    static_assert(AV * NT == BM * 4 && AV >= 1 && AV < 16, "weight slice splits evenly");
+    constexpr int NW = NT / 64;                            // waves
+    constexpr int NCOPY = (HU5 + 63) / 64;                 // 64-unit copies per halo window
+    constexpr int DPW = (NCOPY + NW - 1) / NW;             // copies per wave per chunk
+    constexpr int DPS = 2;                                 // copies per step
+    constexpr int NPS = (DPW + DPS - 1) / DPS;             // steps that issue copies (taps 0 .. NPS-1)
+    static_assert(NPS + 1 <= 6, "copies and the next tile's bias issue before tap 7");
+    static_assert(HWd < 256 && HH < 256, "window coordinates pack into bytes");
     // LDS distance between MFMA column blocks j and j + 1 (32 pixels)
     constexpr int JSTRIDE = TW <= 32 ? (32 / TW) * HWd * kHP * 16 : 32 * kHP * 16;
     __shared__ uint4 lds[(kRing * A_BYTES + 2 * H_BYTES + 2 * B_BYTES) / 16];
@@ -595,7 +624,8 @@ void halo3_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ wp, c
     char* const halo = ring + kRing * A_BYTES;
     char* const sbias = halo + 2 * H_BYTES;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WGN, wn = wave % WGN;
     const int G = gridDim.x;
     // This workgroup's tiles: first + k*G for the full rounds (first is
@@ -639,6 +669,22 @@ void halo3_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ wp, c
     // j * JSTRIDE bytes further)
     const int p0 = wn * WTN + frow;
     const int b_lane = ((p0 / TW) * HWd + p0 % TW) * (kHP * 16) + fch * 16;
+    // halo copies: copy m of this wave writes units base .. base+63 of a halo
+    // buffer, base = min(64 k, HU5 - 64) for k = wave + NW*m (the last copies
+    // overlap, rewriting the same values, instead of running past the
+    // buffer); this lane's unit is window pixel (row, column) and 16-byte
+    // piece ch (ch 4 is the padding unit: it reads 0)
+    int dm_rc[DPW], dm_base[DPW];
+#pragma unroll
+    for (int m = 0; m < DPW; ++m) {
+        const int kk = wave + NW * m;
+        const int base = 64 * kk < HU5 - 64 ? 64 * kk : HU5 - 64;
+        const int u = base + lane;
+        const int hp = u / kHP, ch = u - hp * kHP;
+        const int hr = hp / HWd, hc = hp - hr * HWd;
+        dm_rc[m] = hr | (hc << 8) | (ch << 16);
+        dm_base[m] = base * 16;
+    }
 
     // weight-load offsets of a tile (row within this group's channels, else past the end)
     auto a_offsets = [&](const TileXY& T, int* vo) {
@@ -647,6 +693,21 @@ void halo3_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ wp, c
             const int co = T.ct * BM + a_row[i];
             vo[i] = co < s.cout_g ? ((T.g * s.cout_g + co) * wrow + a_c[i] * 2) : kOOB;
         }
+    };
+
+    // copy m of channel chunk C of tile T into the halo buffer at DST (VALID
+    // false: the copy is still issued, with every lane reading 0, so that
+    // each step issues the same loads on every path and the compiler's load
+    // counting stays exact)
+    auto h3_copy = [&](char* __restrict__ dst, const TileXY& T, int C, int m, bool valid) {
+        const int rc = dm_rc[m];
+        const int hr = rc & 255, hc = (rc >> 8) & 255, ch = rc >> 16;
+        const int hi = T.ho0 - s.pad + hr, wi = T.wo0 - s.pad + hc;
+        const bool ok = valid && ch < 4 && (unsigned)hi < (unsigned)s.H && (unsigned)wi < (unsigned)s.W &&
+                        (CFULL || C * kBK + ch * 8 < s.cin_g);
+        const int off = ok ? (((T.n * s.H + hi) * s.W + wi) * s.Cin + T.g * s.cin_g + ch * 8) * 2 : kOOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (halo_lds_t)(dst + dm_base[m]), 16, off,
+                                                 __builtin_amdgcn_readfirstlane(C * kBK * 2), 0, 0);
     };
 
 #define TILE_OF(KK) ((KK) < nfull ? first + (KK) * G : nfull * G + e_extra)
@@ -661,8 +722,7 @@ void halo3_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ wp, c
         for (int j = 0; j < TN; ++j) acc[i][j] = f32x16{};
 
     uint4 ra[3][AV];           // weight register sets (step % 3)
-    uint4 hv[2][PPS];          // halo / bias pieces (tap % 2)
-    int hl[2][PPS];            // their LDS destinations (-1: none)
+    uint4 bv = make_uint4(0, 0, 0, 0);  // the next tile's bias piece
     bf16x8 af0[TM], bf0[TN], af1[TM], bf1[TN];
 
 #define A3_LOAD(RA, VO, C, TAP)                                                              \
@@ -673,27 +733,10 @@ void halo3_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ wp, c
             (RA)[i] = load16(wr, ok_ ? (VO)[i] : kOOB, so_);                                 \
         }                                                                                    \
     } while (0)
-#define A3_STORE(RA, SLOT)                                                                   \
+#define A3_STORE(RG, RA, SLOT)                                                               \
     do {                                                                                     \
         _Pragma("unroll") for (int i = 0; i < AV; ++i)                                       \
-            *reinterpret_cast<uint4*>(ring + (SLOT) * A_BYTES + a_lds[i]) = (RA)[i];         \
-    } while (0)
-    // halo piece U (window unit tid + U*NT) of chunk C of the tile (N, GG,
-    // HO0, WO0) into halo buffer HB; VALID false or a unit past the window:
-    // a load that returns 0, not stored
-#define H3_LOAD(RH, HL, N, GG, HO0, WO0, C, U, VALID, HB)                                    \
-    do {                                                                                     \
-        const int v_ = tid + (U) * NT;                                                       \
-        const int hp_ = v_ >> 2, hch_ = v_ & 3;                                              \
-        const int hr_ = hp_ / HWd;                                                           \
-        const int hi_ = (HO0) - s.pad + hr_, wi_ = (WO0) - s.pad + hp_ - hr_ * HWd;          \
-        const bool in_ = (VALID) && v_ < HUNITS;                                             \
-        const bool ok_ = in_ && (unsigned)hi_ < (unsigned)s.H && (unsigned)wi_ < (unsigned)s.W && \
-                         (CFULL || (C) * kBK + hch_ * 8 < s.cin_g);                          \
-        (RH) = load16(xr, ok_ ? (((N) * s.H + hi_) * s.W + wi_) * s.Cin * 2 +                \
-                                    ((GG) * s.cin_g + hch_ * 8) * 2 : kOOB,                  \
-                      __builtin_amdgcn_readfirstlane((C) * kBK * 2));                        \
-        (HL) = in_ ? kRing * A_BYTES + (HB) * H_BYTES + (hp_ * kHP + hch_) * 16 : -1;        \
+            *reinterpret_cast<uint4*>((RG) + (SLOT) * A_BYTES + a_lds[i]) = (RA)[i];         \
     } while (0)
 
     // ---- prologue: weight steps 0, 1 in ring slots 0, 1; step 2's weights in
@@ -705,22 +748,23 @@ void halo3_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ wp, c
         uint4 p0r[AV], p1r[AV];
         A3_LOAD(p0r, a_vo_c, 0, 0);
         A3_LOAD(p1r, a_vo_c, 0, 1);
-        constexpr int NP = (HUNITS + NT - 1) / NT;
-        uint4 ph[NP];
-        int pl[NP];
-#pragma unroll
-        for (int u = 0; u < NP; ++u) H3_LOAD(ph[u], pl[u], tc.n, tc.g, tc.ho0, tc.wo0, 0, u, true, 0);
         uint4 pb = make_uint4(0, 0, 0, 0);
         const bool bin = BIAS && tid * 4 < BM;
         if (BIAS) pb = load16(br, bin ? ((tc.g * s.cout_g + tc.ct * BM + tid * 4) * 4) : kOOB);
         A3_LOAD(ra[2], a_vo_c, 0, 2);
-        A3_STORE(p0r, 0);
-        A3_STORE(p1r, 1);
-#pragma unroll
-        for (int u = 0; u < NP; ++u)
-            if (pl[u] >= 0) *reinterpret_cast<uint4*>(ring + pl[u]) = ph[u];
+        A3_STORE(ring, p0r, 0);
+        A3_STORE(ring, p1r, 1);
         if (bin) *reinterpret_cast<uint4*>(sbias + tid * 16) = pb;
+#pragma unroll
+        for (int m = 0; m < DPW; ++m) h3_copy(halo, tc, 0, m, true);
     }
+    // every load of the prologue has landed (this wave's copies included),
+    // then the barrier for everyone's.  Nothing of the prologue stays in
+    // flight into the tile loop: the compiler merges the loop's entry and
+    // back-edge states, and a prologue load still pending at the entry made
+    // it wait at every tile start for all but the last few epilogue stores of
+    // the previous tile.
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
     __syncthreads();
     {
         const char* ab = ring + a_rd0;
@@ -730,33 +774,27 @@ void halo3_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ wp, c
 #pragma unroll
         for (int j = 0; j < TN; ++j) bf0[j] = *reinterpret_cast<const bf16x8*>(bb + j * JSTRIDE);
     }
-    // Nothing of the prologue stays in flight into the tile loop: the
-    // compiler merges the loop's entry and back-edge states, and a prologue
-    // load still pending at the entry made it wait at every tile start for
-    // all but the last few epilogue stores of the previous tile.
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
 
-    // One tap T (a literal 0..8) of the current chunk.
+    // One tap T (a literal 0..8) of the current chunk; RG ring, HC / HX the
+    // current / next halo buffer, SB the bias buffers.
 #define TAPOFF(T) ((((T) / 3) * DIL * HWd + ((T) % 3) * DIL) * (kHP * 16))
 #define HALO3_STEP(T)                                                                        \
     do {                                                                                     \
-        /* (1) loads: weights of step + 3; halo pieces / the next tile's bias */             \
+        /* (1) loads: weights of step + 3; halo copies / the next tile's bias */             \
         if ((T) + 3 < 9) A3_LOAD(ra[(T) % 3], a_vo_c, c, (T) + 3);                           \
         else A3_LOAD(ra[(T) % 3], a_vo_n, cn, (T) + 3 - 9);                                  \
         if ((T) < NPS) {                                                                     \
-            _Pragma("unroll") for (int p = 0; p < PPS; ++p)                                  \
-                H3_LOAD(hv[(T) & 1][p], hl[(T) & 1][p], hn.n, hn.g, hn.ho0, hn.wo0, cn,      \
-                        (T) * PPS + p, h_ok, hsel ^ 1);                                      \
+            _Pragma("unroll") for (int p = 0; p < DPS; ++p)                                  \
+                if ((T) * DPS + p < DPW) h3_copy(HX, hn, cn, (T) * DPS + p, h_ok);           \
         } else if ((T) == NPS) {                                                             \
             const bool bin_ = BIAS && last_chunk && k + 1 < nmine && tid * 4 < BM;           \
-            hv[(T) & 1][0] = load16(br, bin_ ? ((tn.g * s.cout_g + tn.ct * BM + tid * 4) * 4) : kOOB); \
-            hl[(T) & 1][0] = bin_ ? kRing * A_BYTES + 2 * H_BYTES + ((k + 1) & 1) * B_BYTES + tid * 16 : -1; \
+            bv = load16(br, bin_ ? ((tn.g * s.cout_g + tn.ct * BM + tid * 4) * 4) : kOOB);   \
         }                                                                                    \
         __builtin_amdgcn_sched_barrier(0);                                                   \
         /* (2) second slice's operands of this step */                                       \
         {                                                                                    \
-            const char* ab_ = ring + ((T) % 3) * A_BYTES + a_rd1;                            \
-            const char* bb_ = b_cur + TAPOFF(T) + 32;                                        \
+            const char* ab_ = (RG) + ((T) % 3) * A_BYTES + a_rd1;                            \
+            const char* bb_ = (HC) + b_lane + TAPOFF(T) + 32;                                \
             _Pragma("unroll") for (int i = 0; i < TM; ++i)                                   \
                 af1[i] = *reinterpret_cast<const bf16x8*>(ab_ + i * 2048);                   \
             _Pragma("unroll") for (int j = 0; j < TN; ++j)                                   \
@@ -769,8 +807,9 @@ void halo3_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ wp, c
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af0[i], bf0[j], acc[i][j], 0, 0, 0); \
         /* (4) next step's first-slice operands; second slice's matrix ops */                \
         {                                                                                    \
-            const char* ab_ = ring + (((T) + 1) % 3) * A_BYTES + a_rd0;                      \
-            const char* bb_ = (T) + 1 < 9 ? b_cur + TAPOFF((T) + 1 < 9 ? (T) + 1 : 0) : b_nxt; \
+            const char* ab_ = (RG) + (((T) + 1) % 3) * A_BYTES + a_rd0;                      \
+            const char* bb_ = (T) + 1 < 9 ? (HC) + b_lane + TAPOFF((T) + 1 < 9 ? (T) + 1 : 0) \
+                                          : (HX) + b_lane;                                   \
             _Pragma("unroll") for (int i = 0; i < TM; ++i)                                   \
                 af0[i] = *reinterpret_cast<const bf16x8*>(ab_ + i * 2048);                   \
             _Pragma("unroll") for (int j = 0; j < TN; ++j)                                   \
@@ -780,14 +819,13 @@ void halo3_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ wp, c
             _Pragma("unroll") for (int j = 0; j < TN; ++j)                                   \
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af1[i], bf1[j], acc[i][j], 0, 0, 0); \
         __builtin_amdgcn_sched_barrier(0);                                                   \
-        /* (5) LDS stores: weights of step + 2; pieces loaded last step */                   \
-        A3_STORE(ra[((T) + 2) % 3], ((T) + 2) % 3);                                          \
-        if ((T) >= 1 && (T) <= NPS + 1) {                                                    \
-            _Pragma("unroll") for (int p = 0; p < ((T) - 1 < NPS ? PPS : 1); ++p)            \
-                if (hl[((T) + 1) & 1][p] >= 0)                                               \
-                    *reinterpret_cast<uint4*>(ring + hl[((T) + 1) & 1][p]) = hv[((T) + 1) & 1][p]; \
-        }                                                                                    \
-        __syncthreads();                                                                     \
+        /* (5) LDS stores: weights of step + 2; the bias loaded last step */                 \
+        A3_STORE(RG, ra[((T) + 2) % 3], ((T) + 2) % 3);                                      \
+        if ((T) == NPS + 1 && BIAS && last_chunk && k + 1 < nmine && tid * 4 < BM)           \
+            *reinterpret_cast<uint4*>((SB) + ((k + 1) & 1) * B_BYTES + tid * 16) = bv;       \
+        /* the next chunk's halo copies have landed before the barrier closing tap 7 */      \
+        if ((T) == 7) __builtin_amdgcn_s_waitcnt(0x0f70 | AV);                               \
+        halo_barrier();                                                                      \
     } while (0)
 
     const int half = lane >> 5;
@@ -821,17 +859,20 @@ void halo3_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ wp, c
             else {
                 _Pragma("unroll") for (int i = 0; i < AV; ++i) a_vo_n[i] = a_vo_c[i];
             }
-            const char* const b_cur = halo + hsel * H_BYTES + b_lane;
-            const char* const b_nxt = halo + (hsel ^ 1) * H_BYTES + b_lane;
-            HALO3_STEP(0);
-            HALO3_STEP(1);
-            HALO3_STEP(2);
-            HALO3_STEP(3);
-            HALO3_STEP(4);
-            HALO3_STEP(5);
-            HALO3_STEP(6);
-            HALO3_STEP(7);
-            HALO3_STEP(8);
+            // the chunk's nine steps, with each LDS buffer a restrict argument
+            auto chunk = [&](char* __restrict__ RG, const char* __restrict__ HC, char* __restrict__ HX,
+                             char* __restrict__ SB) __attribute__((always_inline)) {
+                HALO3_STEP(0);
+                HALO3_STEP(1);
+                HALO3_STEP(2);
+                HALO3_STEP(3);
+                HALO3_STEP(4);
+                HALO3_STEP(5);
+                HALO3_STEP(6);
+                HALO3_STEP(7);
+                HALO3_STEP(8);
+            };
+            chunk(ring, halo + hsel * H_BYTES, halo + (hsel ^ 1) * H_BYTES, sbias);
             hsel ^= 1;
         }
         // the tile is done: ReLU, bf16, store; then the next tile
@@ -844,7 +885,6 @@ void halo3_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ wp, c
 #undef TILE_OF
 #undef A3_LOAD
 #undef A3_STORE
-#undef H3_LOAD
 #undef TAPOFF
 #undef HALO3_STEP
 }
