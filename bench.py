@@ -558,6 +558,9 @@ def main(argv=None):
                     help="time the fused depthwise-separable pair of config 3")
     ap.add_argument("--winograd", action="store_true",
                     help="time the 3x3 layer through the Winograd F(2x2,3x3) entry")
+    ap.add_argument("--path", default="auto",
+                    choices=["auto", "direct", "depthwise", "gemm1x1", "igemm", "igemm_gather", "igemm_halo"],
+                    help="force the library's kernel path (conv2d_set_path_override) for the timed layers")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-nchw", action="store_true",
@@ -605,6 +608,9 @@ def main(argv=None):
         return 0
     layers = [(c, i) for c in sorted(ci.WORKLOADS) for i in range(len(ci.WORKLOADS[c].layers))] \
         if a.all else [tuple(int(v) for v in a.layer.split(":"))]
+    if a.path != "auto":
+        import cnn_convolution_conv2d_amd as c2
+        c2.conv2d_set_path_override(getattr(c2, "PATH_" + a.path.upper()))
     for cid, li in layers:
         line = bench_layer(cid, li, a.steps, a.warmup, a.cpu_seconds,
                            with_cpu=not a.no_cpu_baseline, with_nchw=not a.no_nchw)

@@ -156,7 +156,14 @@ hipError_t launch_igemm(const Shape& s, const void* x, const void* w_packed, con
 hipError_t launch_igemm_halo(const Shape& s, const void* x, const void* w_packed, const float* bias,
                              void* y, hipStream_t st);
 bool igemm_supports(const Shape& s);
+// the halo kernels can run the shape (stride 1 plans, and 3x3 stride 2)
 bool igemm_halo_supports(const Shape& s);
+// the halo kernel the automatic path choice takes (stride 1 plans only)
+bool igemm_halo_auto(const Shape& s);
+// 3x3 stride 2: the phase-split staged window (served by launch_igemm_halo)
+bool halo_s2_supports(const Shape& s);
+hipError_t launch_halo_s2(const Shape& s, const void* x, const void* w_packed, const float* bias, void* y,
+                          hipStream_t st);
 bool gemm1x1_supports(const Shape& s);
 bool depthwise_supports(const Shape& s);
 hipError_t launch_pointwise(const Shape& s, const void* x, const void* w_packed, const float* bias,

@@ -40,7 +40,7 @@
 // (lincklin.cn section 31): a lane-half swap (v_permlane32_swap) turns the
 // 32x32 result layout into 8 consecutive channels of one pixel per lane, one
 // 16-byte store each.
-#include "mfma.hpp"
+#include "halo.hpp"
 #include "../../include/conv2d.h"
 
 namespace conv2d {
@@ -60,58 +60,11 @@ namespace {
 #define HALO_CFG_M64 256, 2, 64, 1, 4, 16, 16, 8, 32
 #endif
 
-constexpr int kBK = 32;      // input channels per chunk: one 64-byte LDS row per pixel
 constexpr int kKEmax = 5;    // largest effective filter extent (Kh-1)*D+1 the halo buffer holds
-constexpr int kRing = 3;     // weight slices staged in LDS
-
-// Halo tile layout in LDS: one window pixel = 5 16-byte units (80 bytes:
-// its 4 chunks of 8 channels plus one unit of padding).  Because 5 is odd,
-// any 16 consecutive window pixels read at the same chunk fall in 16 distinct
-// 16-byte bank slots (conflict-free ds_read_b128), and moving to another tap
-// is a plain additive offset of (kh*D*width + kw*D) * 80 bytes.
-constexpr int kHP = 5;
-
-struct HaloGrid {
-    int tiles_h, tiles_w, n_ctiles, ntiles;
-    int hwd_magic;  // ceil(2^16 / window width): row = (pixel * magic) >> 16 inside the window
-    int nparts;     // 16-byte halo loads per thread per chunk (one per tap)
-    int spread;     // last-round tiles go to every spread-th first-round workgroup of an XCD
-};
 
 // LDS bytes of one workgroup: weight ring, two halo buffers, two bias buffers.
 constexpr int halo_lds_bytes(int bm, int th, int tw, int ke, bool bias) {
     return kRing * bm * kBK * 2 + 2 * (th + ke - 1) * (tw + ke - 1) * kHP * 16 + (bias ? 2 * bm * 4 : 0);
-}
-
-// Minimum waves per SIMD the registers are budgeted for: the requested
-// workgroups per CU, or fewer where their LDS does not fit (160 KB per CU).
-constexpr int waves_per_simd(int nt, int minb, int lds_bytes) {
-    const int fit = 163840 / lds_bytes;
-    const int b = minb < fit ? minb : fit;
-    return b * nt / 256 < 1 ? 1 : b * nt / 256;
-}
-
-// Tile t -> (output-channel tile, group, image, pixel-block origin); the
-// channel tile varies fastest, then the group, then pixel blocks in row-major
-// order over each image.
-struct TileXY {
-    int ct, g, n, ho0, wo0;
-};
-
-template <int TH, int TW>
-__device__ __forceinline__ TileXY tile_xy(int tile, const HaloGrid& hg, int groups) {
-    TileXY t;
-    t.ct = tile % hg.n_ctiles;
-    tile /= hg.n_ctiles;
-    t.g = tile % groups;
-    tile /= groups;
-    const int tw = tile % hg.tiles_w;
-    tile /= hg.tiles_w;
-    const int th = tile % hg.tiles_h;
-    t.n = tile / hg.tiles_h;
-    t.ho0 = th * TH;
-    t.wo0 = tw * TW;
-    return t;
 }
 
 // KE: largest effective filter extent the halo buffers hold (3 or 5).
@@ -469,105 +422,6 @@ __global__ __launch_bounds__(NT, waves_per_simd(NT, MINB, halo_lds_bytes(BM, TH,
 #undef HALO_NEXT_CHUNK
 }
 
-// Epilogue of one tile from registers: bias, ReLU, bf16.  In the 32x32
-// result layout lane l < 32 of a block holds channels 8q+r (q = 0..3,
-// r = 0..3) of pixel l and lane l + 32 channels 8q+4+r.  A lane-half swap
-// (v_permlane32_swap) gives each lane 8 consecutive channels; a row swap
-// (v_permlane16_swap) then gathers 32 consecutive channels of 16 pixels into
-// one store instruction: lanes l, l+16, l+32, l+48 write the four 16-byte
-// pieces of one pixel's 64 contiguous bytes.  Pixels and channels outside the
-// output get an offset past the end: the buffer store drops them.
-template <int TM, int TN, int WTM, int WTN, int TH, int TW, bool BIAS, bool RELU>
-__device__ __forceinline__ void tile_epilogue(f32x16 (&acc)[TM][TN], const char* sb,
-                                              __amdgpu_buffer_rsrc_t yr, const Shape& s,
-                                              const TileXY& tc, int co0, int wm, int wn, int lane) {
-    const int half = lane >> 5;
-    const bool vec16 = (s.Cout % 8 == 0) && (s.cout_g % 8 == 0);
-    int pix[TN][2];
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int p = wn * WTN + j * 32 + 16 * h + (lane & 15);
-            const int ho = tc.ho0 + p / TW, wo = tc.wo0 + p % TW;
-            pix[j][h] = (ho < s.Ho && wo < s.Wo) ? ((tc.n * s.Ho + ho) * s.Wo + wo) * s.Cout : -1;
-        }
-    // channel of this lane's 16-byte piece within a 32-channel block
-    const int cl = ((lane >> 4) & 1) * 16 + half * 8;
-    const int cw = co0 + wm * WTM;  // first channel (within the group) of the wave's rows
-    const Affine4 aff(s.scale, s.shift, s.Cout);
-    const int cga = tc.g * s.cout_g + cw;  // absolute channel of cw
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        float4 b4[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            b4[q] = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (BIAS) b4[q] = *reinterpret_cast<const float4*>(sb + (wm * WTM + i * 32 + 8 * q + 4 * half) * 4);
-        }
-        const int co = cw + i * 32 + cl;
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            uint32_t pk[4][2];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                float v[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) v[r] = BIAS ? acc[i][j][4 * q + r] + (&b4[q].x)[r] : acc[i][j][4 * q + r];
-                if (s.scale) aff.apply(v, cga + i * 32 + 8 * q + 4 * half);
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (RELU) v[r] = fmaxf(v[r], 0.0f);
-                pk[q][0] = pack_bf16x2(v[0], v[1]);
-                pk[q][1] = pack_bf16x2(v[2], v[3]);
-            }
-            // r8[pr]: 8 channels 16*pr + 8*half .. +7 of pixel lane % 32
-            uint32_t r8[2][4];
-#pragma unroll
-            for (int pr = 0; pr < 2; ++pr)
-#pragma unroll
-                for (int w = 0; w < 2; ++w) {
-                    const auto sw = __builtin_amdgcn_permlane32_swap(pk[2 * pr][w], pk[2 * pr + 1][w], false, false);
-                    r8[pr][w] = sw[0];
-                    r8[pr][2 + w] = sw[1];
-                }
-            // out[h]: channels cl .. cl+7 of pixel 16*h + lane % 16
-            uint32_t out[2][4];
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                const auto sw = __builtin_amdgcn_permlane16_swap(r8[0][d], r8[1][d], false, false);
-                out[0][d] = sw[0];
-                out[1][d] = sw[1];
-            }
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int off = (pix[j][h] + tc.g * s.cout_g + co) * 2;
-                if (vec16) {
-                    store16<kStoreStream>(yr, pix[j][h] >= 0 && co < s.cout_g ? off : kOOB,
-                                          make_uint4(out[h][0], out[h][1], out[h][2], out[h][3]));
-                } else {
-                    store8(yr, pix[j][h] >= 0 && co < s.cout_g ? off : kOOB, make_uint2(out[h][0], out[h][1]));
-                    store8(yr, pix[j][h] >= 0 && co + 4 < s.cout_g ? off + 8 : kOOB, make_uint2(out[h][2], out[h][3]));
-                }
-            }
-        }
-    }
-}
-
-// LDS address space for the destination of buffer-to-LDS copies.
-typedef __attribute__((address_space(3))) void* halo_lds_t;
-
-// This wave's LDS operations complete, then the workgroup barrier.  Unlike
-// __syncthreads, it does not wait for buffer-to-LDS copies still in flight
-// (those into the next chunk's halo buffer); the kernel waits for them
-// explicitly before the barrier after which they are read.
-__device__ __forceinline__ void halo_barrier() {
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt at their maxima (no wait)
-    __builtin_amdgcn_s_barrier();
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
 // 3x3 filters with dilation DIL (1 or 2): the same schedule as halo_kernel,
 // with the nine taps of a chunk unrolled at compile time.  Ring slots, tap
 // offsets and every LDS operand address are immediates; load offsets are
@@ -699,7 +553,12 @@ void halo3_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ wp, c
     // false: the copy is still issued, with every lane reading 0, so that
     // each step issues the same loads on every path and the compiler's load
     // counting stays exact)
-    auto h3_copy = [&](char* __restrict__ dst, const TileXY& T, int C, int m, bool valid) {
+    // (DST is deliberately not a restrict parameter: the copies then carry
+    // only the alias scope of the chunk function's buffer argument, which
+    // the compiler's load-wait tracking can follow for a few scopes at a
+    // time; a scope per inlined copy would exhaust it and make every LDS
+    // access wait for all copies in flight)
+    auto h3_copy = [&](char* dst, const TileXY& T, int C, int m, bool valid) {
         const int rc = dm_rc[m];
         const int hr = rc & 255, hc = (rc >> 8) & 255, ch = rc >> 16;
         const int hi = T.ho0 - s.pad + hr, wi = T.wo0 - s.pad + hc;
@@ -1034,10 +893,12 @@ hipError_t launch_cfg(const Shape& s, const HaloPlan& p, const bf16_t* x, const 
 
 }  // namespace
 
-bool igemm_halo_supports(const Shape& s) { return make_plan(s).ok; }
+bool igemm_halo_supports(const Shape& s) { return make_plan(s).ok || halo_s2_supports(s); }
+bool igemm_halo_auto(const Shape& s) { return make_plan(s).ok; }
 
 hipError_t launch_igemm_halo(const Shape& s, const void* x, const void* w_packed, const float* bias,
                              void* y, hipStream_t st) {
+    if (s.stride == 2) return launch_halo_s2(s, x, w_packed, bias, y, st);
     (void)hipGetLastError();  // report only this launch's error
     const HaloPlan p = make_plan(s);
     if (!p.ok) return hipErrorInvalidValue;

@@ -67,7 +67,10 @@ enum {
                                      Cout/G % 4 == 0                             */
     CONV2D_PATH_IGEMM_HALO = 6  /* implicit GEMM on an LDS halo tile; stride 1,
                                    (K-1)*D+1 <= 5, Cin/G % 8 == 0,
-                                   Cout/G % 4 == 0 and > 32                      */
+                                   Cout/G % 4 == 0 and > 32; also 3x3 stride 2,
+                                   dilation 1 on a phase-split window, run only
+                                   when this path is forced (the automatic
+                                   choice gives stride 2 to the gather)         */
 };
 
 /* return codes */

@@ -178,10 +178,19 @@ def test_path_selection_fallbacks_and_override():
     c2.conv2d_set_path_override(c2.PATH_IGEMM)
     try:
         assert c2.conv2d_select_path(1, 64, 9, 9, 64, 3, 3, 1, 1, 1, 1, c2.BF16) == c2.PATH_IGEMM_HALO
+        # the implicit-GEMM override picks the gather for every stride above 1
         assert c2.conv2d_select_path(1, 64, 9, 9, 64, 3, 3, 2, 1, 1, 1, c2.BF16) == c2.PATH_IGEMM_GATHER
+        assert c2.conv2d_select_path(1, 64, 9, 9, 64, 3, 3, 3, 1, 1, 1, c2.BF16) == c2.PATH_IGEMM_GATHER
         c2.conv2d_set_path_override(c2.PATH_IGEMM_HALO)
+        # forced halo path: 3x3 stride 2 runs on the phase-split staged window;
+        # stride 3, or stride 2 with dilation, has no halo kernel
+        assert c2.conv2d_select_path(1, 64, 9, 9, 64, 3, 3, 2, 1, 1, 1, c2.BF16) == c2.PATH_IGEMM_HALO
         with pytest.raises(c2.Conv2dError):
-            c2.conv2d_select_path(1, 64, 9, 9, 64, 3, 3, 2, 1, 1, 1, c2.BF16)
+            c2.conv2d_select_path(1, 64, 9, 9, 64, 3, 3, 3, 1, 1, 1, c2.BF16)
+        with pytest.raises(c2.Conv2dError):
+            c2.conv2d_select_path(1, 64, 9, 9, 64, 3, 3, 2, 1, 2, 1, c2.BF16)
+        with pytest.raises(c2.Conv2dError):  # 32 output channels: below the kernel's minimum
+            c2.conv2d_select_path(1, 64, 9, 9, 32, 3, 3, 2, 1, 1, 1, c2.BF16)
     finally:
         c2.conv2d_set_path_override(c2.PATH_AUTO)
     assert c2.lib.conv2d_set_path_override(9) == c2.ERR_ARG

@@ -48,7 +48,12 @@ def _need_gpu():
 
 
 def _check_path(case, want):
+    """The path the calls of this case will take; a 3x3 stride-2 case is sent
+    to the staged-window kernel by forcing the halo path (the automatic
+    choice gives stride 2 to the gather kernel)."""
     N, Cin, H, W, Cout, Kh, Kw, S, P, D, G = case
+    if want == c2.PATH_IGEMM_HALO and S == 2:
+        c2.conv2d_set_path_override(c2.PATH_IGEMM_HALO)
     got = c2.conv2d_select_path(N, Cin, H, W, Cout, Kh, Kw, S, P, D, G, c2.BF16)
     assert got == want, f"{case}: path {c2.PATH_NAMES.get(got, got)}, expected {c2.PATH_NAMES[want]}"
 
@@ -95,6 +100,16 @@ CAPPED = [
     # workgroup of each XCD; 40 leaves 32 (no spread); 27 is not a multiple
     # of 8 (plain round-robin)
     ((2, 64, 96, 96, 128, 3, 3, 1, 1, 1, 1), HALO, (27, 40, 64)),
+    # 3x3 stride 2 on the phase-split window (4x32 pixel blocks; the halo
+    # path forced): 128- and 64-channel tiles, ragged output channels,
+    # Cin/G % 32 != 0, padding 0 and 2, groups, more than one 32-wide block
+    # per row
+    ((2, 64, 29, 57, 128, 3, 3, 2, 1, 1, 1), HALO, (1, 3)),
+    ((2, 72, 30, 70, 96, 3, 3, 2, 1, 1, 1), HALO, (2, 5)),
+    ((3, 64, 23, 40, 64, 3, 3, 2, 1, 1, 1), HALO, (1, 4)),
+    ((2, 32, 21, 33, 48, 3, 3, 2, 0, 1, 1), HALO, (1, 3)),
+    ((1, 64, 16, 16, 128, 3, 3, 2, 2, 1, 1), HALO, (1, 2)),
+    ((2, 128, 20, 20, 256, 3, 3, 2, 1, 1, 2), HALO, (3, 7)),
     # streaming 1x1 kernel: half tiles (256 in), whole tiles (64 in, 144 in),
     # straight operand loads (40 in, 136 out)
     ((3, 256, 20, 23, 64, 1, 1, 1, 0, 1, 1), GEMM1X1, (1, 5)),
@@ -146,11 +161,13 @@ NATURAL = [
     (10, 64, 128, 128, 256, 3, 3, 1, 2, 2, 2),
     # unrolled 3x3, 72 input channels (chunks of 32, 32, 8): 20 x 64 tiles
     (20, 72, 128, 128, 128, 3, 3, 1, 1, 1, 1),
+    # 3x3 stride 2, 128 -> 128 at 56x56 -> 28x28: 80 images x 7 blocks
+    (80, 128, 56, 56, 128, 3, 3, 2, 1, 1, 1),
 ]
 
 
 @pytest.mark.parametrize("mode", ["random", "int"])
-@pytest.mark.parametrize("case", NATURAL, ids=[f"n{c[0]}c{c[1]}o{c[4]}k{c[5]}d{c[9]}g{c[10]}" for c in NATURAL])
+@pytest.mark.parametrize("case", NATURAL, ids=[f"n{c[0]}c{c[1]}o{c[4]}k{c[5]}s{c[7]}d{c[9]}g{c[10]}" for c in NATURAL])
 def test_more_tiles_than_workgroups(case, mode):
     _check_path(case, c2.PATH_IGEMM_HALO)
     say(f"[multitile] natural {case} {mode}")

@@ -98,6 +98,29 @@ def test_layer_full_size(cid, li, mode):
     say(f"[parity] cfg{cid} {ly.name} full {mode}: worst err/tol {worst:.3g}")
 
 
+@pytest.mark.parametrize("mode", ["random", "int"])
+def test_stride2_staged_window_full_size(mode):
+    """The 3x3 stride-2 layer (64 x 128 x 56 x 56 -> 128 x 28 x 28) on the
+    phase-split staged-window kernel, which runs when the halo path is
+    forced; every output element compared with the oracle."""
+    cid, li = 5, 3
+    ly = ci.layer(cid, li)
+    assert ly.stride == 2 and ly.Kh == 3
+    x, w, b = ci.layer_tensors(cid, li, mode=mode)
+    c2.conv2d_set_path_override(c2.PATH_IGEMM_HALO)
+    try:
+        assert c2.conv2d_select_path(ly.N, ly.Cin, ly.H, ly.W, ly.Cout, ly.Kh, ly.Kw, ly.stride, ly.pad,
+                                     ly.dilation, ly.groups, c2.BF16) == c2.PATH_IGEMM_HALO
+        say(f"[parity] cfg{cid} {ly.name} staged window full {mode} x{x.shape}")
+        yd = run_nhwc(x, w, b, ly.stride, ly.pad, ly.dilation, ly.groups, ly.dtype, ly.epilogue,
+                      return_dev=True)
+    finally:
+        c2.conv2d_set_path_override(c2.PATH_AUTO)
+    worst = compare_full(yd, x, w, b, ly.stride, ly.pad, ly.dilation, ly.groups, _relu(ly), ly.dtype, mode,
+                         f"cfg{cid} {ly.name} staged window full {mode}")
+    say(f"[parity] cfg{cid} {ly.name} staged window full {mode}: worst err/tol {worst:.3g}")
+
+
 def test_chained_separable_pair():
     """Pointwise takes the GPU's own depthwise output (each kernel checked on
     exactly the input it saw)."""
