@@ -15,7 +15,12 @@ depthwise-separable pair of config 3 as one fused pass
 144 -> 24, the intermediate kept on chip).
 
 Timing: W untimed warm-up steps, then exactly K steps between two
-torch.cuda.synchronize() calls (wall clock -> ms_per_step and value).  Input
+torch.cuda.synchronize() calls (wall clock -> ms_per_step and value).  The
+defaults (W = 300, K = 500; under 0.2 s of GPU time on the 3x3 layer) put the
+timed steps past the GPU's power-management transient: on the 3x3 layer
+launch durations rise from ~215 us to 250-290 us around launches 7-30 and
+settle at ~211 us within about 100 launches (``--launch-times`` prints every
+launch's duration).  Input
 and output buffers rotate over R sets whose total size is >= 512 MB, so the
 256 MB Infinity Cache cannot hold the working set across steps.  Each launch
 is also bracketed by HIP events on the stream it runs on; their mean is the
@@ -67,10 +72,15 @@ ROTATE_BYTES = 512 << 20
 METRIC = "conv2d fwd TFLOP/s (GB/s for depthwise) and % of MI355X roofline, 1 GPU"
 KERNEL_SOURCES = {"direct": ["direct.hip"], "depthwise": ["depthwise.hip", "dwrow.hpp"],
                   "gemm1x1": ["pointwise.hip", "igemm.hip"], "igemm_gather": ["igemm.hip"],
-                  "igemm_halo": ["igemm_halo.hip"], "separable": ["separable.hip", "dwrow.hpp"],
+                  "igemm_halo": ["igemm_halo.hip", "igemm_halo_s2.hip", "halo.hpp"],
+                  "separable": ["separable.hip", "dwrow.hpp"],
                   "transposed_igemm_gather": ["igemm.hip"], "transposed_direct": ["transposed.hip"],
                   "transposed_gemm1x1": ["pointwise.hip"], "transposed_igemm_halo": ["transposed.hip"],
                   "winograd": ["winograd.hip"]}
+
+
+FORCED_PATH = None  # set by --path: the kernel path forced for the timed layers
+LAUNCH_TIMES = False  # set by --launch-times: report every launch's duration
 
 
 def out_hw(ly):
@@ -156,11 +166,15 @@ def host_cpu():
 
 
 def launch_stats(launch_ms):
-    """Mean and p10/p50/p90 of the per-launch HIP-event durations, in us."""
+    """Mean and p10/p50/p90 of the per-launch HIP-event durations, in us
+    (with --launch-times also every launch's duration, in launch order)."""
     us = np.asarray(launch_ms) * 1e3
     p10, p50, p90 = np.percentile(us, [10, 50, 90])
-    return {"kernel_mean_us": round(float(us.mean()), 3), "kernel_median_us": round(float(p50), 3),
-            "kernel_p10_us": round(float(p10), 3), "kernel_p90_us": round(float(p90), 3)}
+    out = {"kernel_mean_us": round(float(us.mean()), 3), "kernel_median_us": round(float(p50), 3),
+           "kernel_p10_us": round(float(p10), 3), "kernel_p90_us": round(float(p90), 3)}
+    if LAUNCH_TIMES:
+        out["launch_us"] = [round(float(v), 1) for v in us]
+    return out
 
 
 _SINGLE_THREAD_CHILD = r"""
@@ -345,7 +359,8 @@ def bench_layer(cid, li, steps, warmup, cpu_seconds, with_cpu, winograd=False, w
         value = nbytes / (ms_per_step * 1e-3) / 1e9
         achieved = nbytes / (mean_ms * 1e-3) / 1e9
         peak = PEAK_HBM_GBS
-    key = f"cfg{cid}:{ly.name}" + (":winograd" if winograd else "")
+    # a forced path's counters are kept under their own key
+    key = f"cfg{cid}:{ly.name}" + (":winograd" if winograd else "") + (f":{pname}" if FORCED_PATH else "")
     traffic = measured_traffic(key, pname)
     nchw = None
     if with_nchw and not winograd and not ly.transposed:
@@ -550,8 +565,8 @@ def hbm_ceiling(steps):
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--layer", default="2:0", help="workload layer as CID:LAYER_INDEX")
     ap.add_argument("--all", action="store_true", help="time every workload layer and the fused pair")
     ap.add_argument("--separable", action="store_true",
@@ -561,6 +576,8 @@ def main(argv=None):
     ap.add_argument("--path", default="auto",
                     choices=["auto", "direct", "depthwise", "gemm1x1", "igemm", "igemm_gather", "igemm_halo"],
                     help="force the library's kernel path (conv2d_set_path_override) for the timed layers")
+    ap.add_argument("--launch-times", action="store_true",
+                    help="add every timed launch's duration (us, in launch order) to the JSON line")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-nchw", action="store_true",
@@ -571,6 +588,8 @@ def main(argv=None):
                     help="only run 5 plain device copies of 256 MiB (known HBM traffic), for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
     a = ap.parse_args(argv)
+    global FORCED_PATH, LAUNCH_TIMES
+    LAUNCH_TIMES = a.launch_times
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
         print(f"bench.py: the library and this benchmark use one GPU (asked for --gpus {a.gpus}, "
@@ -610,6 +629,7 @@ def main(argv=None):
         if a.all else [tuple(int(v) for v in a.layer.split(":"))]
     if a.path != "auto":
         import cnn_convolution_conv2d_amd as c2
+        FORCED_PATH = a.path
         c2.conv2d_set_path_override(getattr(c2, "PATH_" + a.path.upper()))
     for cid, li in layers:
         line = bench_layer(cid, li, a.steps, a.warmup, a.cpu_seconds,
