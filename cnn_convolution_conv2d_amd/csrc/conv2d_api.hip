@@ -9,6 +9,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
+#include <vector>
 
 #include "../../include/conv2d.h"
 #include "common.hpp"
@@ -194,11 +195,19 @@ size_t elem_bytes(int dtype) { return dtype == CONV2D_F32 ? 4 : 2; }
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// Per-device scratch of the NCHW entry.
+// Scratch of the NCHW entries: one block per (device, stream), so calls on
+// different streams never share staging memory.  A block only grows; the
+// work that may still read the old block is the earlier work of the same
+// stream, so growing waits for that stream.
 constexpr int kMaxDevices = 64;
+struct ScratchBlock {
+    int dev;
+    hipStream_t stream;
+    void* ptr;
+    size_t bytes;
+};
 std::mutex g_scratch_mu;
-void* g_scratch[kMaxDevices] = {};
-size_t g_scratch_bytes[kMaxDevices] = {};
+std::vector<ScratchBlock> g_scratch;
 
 int get_scratch(size_t bytes, hipStream_t stream, void** out) {
     int dev = 0;
@@ -206,8 +215,15 @@ int get_scratch(size_t bytes, hipStream_t stream, void** out) {
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
     if (dev < 0 || dev >= kMaxDevices) return set_error(CONV2D_ERR_UNSUPPORTED, "device id %d", dev);
     std::lock_guard<std::mutex> lk(g_scratch_mu);
-    if (g_scratch_bytes[dev] < bytes) {
-        // Growing synchronises the device and allocates, neither of which a
+    ScratchBlock* b = nullptr;
+    for (auto& sb : g_scratch)
+        if (sb.dev == dev && sb.stream == stream) b = &sb;
+    if (!b) {
+        g_scratch.push_back(ScratchBlock{dev, stream, nullptr, 0});
+        b = &g_scratch.back();
+    }
+    if (b->bytes < bytes) {
+        // Growing waits for the stream and allocates, neither of which a
         // stream capture allows.
         hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
         e = hipStreamIsCapturing(stream, &cs);
@@ -216,24 +232,24 @@ int get_scratch(size_t bytes, hipStream_t stream, void** out) {
             return set_error(CONV2D_ERR_UNSUPPORTED,
                              "the NCHW entry's scratch must grow to %zu bytes, which cannot happen during a stream "
                              "capture: call it once before capturing, or use conv2d_fwd_nhwc_packed", bytes);
-        if (g_scratch[dev]) {
-            // Earlier work on any stream may still read the old block.
-            e = hipDeviceSynchronize();
-            if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
-            e = hipFree(g_scratch[dev]);
-            g_scratch[dev] = nullptr;
-            g_scratch_bytes[dev] = 0;
+        if (b->ptr) {
+            // earlier work on this stream may still read the old block
+            e = hipStreamSynchronize(stream);
+            if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+            e = hipFree(b->ptr);
+            b->ptr = nullptr;
+            b->bytes = 0;
             if (e != hipSuccess) return hip_fail(e, "hipFree");
         }
         size_t want = round_up(bytes, size_t(1) << 21);
-        e = hipMalloc(&g_scratch[dev], want);
+        e = hipMalloc(&b->ptr, want);
         if (e != hipSuccess) {
-            g_scratch[dev] = nullptr;
+            b->ptr = nullptr;
             return hip_fail(e, "hipMalloc(scratch)");
         }
-        g_scratch_bytes[dev] = want;
+        b->bytes = want;
     }
-    *out = g_scratch[dev];
+    *out = b->ptr;
     return CONV2D_OK;
 }
 
@@ -744,15 +760,13 @@ void conv2d_release_scratch(void) {
     std::lock_guard<std::mutex> lk(g_scratch_mu);
     int cur = 0;
     if (hipGetDevice(&cur) != hipSuccess) return;
-    for (int d = 0; d < kMaxDevices; ++d) {
-        if (!g_scratch[d]) continue;
-        if (hipSetDevice(d) == hipSuccess) {
+    for (auto& b : g_scratch) {
+        if (b.ptr && hipSetDevice(b.dev) == hipSuccess) {
             (void)hipDeviceSynchronize();
-            (void)hipFree(g_scratch[d]);
+            (void)hipFree(b.ptr);
         }
-        g_scratch[d] = nullptr;
-        g_scratch_bytes[d] = 0;
     }
+    g_scratch.clear();
     (void)hipSetDevice(cur);
 }
 

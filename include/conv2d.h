@@ -96,10 +96,13 @@ enum {
  *   y    [N][Cout][Ho][Wo]         (NCHW), written completely
  * fp32 runs the direct kernel on these layouts.  bf16 repacks x to NHWC and
  * w to the packed layout, runs the chosen kernel and repacks y back to NCHW
- * (lincklin.cn sections 29-30), using a per-device scratch block that the
- * library grows on demand with hipMalloc (so this entry may allocate and may
- * block while it does) and frees in conv2d_release_scratch().  Calls that
- * share a device share that scratch: issue them on one stream.  A call that
+ * (lincklin.cn sections 29-30), using a scratch block per device and stream
+ * that the library grows on demand with hipMalloc (so this entry may
+ * allocate, and waits for earlier work on its stream while it does) and
+ * frees in conv2d_release_scratch().  Calls on different streams use
+ * different blocks and may overlap; calls on one stream share its block and
+ * run in order.  A block stays allocated, per stream used, until
+ * conv2d_release_scratch().  A call that
  * would have to grow the scratch while its stream is being captured into a
  * graph returns CONV2D_ERR_UNSUPPORTED instead (nothing is enqueued).
  */
@@ -242,8 +245,8 @@ int conv2d_fwd_winograd_nhwc(const void* x, const void* w_wino, const float* bia
  *   bias fp32 [Cout], required iff epilogue has CONV2D_EPI_BIAS
  *   y    [N][Cout][Ho][Wo]      (NCHW), written completely
  * fp32 runs the direct kernel on these layouts; bf16 repacks x and w, runs
- * the chosen kernel and repacks y, in the same per-device scratch as
- * conv2d_fwd (so it may allocate and block; calls on one device share it).
+ * the chosen kernel and repacks y, in the same per-(device, stream) scratch
+ * as conv2d_fwd (so it may allocate, and wait for its stream while it does).
  *
  * conv2d_transpose_fwd_nhwc_packed -- channels-last, allocates nothing:
  *   x        [N][H][W][Cin]     (NHWC)
@@ -356,7 +359,8 @@ int conv2d_set_grid_limit(int max_workgroups);
  * call prints one line to stderr naming its shape and the kernel path it
  * chose (lpnh.cn section 6.3: check that the intended kernel ran). */
 
-/* Free the conv2d_fwd scratch of every device (after synchronising them). */
+/* Free the NCHW entries' scratch blocks of every device and stream (after
+ * synchronising the devices). */
 void conv2d_release_scratch(void);
 
 /* Static text for a return code, and the calling thread's last detailed

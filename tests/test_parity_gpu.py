@@ -307,6 +307,33 @@ def test_nchw_entry_full_first_layer():
     check_f32(y, yref, s, np.abs(b)[None, :, None, None].astype(np.float64), "cfg1 full NCHW")
 
 
+def test_nchw_entry_two_streams():
+    """The NCHW entry on two streams at once, each with its own input: every
+    stream stages through its own scratch block, so the two never overwrite
+    each other's repacked data; both results against the oracle."""
+    from helpers import lib_dtype, to_dev
+    N, Cin, H, W, Cout = 4, 64, 40, 40, 128
+    xs, outs = [], []
+    _, w, b = ci.random_tensors(7100, N, Cin, H, W, Cout, 3, 3, 1, bias=1)
+    for k in range(2):
+        x, _, _ = ci.random_tensors(7101 + k, N, Cin, H, W, Cout, 3, 3, 1, bias=1)
+        xs.append(x)
+    wd, bd = to_dev(w, ci.BF16), torch.from_numpy(np.asarray(b, np.float32)).cuda()
+    xd = [to_dev(x, ci.BF16) for x in xs]
+    yd = [torch.full((N, Cout, H, W), float("nan"), dtype=torch.bfloat16, device="cuda") for _ in xs]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    say("[parity] NCHW entry on two streams")
+    for rep in range(6):
+        for k in range(2):
+            c2.conv2d_fwd(xd[k], wd, bd, yd[k], N, Cin, H, W, Cout, 3, 3, 1, 1, 1, 1, lib_dtype(ci.BF16),
+                          ci.EPI_BIAS | ci.EPI_RELU, stream=streams[k])
+    torch.cuda.synchronize()
+    for k in range(2):
+        yref, sc = oracle.conv2d(xs[k], w, b, 1, 1, 1, 1, relu=True)
+        check_bf16(yd[k].float().cpu().numpy().astype(np.float64), yref, sc, f"stream {k}")
+
+
 # ------------------------------------------------------------------ repacks
 
 @pytest.mark.parametrize("dtype", [ci.F32, ci.BF16])
