@@ -261,6 +261,48 @@ __global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ sr
     }
 }
 
+// The same transpose for 2-byte elements when rows and cols are multiples of
+// 8 (and both tensors 16-byte aligned): each thread moves one 8x8 block with
+// eight 16-byte loads (eight consecutive source rows, the same eight
+// columns), a transpose in registers, and eight 16-byte stores (eight
+// consecutive destination rows, the same eight source rows).  Lane l of a
+// wave takes column block l % 8 and row block l / 8 of a 64x64 tile, so each
+// load or store instruction of a wave covers eight whole 128-byte runs; no
+// LDS and no barrier.  A workgroup's four waves take four tiles side by side.
+__global__ __launch_bounds__(256) void transpose8x8_kernel(const uint16_t* __restrict__ src,
+                                                           uint16_t* __restrict__ dst, int batch, int rows,
+                                                           int cols) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int c = (blockIdx.x * 4 + wave) * 64 + (lane & 7) * 8;
+    const size_t plane = (size_t)rows * cols;
+    if (c >= cols) return;
+    for (int b = blockIdx.z; b < batch; b += gridDim.z) {
+        for (int r0 = blockIdx.y * 64; r0 < rows; r0 += gridDim.y * 64) {
+            const int r = r0 + (lane >> 3) * 8;
+            if (r >= rows) continue;  // rows % 8 == 0: the block is whole or absent
+            const uint16_t* sp = src + b * plane + (size_t)r * cols + c;
+            uint4 v[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = *reinterpret_cast<const uint4*>(sp + (size_t)i * cols);
+            uint16_t* dp = dst + b * plane + (size_t)c * rows + r;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                // column j: word k holds rows 2k (low half) and 2k + 1 (high half);
+                // v_perm_b32 takes the low (j even) or high (j odd) half of each
+                const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+                uint32_t o[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const uint32_t* lo = reinterpret_cast<const uint32_t*>(&v[2 * k]);
+                    const uint32_t* hi = reinterpret_cast<const uint32_t*>(&v[2 * k + 1]);
+                    o[k] = __builtin_amdgcn_perm(hi[j >> 1], lo[j >> 1], sel);
+                }
+                *reinterpret_cast<uint4*>(dp + (size_t)j * rows) = make_uint4(o[0], o[1], o[2], o[3]);
+            }
+        }
+    }
+}
+
 // Weight repack: [Cout][Cin/G][Kh][Kw] -> [Cout][Kh][Kw][Cin/G], or for a
 // depthwise filter bank [C][1][Kh][Kw] -> [Kh][Kw][C].  One thread per element.
 template <typename T>
@@ -292,6 +334,13 @@ hipError_t launch_transpose(const void* src, void* dst, int batch, int rows, int
                             int elem_bytes, hipStream_t st) {
     (void)hipGetLastError();  // report only this launch's error
     const int ty = (rows + kTile - 1) / kTile;
+    if (elem_bytes == 2 && rows % 8 == 0 && cols % 8 == 0 &&
+        ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15) == 0) {
+        dim3 grid((cols + 4 * kTile - 1) / (4 * kTile), ty < 65535 ? ty : 65535, batch < 65535 ? batch : 65535);
+        hipLaunchKernelGGL(transpose8x8_kernel, grid, dim3(256), 0, st, static_cast<const uint16_t*>(src),
+                           static_cast<uint16_t*>(dst), batch, rows, cols);
+        return hipGetLastError();
+    }
     dim3 grid((cols + kTile - 1) / kTile, ty < 65535 ? ty : 65535, batch < 65535 ? batch : 65535);
     if (elem_bytes == 4)
         hipLaunchKernelGGL(transpose_kernel<float>, grid, dim3(256), 0, st,

@@ -337,7 +337,10 @@ def test_nchw_entry_two_streams():
 # ------------------------------------------------------------------ repacks
 
 @pytest.mark.parametrize("dtype", [ci.F32, ci.BF16])
-@pytest.mark.parametrize("shape", [(2, 3, 5, 7), (1, 144, 56, 56), (3, 65, 1, 130), (1, 1, 1, 1)])
+# (channels and H*W multiples of 8 take the 8x8-block bf16 kernel, with full
+# and partial 64x64 tiles; the others the LDS-tile kernel)
+@pytest.mark.parametrize("shape", [(2, 3, 5, 7), (1, 144, 56, 56), (3, 65, 1, 130), (1, 1, 1, 1),
+                                   (2, 40, 9, 24), (3, 256, 28, 28), (1, 8, 1, 8)])
 def test_layout_repack_roundtrip(dtype, shape):
     from helpers import lib_dtype, to_dev
     rng = np.random.default_rng(1)
