@@ -334,6 +334,25 @@ def test_nchw_entry_two_streams():
         check_bf16(yd[k].float().cpu().numpy().astype(np.float64), yref, sc, f"stream {k}")
 
 
+def test_conv2d_log_names_the_path():
+    """With CONV2D_LOG set, a forward call prints its shape and the kernel
+    path it took (a child process: the switch is read once per process)."""
+    import os
+    import subprocess
+    here = os.path.dirname(os.path.abspath(__file__))
+    code = (f"import sys; sys.path.insert(0, {os.path.dirname(here)!r}); sys.path.insert(0, {here!r})\n"
+            "import conv_inputs as ci\n"
+            "from helpers import run_nhwc\n"
+            "x, w, b = ci.random_tensors(1, 1, 64, 9, 9, 128, 3, 3, 1, bias=1)\n"
+            "run_nhwc(x, w, b, 1, 1, 1, 1, ci.BF16, 3)\n")
+    say("[parity] CONV2D_LOG child process")
+    r = subprocess.run([sys.executable, "-c", code], env=dict(os.environ, CONV2D_LOG="1"), capture_output=True,
+                       text=True, timeout=240)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert ("conv2d: conv2d_fwd_nhwc_packed N=1 Cin=64 H=9 W=9 Cout=128 K=3x3 S=1 P=1 D=1 G=1 dtype=bf16 epi=3 "
+            "-> igemm_halo") in r.stderr, r.stderr[-2000:]
+
+
 # ------------------------------------------------------------------ repacks
 
 @pytest.mark.parametrize("dtype", [ci.F32, ci.BF16])
