@@ -117,11 +117,17 @@ __global__ __launch_bounds__(kPwThreads, 2) void pw_kernel(const bf16_t* __restr
     // 32-channel block, of pixel 16*e + lane % 16 (e = 0, 1) of the tile
     const int cl = ((lane >> 4) & 1) * 16 + h * 8;
     const bool vec16 = cout % 8 == 0;
-    // streaming stores (measured): faster for the pixel-shuffle epilogue and
-    // for outputs narrower than 64 channels, slower for the plain 64- and
-    // 256-channel layers, where the lines written by two store instructions
-    // then leave L2 as separate partial writes
-    const bool stream = SHUF || cout < 64;
+    // Output blocks in pairs (MB even, 16-byte pieces, no pixel shuffle):
+    // two 32-channel blocks are merged with 8-lane row shifts (DPP) so that
+    // each store instruction writes the 64 channels of 8 pixels, i.e. whole
+    // 128-byte lines.  Streaming (nt) stores then add no partial-line writes
+    // and free L2 for the activations (measured: 256->64 32.6 -> 30.0 us,
+    // 64->256 33.4 -> 29.0 us).  Without the merge, streaming stores were
+    // measured faster only for the pixel-shuffle epilogue and for outputs
+    // narrower than 64 channels (the merge itself measured no faster for the
+    // pixel-shuffle layer).
+    const bool merged = MB % 2 == 0 && vec16 && !SHUF;
+    const bool stream = SHUF || cout < 64 || merged;
     const Affine4 aff(scale, shift, cout);  // folded batch normalisation, when scale is given
 
     const int nw = gridDim.x * (kPwThreads / 64);
@@ -222,10 +228,55 @@ __global__ __launch_bounds__(kPwThreads, 2) void pw_kernel(const bf16_t* __restr
             if ((u % P) * 8 >= cin) wl[rows * P + u] = make_uint4(0, 0, 0, 0);
     __syncthreads();
 
+    int cur_c0 = 0;  // first output channel of the tile being finished (for pw_pack)
+    // output offset of tile pixel p (-1: past the end); pixel shuffle:
+    // output pixel (n, ih*S, iw*S), to which a row's tap adds kh*Wo + kw
+    auto pw_pix = [&](int p) {
+        if (SHUF) {
+            const int iw = p % sh.w, t = p / sh.w;
+            const int ih = t % sh.h, n = t / sh.h;
+            return p < npix ? (n * sh.ho + ih * sh.stride) * sh.wo + iw * sh.stride : -1;
+        }
+        return p < npix ? p * cout : -1;
+    };
+    // block mb of the accumulators -> two 16-byte pieces per lane: o[e] holds
+    // rows (channels) cl .. cl+7 of the block, of tile pixel 16*e + lane % 16
+    auto pw_pack = [&](int mb, uint32_t (&o)[2][4]) __attribute__((always_inline)) {
+        uint32_t pk[4][2];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            float v[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] = acc[mb][4 * q + r];
+            if (scale) aff.apply(v, cur_c0 + mb * 32 + 8 * q + 4 * h);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (relu) v[r] = fmaxf(v[r], 0.0f);
+            pk[q][0] = pack_bf16x2(v[0], v[1]);
+            pk[q][1] = pack_bf16x2(v[2], v[3]);
+        }
+        uint32_t r8[2][4];
+#pragma unroll
+        for (int pr = 0; pr < 2; ++pr)
+#pragma unroll
+            for (int w = 0; w < 2; ++w) {
+                const auto sw = __builtin_amdgcn_permlane32_swap(pk[2 * pr][w], pk[2 * pr + 1][w], false, false);
+                r8[pr][w] = sw[0];
+                r8[pr][2 + w] = sw[1];
+            }
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const auto sw = __builtin_amdgcn_permlane16_swap(r8[0][d], r8[1][d], false, false);
+            o[0][d] = sw[0];
+            o[1][d] = sw[1];
+        }
+    };
+
     // one tile: bias-initialised accumulators, KS x MB matrix ops, epilogue
 #define PW_TILE(B, I)                                                                        \
     do {                                                                                     \
         const int T = (I) / nmh, c0_ = ((I) - T * nmh) * (MB * 32);                          \
+        cur_c0 = c0_;                                                                        \
         PW_STAGE(B);                                                                         \
         _Pragma("unroll") for (int mb = 0; mb < MB; ++mb)                                    \
             _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                  \
@@ -248,42 +299,48 @@ __global__ __launch_bounds__(kPwThreads, 2) void pw_kernel(const bf16_t* __restr
                 }                                                                            \
             }                                                                                \
         }                                                                                    \
-        int pix_[2];                                                                         \
+        int pix_[2], pix8_[2][2];                                                            \
         _Pragma("unroll") for (int e = 0; e < 2; ++e) {                                      \
-            const int p_ = (T) * 32 + 16 * e + (lane & 15);                                  \
-            if (SHUF) {                                                                      \
-                /* output pixel (n, ih*S, iw*S): the tap adds kh*Wo + kw */                  \
-                const int iw_ = p_ % sh.w, t_ = p_ / sh.w;                                   \
-                const int ih_ = t_ % sh.h, n_ = t_ / sh.h;                                   \
-                pix_[e] = p_ < npix ? (n_ * sh.ho + ih_ * sh.stride) * sh.wo + iw_ * sh.stride : -1; \
-            } else {                                                                         \
-                pix_[e] = p_ < npix ? p_ * cout : -1;                                        \
-            }                                                                                \
+            pix_[e] = pw_pix((T) * 32 + 16 * e + (lane & 15));                              \
+            pix8_[e][0] = pw_pix((T) * 32 + 16 * e + (lane & 7));                           \
+            pix8_[e][1] = pw_pix((T) * 32 + 16 * e + 8 + (lane & 7));                       \
         }                                                                                    \
-        _Pragma("unroll") for (int mb = 0; mb < MB; ++mb) {                                  \
-            uint32_t pk_[4][2];                                                              \
-            _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                  \
-                float v_[4];                                                                 \
-                _Pragma("unroll") for (int r = 0; r < 4; ++r) v_[r] = acc[mb][4 * q + r];   \
-                if (scale) aff.apply(v_, c0_ + mb * 32 + 8 * q + 4 * h);                     \
-                _Pragma("unroll") for (int r = 0; r < 4; ++r)                                \
-                    if (relu) v_[r] = fmaxf(v_[r], 0.0f);                                    \
-                pk_[q][0] = pack_bf16x2(v_[0], v_[1]);                                       \
-                pk_[q][1] = pack_bf16x2(v_[2], v_[3]);                                       \
-            }                                                                                \
-            uint32_t r8_[2][4];                                                              \
-            _Pragma("unroll") for (int pr = 0; pr < 2; ++pr)                                 \
-                _Pragma("unroll") for (int w = 0; w < 2; ++w) {                              \
-                    const auto sw_ = __builtin_amdgcn_permlane32_swap(pk_[2 * pr][w], pk_[2 * pr + 1][w], false, false); \
-                    r8_[pr][w] = sw_[0];                                                     \
-                    r8_[pr][2 + w] = sw_[1];                                                 \
+        if (merged) {                                                                        \
+            /* blocks in pairs, merged so that each store writes whole 128-byte */          \
+            /* lines: lane l holds pixel (l & 7) (+8 in the second register) */             \
+            _Pragma("unroll") for (int mb = 0; mb < MB; mb += 2) {                           \
+                uint32_t o0_[2][4], o1_[2][4];                                               \
+                pw_pack(mb, o0_);                                                            \
+                pw_pack(mb + 1, o1_);                                                        \
+                const int co_ = c0_ + mb * 32 + cl + ((lane & 8) ? 32 : 0);                  \
+                int tapoff_ = 0, cc_ = co_;                                                  \
+                if (SHUF) {                                                                  \
+                    const int tap_ = co_ / sh.cout;                                          \
+                    cc_ = co_ - tap_ * sh.cout;                                              \
+                    const int kh_ = tap_ / sh.kw;                                            \
+                    tapoff_ = kh_ * sh.wo + tap_ - kh_ * sh.kw;                              \
                 }                                                                            \
-            uint32_t o_[2][4];                                                               \
-            _Pragma("unroll") for (int d = 0; d < 4; ++d) {                                  \
-                const auto sw_ = __builtin_amdgcn_permlane16_swap(r8_[0][d], r8_[1][d], false, false); \
-                o_[0][d] = sw_[0];                                                           \
-                o_[1][d] = sw_[1];                                                           \
+                _Pragma("unroll") for (int e = 0; e < 2; ++e) {                              \
+                    uint32_t ra_[4], rb_[4];                                                 \
+                    _Pragma("unroll") for (int d = 0; d < 4; ++d) {                          \
+                        ra_[d] = __builtin_amdgcn_update_dpp(o0_[e][d], o1_[e][d], 0x118, 0xf, 0xc, false); \
+                        rb_[d] = __builtin_amdgcn_update_dpp(o1_[e][d], o0_[e][d], 0x108, 0xf, 0x3, false); \
+                    }                                                                        \
+                    _Pragma("unroll") for (int g_ = 0; g_ < 2; ++g_) {                       \
+                        const int pp_ = pix8_[e][g_];                                        \
+                        const int off_ = SHUF ? ((pp_ + tapoff_) * sh.cout + cc_) * 2 : (pp_ + co_) * 2; \
+                        const int so_ = pp_ >= 0 && co_ < cout ? off_ : kOOB;                \
+                        const uint4 ov_ = g_ ? make_uint4(rb_[0], rb_[1], rb_[2], rb_[3])   \
+                                             : make_uint4(ra_[0], ra_[1], ra_[2], ra_[3]);  \
+                        if (stream) store16<kStoreStream>(yr, so_, ov_);                     \
+                        else store16(yr, so_, ov_);                                          \
+                    }                                                                        \
+                }                                                                            \
             }                                                                                \
+        } else {                                                                             \
+        _Pragma("unroll") for (int mb = 0; mb < MB; ++mb) {                                  \
+            uint32_t o_[2][4];                                                               \
+            pw_pack(mb, o_);                                                                 \
             const int co_ = c0_ + mb * 32 + cl;                                              \
             int tapoff_ = 0, cc_ = co_;  /* pixel shuffle: row (tap, cc) */                  \
             if (SHUF) {                                                                      \
@@ -305,6 +362,7 @@ __global__ __launch_bounds__(kPwThreads, 2) void pw_kernel(const bf16_t* __restr
                            make_uint2(o_[e][2], o_[e][3]));                                  \
                 }                                                                            \
             }                                                                                \
+        }                                                                                    \
         }                                                                                    \
     } while (0)
 
