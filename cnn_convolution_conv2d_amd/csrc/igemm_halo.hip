@@ -271,67 +271,11 @@ __global__ __launch_bounds__(NT, waves_per_simd(NT, MINB, halo_lds_bytes(BM, TH,
 #pragma unroll
     for (int j = 0; j < TN; ++j) bf0[j] = *reinterpret_cast<const bf16x8*>(halo + b_rd[j]);
 
-    // Epilogue of the current tile (tc): bias, ReLU, bf16; lane l < 32 of a
-    // 32x32 block holds channels 8q+r (q = 0..3, r = 0..3) of pixel l, lane
-    // l + 32 channels 8q+4+r; one v_permlane32_swap per pair of q gives each
-    // lane 8 consecutive channels (16 bytes) of one pixel.
-    const int half = lane >> 5;
-    const bool vec16 = (s.Cout % 8 == 0) && (s.cout_g % 8 == 0);
+    // Epilogue of the current tile (tc): bias (this tile's bias buffer),
+    // ReLU, bf16, whole-line stores (the shared tile epilogue).
 #define HALO_EPILOGUE()                                                                      \
-    do {                                                                                     \
-        int pix_[TN];                                                                        \
-        _Pragma("unroll") for (int j = 0; j < TN; ++j) {                                     \
-            const int p_ = wn * WTN + j * 32 + (lane & 31);                                  \
-            const int ho_ = tc.ho0 + p_ / TW, wo_ = tc.wo0 + p_ % TW;                        \
-            pix_[j] = (ho_ < s.Ho && wo_ < s.Wo) ? ((tc.n * s.Ho + ho_) * s.Wo + wo_) * s.Cout : -1; \
-        }                                                                                    \
-        const int cw_ = tc.ct * BM + wm * WTM;  /* first channel (within the group) of the wave */ \
-        const Affine4 aff_(s.scale, s.shift, s.Cout);                                        \
-        _Pragma("unroll") for (int i = 0; i < TM; ++i) {                                     \
-            float4 b4_[4];                                                                   \
-            _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                  \
-                b4_[q] = make_float4(0.f, 0.f, 0.f, 0.f);                                    \
-                if (BIAS)                                                                    \
-                    b4_[q] = *reinterpret_cast<const float4*>(                               \
-                        sbias + (k & 1) * B_BYTES + (wm * WTM + i * 32 + 8 * q + 4 * half) * 4); \
-            }                                                                                \
-            _Pragma("unroll") for (int j = 0; j < TN; ++j) {                                 \
-                uint32_t pk_[4][2];                                                          \
-                _Pragma("unroll") for (int q = 0; q < 4; ++q) {                              \
-                    float v_[4];                                                             \
-                    _Pragma("unroll") for (int r = 0; r < 4; ++r)                            \
-                        v_[r] = acc[i][j][4 * q + r] + (&b4_[q].x)[r];                       \
-                    if (s.scale) aff_.apply(v_, tc.g * s.cout_g + cw_ + i * 32 + 8 * q + 4 * half); \
-                    _Pragma("unroll") for (int r = 0; r < 4; ++r)                            \
-                        if (RELU) v_[r] = fmaxf(v_[r], 0.0f);                                \
-                    pk_[q][0] = pack_bf16x2(v_[0], v_[1]);                                   \
-                    pk_[q][1] = pack_bf16x2(v_[2], v_[3]);                                   \
-                }                                                                            \
-                _Pragma("unroll") for (int pr = 0; pr < 2; ++pr) {                           \
-                    uint32_t lo_[2], hi_[2];                                                 \
-                    _Pragma("unroll") for (int w = 0; w < 2; ++w) {                          \
-                        const auto sw_ = __builtin_amdgcn_permlane32_swap(                   \
-                            pk_[2 * pr][w], pk_[2 * pr + 1][w], false, false);               \
-                        lo_[w] = sw_[0];                                                     \
-                        hi_[w] = sw_[1];                                                     \
-                    }                                                                        \
-                    /* out-of-range pixels and channels get an offset past  \
-                       the end: the buffer store drops them */               \
-                    const int co_ = cw_ + i * 32 + 16 * pr + 8 * half;                       \
-                    const int off_ = (pix_[j] + tc.g * s.cout_g + co_) * 2;                  \
-                    if (vec16) {                                                             \
-                        store16(yr, pix_[j] >= 0 && co_ < s.cout_g ? off_ : kOOB,            \
-                                make_uint4(lo_[0], lo_[1], hi_[0], hi_[1]));                 \
-                    } else {                                                                 \
-                        store8(yr, pix_[j] >= 0 && co_ < s.cout_g ? off_ : kOOB,             \
-                               make_uint2(lo_[0], lo_[1]));                                  \
-                        store8(yr, pix_[j] >= 0 && co_ + 4 < s.cout_g ? off_ + 8 : kOOB,     \
-                               make_uint2(hi_[0], hi_[1]));                                  \
-                    }                                                                        \
-                }                                                                            \
-            }                                                                                \
-        }                                                                                    \
-    } while (0)
+    tile_epilogue<TM, TN, WTM, WTN, TH, TW, BIAS, RELU>(acc, sbias + (k & 1) * B_BYTES, yr, s, tc, tc.ct * BM, \
+                                                        wm, wn, lane)
 
     // One K-step.  RA_LD/RA_ST: weight registers loaded now (for step + 3) /
     // stored now (step + 2, loaded one step ago); RH_LD/HL_LD, RH_ST/HL_ST:
