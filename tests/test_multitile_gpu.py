@@ -88,9 +88,8 @@ CAPPED = [
     # unrolled 3x3 kernel: 128- and 64-channel tiles, dilation 2 with
     # 128-channel tiles (5x5-span halo buffers), Cin/G % 32 != 0, the 8x32
     # pixel block, groups
-    ((2, 64, 37, 35, 256, 3, 3, 1, 1, 1, 1), HALO, (1, 7, 24)),
     ((2, 128, 33, 40, 64, 3, 3, 1, 1, 1, 1), HALO, (4, 16)),
-    ((2, 64, 30, 34, 256, 3, 3, 1, 2, 2, 2), HALO, (1, 9, 32)),
+    ((2, 64, 30, 34, 256, 3, 3, 1, 2, 2, 2), HALO, (1, 9, 20, 32)),
     ((2, 256, 21, 19, 256, 3, 3, 1, 2, 2, 4), HALO, (5, 40)),
     ((2, 40, 25, 27, 128, 3, 3, 1, 1, 1, 1), HALO, (3, 8)),
     ((2, 72, 25, 27, 96, 3, 3, 1, 1, 1, 1), HALO, (2, 13)),
@@ -100,6 +99,16 @@ CAPPED = [
     # workgroup of each XCD; 40 leaves 32 (no spread); 27 is not a multiple
     # of 8 (plain round-robin)
     ((2, 64, 96, 96, 128, 3, 3, 1, 1, 1, 1), HALO, (27, 40, 64)),
+    # two or four 128-channel tiles per pixel block: 36 tiles (2 images x 3 x
+    # 3 blocks x 2), a last round of 1, 1, 4 and 12 tiles under caps 5, 7, 8
+    # and 24, none under 12; dilation 2 with 256 channels per group (cap 40:
+    # a last round of 8 tiles on 40 workgroups); Cin/G % 32 != 0; the 8x32
+    # block (8 tiles, cap 7)
+    ((2, 64, 37, 35, 256, 3, 3, 1, 1, 1, 1), HALO, (1, 5, 7, 8, 12, 24)),
+    ((2, 64, 30, 34, 512, 3, 3, 1, 2, 2, 2), HALO, (1, 5, 8, 40)),
+    ((4, 64, 8, 64, 128, 3, 3, 1, 1, 1, 1), HALO, (3, 7)),
+    ((2, 40, 25, 27, 256, 3, 3, 1, 1, 1, 1), HALO, (2, 3, 6)),
+    ((1, 64, 20, 22, 512, 3, 3, 1, 1, 1, 1), HALO, (1, 3)),
     # 3x3 stride 2 on the phase-split window (4x32 pixel blocks; the halo
     # path forced): 128- and 64-channel tiles, ragged output channels,
     # Cin/G % 32 != 0, padding 0 and 2, groups, more than one 32-wide block
@@ -161,6 +170,8 @@ NATURAL = [
     (10, 64, 128, 128, 256, 3, 3, 1, 2, 2, 2),
     # unrolled 3x3, 72 input channels (chunks of 32, 32, 8): 20 x 64 tiles
     (20, 72, 128, 128, 128, 3, 3, 1, 1, 1, 1),
+    # the 3x3 workload's shape at 6 images: 6 x 49 blocks x 2 channel tiles
+    (6, 64, 112, 112, 256, 3, 3, 1, 1, 1, 1),
     # 3x3 stride 2, 128 -> 128 at 56x56 -> 28x28: 80 images x 7 blocks
     (80, 128, 56, 56, 128, 3, 3, 2, 1, 1, 1),
 ]
