@@ -46,6 +46,11 @@ fp32 first layer and the whole depthwise-separable pair.
 
 ``--hbm-ceiling`` only times a plain device copy that moves each HBM-bound
 layer's total bytes (context for their HBM fractions).
+
+``--power SECONDS`` adds ``sustained``: after the timed steps the layer runs
+back to back for SECONDS while amd-smi reads the socket power and the
+graphics clock every two seconds (the clock the chip holds under the kernel,
+against the 2.4 GHz the spec peaks assume).
 """
 from __future__ import annotations
 
@@ -54,6 +59,7 @@ import hashlib
 import json
 import math
 import os
+import subprocess
 import sys
 import time
 
@@ -200,7 +206,6 @@ def oracle_single_thread():
     """The oracle on one host thread over the whole fp32 first layer and the
     whole depthwise-separable pair (each layer separately), in a child
     process started with OMP_NUM_THREADS=1; seconds and GFLOP/s per layer."""
-    import subprocess
     env = dict(os.environ, OMP_NUM_THREADS="1")
     r = subprocess.run([sys.executable, "-c", _SINGLE_THREAD_CHILD, ROOT], env=env, capture_output=True,
                        text=True, timeout=300)
@@ -273,7 +278,81 @@ def time_nchw_entry(c2, ly, x, w, b, ho, wo, tdt, dt_lib, dev, stream, steps, fl
             "ms_per_call": round(ms, 5), "value": round(value, 3), "unit": unit, "buffer_sets": 1}
 
 
-def bench_layer(cid, li, steps, warmup, cpu_seconds, with_cpu, winograd=False, with_nchw=True):
+def smi_sample(gpu):
+    """One amd-smi reading of the GPU's socket power (W) and graphics clock
+    (MHz, the mean over its graphics partitions, one per XCD)."""
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-p", "-c", "-g", str(gpu)], capture_output=True, text=True,
+                           timeout=20)
+    except (OSError, subprocess.TimeoutExpired) as e:
+        return {"error": str(e)[:200]}
+
+    def num(t):
+        v = t.split(":", 1)[1].split()
+        try:
+            return float(v[0])
+        except (IndexError, ValueError):
+            return None
+
+    power, clocks, in_gfx = None, [], False
+    for ln in r.stdout.splitlines():
+        t = ln.strip()
+        if t.startswith("SOCKET_POWER:") and power is None:
+            power = num(t)
+        elif t.endswith(":") and not t.startswith("CLK"):
+            in_gfx = t.startswith("GFX_")
+        elif in_gfx and t.startswith("CLK:"):
+            c = num(t)
+            if c is not None:
+                clocks.append(c)
+    if power is None and not clocks:
+        return {"error": (r.stderr or r.stdout or "no output")[-200:]}
+    return {"socket_power_w": power,
+            "gfx_clock_mhz": round(sum(clocks) / len(clocks), 1) if clocks else None,
+            "gfx_clocks_mhz": clocks}
+
+
+def sustained_power(step, stream, seconds, gpu):
+    """Launch STEP back to back for SECONDS, reading amd-smi every two seconds
+    from the second second on: the power and clock the chip holds under the
+    kernel (the spec peaks assume 2.4 GHz)."""
+    import threading
+    import torch
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        if stop.wait(2.0):
+            return
+        while not stop.is_set():
+            samples.append(smi_sample(gpu))
+            stop.wait(2.0)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    t0 = time.perf_counter()
+    th.start()
+    n, spans = 0, []
+    while time.perf_counter() - t0 < seconds:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(100):
+            step(n + i)
+        e1.record(stream)
+        e1.synchronize()
+        spans.append(e0.elapsed_time(e1) / 100)
+        n += 100
+    stop.set()
+    th.join()
+    good = [x for x in samples if "error" not in x]
+    out = {"seconds": seconds, "launches": n, "mean_us": round(float(np.mean(spans)) * 1e3, 2),
+           "samples": samples}
+    for k in ("socket_power_w", "gfx_clock_mhz"):
+        v = [x[k] for x in good if x.get(k) is not None]
+        if v:
+            out[k + "_mean"] = round(float(np.mean(v)), 1)
+    return out
+
+
+def bench_layer(cid, li, steps, warmup, cpu_seconds, with_cpu, winograd=False, with_nchw=True, power_seconds=0.0):
     import torch
     import cnn_convolution_conv2d_amd as c2
 
@@ -349,6 +428,7 @@ def bench_layer(cid, li, steps, warmup, cpu_seconds, with_cpu, winograd=False, w
     launch_ms = np.array([a.elapsed_time(e) for a, e in ev])
     mean_ms = float(launch_ms.mean())
     ms_per_step = wall * 1e3 / steps
+    power = sustained_power(step, stream, power_seconds, torch.cuda.current_device()) if power_seconds > 0 else None
 
     unit = "TFLOP/s" if bound in ("mfma", "alu") else "GB/s"
     if unit == "TFLOP/s":
@@ -399,6 +479,8 @@ def bench_layer(cid, li, steps, warmup, cpu_seconds, with_cpu, winograd=False, w
     }
     if nchw is not None:
         line["nchw_entry"] = nchw
+    if power is not None:
+        line["sustained"] = power
     if winograd:
         # FLOP/s above count the convolution's own multiply-adds; the matrix
         # cores execute 16/36 of them (F(2x2,3x3)) on the transformed data
@@ -578,6 +660,9 @@ def main(argv=None):
                     help="force the library's kernel path (conv2d_set_path_override) for the timed layers")
     ap.add_argument("--launch-times", action="store_true",
                     help="add every timed launch's duration (us, in launch order) to the JSON line")
+    ap.add_argument("--power", type=float, default=0.0, metavar="SECONDS",
+                    help="after the timed steps, launch the layer back to back for SECONDS and read the "
+                         "socket power and graphics clock with amd-smi every two seconds")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-nchw", action="store_true",
@@ -619,7 +704,7 @@ def main(argv=None):
     if a.winograd and not a.all:
         cid, li = (int(v) for v in a.layer.split(":"))
         print(json.dumps(bench_layer(cid, li, a.steps, a.warmup, a.cpu_seconds, with_cpu=not a.no_cpu_baseline,
-                                     winograd=True)), flush=True)
+                                     winograd=True, power_seconds=a.power)), flush=True)
         return 0
     if a.separable and not a.all:
         print(json.dumps(bench_separable(a.steps, a.warmup, a.cpu_seconds,
@@ -633,7 +718,7 @@ def main(argv=None):
         c2.conv2d_set_path_override(getattr(c2, "PATH_" + a.path.upper()))
     for cid, li in layers:
         line = bench_layer(cid, li, a.steps, a.warmup, a.cpu_seconds,
-                           with_cpu=not a.no_cpu_baseline, with_nchw=not a.no_nchw)
+                           with_cpu=not a.no_cpu_baseline, with_nchw=not a.no_nchw, power_seconds=a.power)
         if not a.no_cpu_baseline and (cid, li) == layers[0]:
             line["cpu_baseline"]["single_thread"] = oracle_single_thread()
         print(json.dumps(line), flush=True)
