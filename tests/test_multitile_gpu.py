@@ -107,6 +107,9 @@ CAPPED = [
     ((2, 64, 37, 35, 256, 3, 3, 1, 1, 1, 1), HALO, (1, 5, 7, 8, 12, 24)),
     ((2, 64, 30, 34, 512, 3, 3, 1, 2, 2, 2), HALO, (1, 5, 8, 40)),
     ((4, 64, 8, 64, 128, 3, 3, 1, 1, 1, 1), HALO, (3, 7)),
+    # one image of 3 x 3 blocks, two channel tiles: 18 tiles, a last round of
+    # 3 or 2 tiles under caps 3 and 4
+    ((1, 64, 37, 35, 256, 3, 3, 1, 1, 1, 1), HALO, (1, 3, 4)),
     ((2, 40, 25, 27, 256, 3, 3, 1, 1, 1, 1), HALO, (2, 3, 6)),
     ((1, 64, 20, 22, 512, 3, 3, 1, 1, 1, 1), HALO, (1, 3)),
     # 3x3 stride 2 on the phase-split window (4x32 pixel blocks; the halo
