@@ -171,43 +171,53 @@ namespace {
 // width (lpnh.cn section 4.2: the stride-1 convolution of the zero-inserted
 // input, of which only these taps meet real pixels).  All four phases of a
 // block of positions read rows u - 1 .. u + 2 at most, so a workgroup stages
-// that input window once per channel chunk and every tap of every phase reads
+// that input window once per channel block and every tap of every phase reads
 // its MFMA operands from it at a shifted offset -- instead of gathering each
 // tap's slice again from L2 as the phase-split gather kernel does.
 //
-// Workgroup: 8 x 32 phase-grid positions of one image x 32 output channels;
-// 8 waves, wave w computes phase ((w % 4) / 2, w % 2) for position rows
-// 4*(w / 4) .. +3: four 32x32 MFMA tiles (32 channels x one row of 32
-// positions); two waves per SIMD hide each other's LDS latency.  Per chunk
-// of 32 input channels, copied into LDS by buffer-to-LDS loads,
-// triple-buffered (a chunk's copies are issued two chunks ahead, so their
-// latency is covered by two chunks of work):
-//   weights [16 taps][32 co][4 pieces of 8 channels]  (32 KB)
-//   window  [10 rows][34 columns][4 pieces]             (21 KB)
-// A 64-byte row (one co and tap, or one pixel) holds its four 16-byte pieces
-// XOR-swizzled with (row / 4) mod 4, so any 16 consecutive rows read at the
-// same logical piece land in 16 distinct 16-byte bank groups; the copies apply
-// the swizzle on the global side (lane order in LDS is fixed).
-constexpr int kThWin = 10, kTwWin = 34;                // window rows, columns
+// Workgroup: 8 x 32 phase-grid positions of one image x 64 output channels;
+// 8 waves, wave w computes phase p = w % 4 = (ph_h, ph_w) for position rows
+// 4*(w / 4) .. +3 and all 64 channels: eight 32x32 MFMA tiles (two channel
+// blocks x four rows of 32 positions), so per 16-channel step two A and four
+// B operand reads feed eight MFMAs.  Waves w and w + 4 share a SIMD and hide
+// each other's LDS latency.
+//
+// The channel loop runs over blocks of 64 input channels, so that each
+// pixel's and each weight row's slice of a block is one whole 128-byte line
+// (the copies' cost is set by the number of lines they touch, not by their
+// bytes).  Per block, the 10 x 34 input window (48 KB) is copied once and
+// double-buffered; the block is then worked in four steps (jh, jw), in each
+// of which every phase applies its tap (k0h + 2jh, k0w + 2jw), whose weights
+// for the four phases (32 KB) are copied one step ahead into a double
+// buffer.  All copies are buffer-to-LDS loads.  LDS layout, in 16-byte units:
+//   weights [2][4 phases][64 co][8 pieces of 8 channels]  (a row's pieces
+//           XOR-swizzled with (row / 2) mod 8)
+//   window  [2][10 rows][34 columns][9 units]  (8 pieces and one unit of
+//           padding: an odd pitch)
+// With either layout 16 consecutive rows read at one logical piece fall in
+// 16 distinct 16-byte bank groups, and lanes 16..31 read 16 rows further,
+// a multiple of 16 units away.
+constexpr int kThBK = 64;                               // input channels per block
+constexpr int kThWin = 10, kTwWin = 34;                 // window rows, columns
 constexpr int kThPos = 8, kTwPos = 32;                  // positions per tile
-constexpr int kThCo = 32;                               // output channels per workgroup
+constexpr int kThCo = 64;                               // output channels per workgroup
 constexpr int kThThreads = 512, kThWaves = kThThreads / 64;
 constexpr int kThRows = kThPos / 2;                     // position rows per wave
-constexpr int kThWUnits = 16 * kThCo * 4;               // 2048
-constexpr int kThXUnits = kThWin * kTwWin * 4;          // 1360
-constexpr int kThXCopies = 24;                          // window copy instructions: 3 per wave
-constexpr int kThBuf = kThWUnits + kThXUnits;           // 3408 units
-constexpr int kThLds = 3 * kThBuf * 16;                 // 163584 bytes
-// copy instructions each wave issues per chunk (4 weight + 3 window): the
-// wait for a chunk leaves exactly the next chunk's copies outstanding
-constexpr int kThCopiesPerWave = 32 / kThWaves + kThXCopies / kThWaves;
-static_assert(kThCopiesPerWave == 7, "vmcnt immediate below");
+constexpr int kThPitch = 9;                             // window units per pixel
+constexpr int kThWUnits = 4 * kThCo * 8;                // 2048 per step
+constexpr int kThXUnits = kThWin * kTwWin * kThPitch;   // 3060 per block
+constexpr int kThWCopies = kThWUnits / 64;              // 32: 4 per wave per step
+constexpr int kThXCopies = 48;                          // 6 per wave per block, the last ones overlapping
+constexpr int kThLds = (2 * kThWUnits + 2 * kThXUnits) * 16;   // 163456 bytes
+static_assert(kThWCopies == 4 * kThWaves && kThXCopies == 6 * kThWaves, "copy split below");
+static_assert(64 * (kThXCopies - 1) >= kThXUnits - 64, "window copies cover the window");
+static_assert(kThLds <= 163840, "LDS");
 
 struct TconvHaloGrid {
     int N, Cin, H, W, Cout, pad, Ho, Wo;
     int lo;            // window origin relative to the tile: floor(P/2) - 1
     int nbu, nbv, ncb; // tiles along u, along v, output-channel groups
-    int nchunk;        // 32-channel chunks
+    int nblk;          // 64-channel blocks
 };
 
 typedef __attribute__((address_space(3))) void* th_lds_t;
@@ -222,76 +232,124 @@ __device__ __forceinline__ void th_barrier() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-__device__ __forceinline__ void th_stage(uint4* __restrict__ wdst, uint4* __restrict__ xdst,
-                                         const TconvHaloGrid& g, __amdgpu_buffer_rsrc_t wr,
-                                         __amdgpu_buffer_rsrc_t xr, int kc, int co0, int n, int ih0, int iw0,
-                                         int wave, int lane) {
-    const int c0 = kc * 32;
-    // weights: instruction i covers tap i/2, output channels 16*(i%2) + lane/4
+// Weights of step t (jh = t / 2, jw = t % 2) of block b: instruction i
+// writes units 64i .. 64i+63, i.e. rows 8i .. 8i+7 of [phase][co], each row
+// the 8 pieces of one 128-byte line.
+__device__ __forceinline__ void th_stage_w(uint4* __restrict__ wdst, const TconvHaloGrid& g,
+                                           __amdgpu_buffer_rsrc_t wr, int b, int t, int co0, int wave,
+                                           int lane) {
+    const int c0 = b * kThBK, jh = t >> 1, jw = t & 1;
 #pragma unroll
-    for (int m = 0; m < 32 / kThWaves; ++m) {
+    for (int m = 0; m < kThWCopies / kThWaves; ++m) {
         const int i = wave + kThWaves * m;
-        const int tap = i >> 1, col = 16 * (i & 1) + (lane >> 2);
-        const int piece = (lane & 3) ^ ((col >> 2) & 3);
-        const int co = co0 + col;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (th_lds_t)(wdst + i * 64), 16,
-                                                 co < g.Cout ? ((co * 16 + tap) * g.Cin + c0 + 8 * piece) * 2 : kOOB,
-                                                 0, 0, 0);
+        const int row = 8 * i + (lane >> 3);
+        const int p = row >> 6, col = row & 63;
+        const int piece = (lane & 7) ^ ((col >> 1) & 7);
+        const int kh = (((p >> 1) + g.pad) & 1) + 2 * jh, kw = (((p & 1) + g.pad) & 1) + 2 * jw;
+        const int co = co0 + col, ci = c0 + 8 * piece;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            wr, (th_lds_t)(wdst + i * 64), 16,
+            co < g.Cout && ci < g.Cin ? ((co * 16 + kh * 4 + kw) * g.Cin + ci) * 2 : kOOB, 0, 0, 0);
     }
-    // window: unit s = pixel*4 + slot, pixel = row*34 + column; instruction k
-    // writes units base .. base+63 with base = min(64k, 1360-64), so the last
-    // instructions overlap (rewriting the same values) instead of running past
-    // the window
+}
+
+// Window of block b, copy instructions k = wave + 8j for j in [j0, j1):
+// instruction k writes units base .. base+63, base = min(64k, 3060-64) (the
+// last ones overlap, rewriting the same values, instead of running past the
+// window); unit s is slot s % 9 of window pixel s / 9 = row*34 + column,
+// slot 8 the padding (written with zeros).
+__device__ __forceinline__ void th_stage_x(uint4* __restrict__ xdst, const TconvHaloGrid& g,
+                                           __amdgpu_buffer_rsrc_t xr, int b, int j0, int j1, int n, int ih0,
+                                           int iw0, int wave, int lane) {
+    const int c0 = b * kThBK;
 #pragma unroll
-    for (int m = 0; m < kThXCopies / kThWaves; ++m) {
-        const int k = wave + kThWaves * m;
+    for (int j = j0; j < j1; ++j) {
+        const int k = wave + kThWaves * j;
         const int base = min(64 * k, kThXUnits - 64);
         const int s = base + lane;
-        const int wp = s >> 2, piece = (s & 3) ^ ((wp >> 2) & 3);
+        const int wp = s / kThPitch, slot = s - wp * kThPitch;
         const int wrow = wp / kTwWin, wcol = wp - wrow * kTwWin;
-        const int ih = ih0 + wrow, iw = iw0 + wcol;
-        const bool ok = (unsigned)ih < (unsigned)g.H && (unsigned)iw < (unsigned)g.W;
+        const int ih = ih0 + wrow, iw = iw0 + wcol, ci = c0 + 8 * slot;
+        const bool ok = slot < 8 && ci < g.Cin && (unsigned)ih < (unsigned)g.H && (unsigned)iw < (unsigned)g.W;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (th_lds_t)(xdst + base), 16,
-                                                 ok ? (((n * g.H + ih) * g.W + iw) * g.Cin + c0 + 8 * piece) * 2 : kOOB,
+                                                 ok ? (((n * g.H + ih) * g.W + iw) * g.Cin + ci) * 2 : kOOB,
                                                  0, 0, 0);
     }
 }
 
-// One chunk: start the copies of chunk `next` (two ahead), then the phase's four taps x two
-// 16-channel steps x four position rows of MFMAs from the current buffers
-// (tapo already includes this wave's first row).
-__device__ __forceinline__ void th_chunk(const uint4* __restrict__ wc, const uint4* __restrict__ xc,
-                                         uint4* __restrict__ wn, uint4* __restrict__ xn, f32x16 acc[kThRows],
-                                         const TconvHaloGrid& g, __amdgpu_buffer_rsrc_t wr,
-                                         __amdgpu_buffer_rsrc_t xr, int next, int co0, int n, int ih0, int iw0,
-                                         int wave, int lane, const int tapk[4], const int tapo[4]) {
-    if (next >= 0) th_stage(wn, xn, g, wr, xr, next, co0, n, ih0, iw0, wave, lane);
+// One step: four 16-channel K-steps of eight MFMAs from this wave's phase
+// row of the weight buffer and its tap's shifted view of the window (tapo:
+// the window pixel of position (r0, 0) for this step's tap).
+__device__ __forceinline__ void th_step(const uint4* __restrict__ wc, const uint4* __restrict__ xc,
+                                        f32x16 (&acc)[2][kThRows], int p, int tapo, int lane) {
     const int frow = lane & 31, half = lane >> 5;
-    // Eight operand groups per chunk: (tap t, 16-channel step ks) = (gi / 2,
-    // gi % 2), each one A operand and four B operands (the wave's position
-    // rows).  Two register sets: group gi+1 is read while group gi's MFMAs
-    // issue; the scheduling fence keeps the compiler from collapsing the
-    // pipeline into one read per MFMA.
-    bf16x8 a[2], b[2][kThRows];
-    auto load_group = [&](int gi, int set) {
-        const int t = gi >> 1, q = 2 * (gi & 1) + half;   // this lane's 8-channel piece
-        a[set] = __builtin_bit_cast(bf16x8, wc[(tapk[t] * kThCo + frow) * 4 + (q ^ ((frow >> 2) & 3))]);
+    const int wsw = (frow >> 1) & 7;                         // swizzle of weight row 32i + frow
+    const uint4* const wrow = wc + (p * kThCo + frow) * 8;
+    const uint4* const xrow = xc + (tapo + frow) * kThPitch;
+    // Two register sets: K-step ks+1 is read while ks's MFMAs issue; the
+    // scheduling fence keeps the compiler from collapsing the pipeline into
+    // one read per MFMA.
+    bf16x8 a[2][2], bb[2][kThRows];
+    auto load_group = [&](int ks, int set) {
+        const int q = 2 * ks + half;                         // this lane's 8-channel piece
 #pragma unroll
-        for (int r = 0; r < kThRows; ++r) {
-            const int wp = tapo[t] + r * kTwWin + frow;   // window pixel of position (r, frow)
-            b[set][r] = __builtin_bit_cast(bf16x8, xc[wp * 4 + (q ^ ((wp >> 2) & 3))]);
-        }
+        for (int i = 0; i < 2; ++i) a[set][i] = __builtin_bit_cast(bf16x8, wrow[32 * 8 * i + (q ^ wsw)]);
+#pragma unroll
+        for (int r = 0; r < kThRows; ++r)
+            bb[set][r] = __builtin_bit_cast(bf16x8, xrow[r * kTwWin * kThPitch + q]);
     };
     load_group(0, 0);
 #pragma unroll
-    for (int gi = 0; gi < 8; ++gi) {
-        if (gi + 1 < 8) load_group(gi + 1, (gi + 1) & 1);
+    for (int ks = 0; ks < 4; ++ks) {
+        if (ks + 1 < 4) load_group(ks + 1, (ks + 1) & 1);
 #pragma unroll
-        for (int r = 0; r < kThRows; ++r)
-            acc[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[gi & 1], b[gi & 1][r], acc[r], 0, 0, 0);
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int r = 0; r < kThRows; ++r)
+                acc[i][r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks & 1][i], bb[ks & 1][r], acc[i][r], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
     }
 }
+
+// Pack one 32x32 result block into bf16 with ReLU: out[h] holds channels
+// cl .. cl+7 (cl = 16*((lane/16) % 2) + 8*(lane/32)) of position
+// 16h + lane % 16.  In the 32x32 result layout lane l < 32 holds channels
+// 8q + r (q, r = 0..3) of position l and lane l + 32 channels 8q + 4 + r; a
+// lane-half swap gives each lane 8 consecutive channels, a row swap then
+// 16 positions per register.
+template <bool RELU>
+__device__ __forceinline__ void th_pack(const f32x16& acc, uint32_t (&out)[2][4]) {
+    uint32_t pk[4][2];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        float v[4] = {acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+        if (RELU)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = fmaxf(v[i], 0.0f);
+        pk[q][0] = pack_bf16x2(v[0], v[1]);
+        pk[q][1] = pack_bf16x2(v[2], v[3]);
+    }
+    uint32_t r8[2][4];
+#pragma unroll
+    for (int pr = 0; pr < 2; ++pr)
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+            const auto sw = __builtin_amdgcn_permlane32_swap(pk[2 * pr][w], pk[2 * pr + 1][w], false, false);
+            r8[pr][w] = sw[0];
+            r8[pr][2 + w] = sw[1];
+        }
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const auto sw = __builtin_amdgcn_permlane16_swap(r8[0][d], r8[1][d], false, false);
+        out[0][d] = sw[0];
+        out[1][d] = sw[1];
+    }
+}
+
+// Window copies a wave issues during step t of a block for the next block:
+// j in [th_xj(t), th_xj(t+1)), two in each of the first two steps, one in
+// each of the last two.
+constexpr int th_xj(int t) { return t < 2 ? 2 * t : t + 2; }
 
 template <bool BIAS, bool RELU>
 __global__ __launch_bounds__(kThThreads, 1) void tconv_halo_kernel(const bf16_t* __restrict__ x,
@@ -299,6 +357,8 @@ __global__ __launch_bounds__(kThThreads, 1) void tconv_halo_kernel(const bf16_t*
                                                             const float* __restrict__ bias,
                                                             bf16_t* __restrict__ y, TconvHaloGrid g) {
     extern __shared__ uint4 thlds[];
+    uint4* const wbuf = thlds;                       // [2][kThWUnits]
+    uint4* const xbuf = thlds + 2 * kThWUnits;       // [2][kThXUnits]
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     int item = xcd_tile_index();
@@ -316,116 +376,119 @@ __global__ __launch_bounds__(kThThreads, 1) void tconv_halo_kernel(const bf16_t*
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(wp, (uint32_t)g.Cout * 16u * g.Cin * 2u);
     const __amdgpu_buffer_rsrc_t yr = make_rsrc(y, (uint32_t)g.N * g.Ho * g.Wo * g.Cout * 2u);
 
-    // this wave's phase, its first position row, and its four taps: weight tap
-    // index kh*4 + kw and the window pixel of position (r0, 0) for that tap
-    const int ph_h = (wave >> 1) & 1, ph_w = wave & 1, r0 = kThRows * (wave >> 2);
-    const int k0h = (ph_h + g.pad) & 1, bh = (ph_h + g.pad) >> 1;
-    const int k0w = (ph_w + g.pad) & 1, bw = (ph_w + g.pad) >> 1;
-    int tapk[4], tapo[4];
+    // this wave's phase, its first position row, and for each step t = (jh,
+    // jw) the window pixel of position (r0, 0) under that step's tap
+    const int p = wave & 3, ph_h = p >> 1, ph_w = p & 1, r0 = kThRows * (wave >> 2);
+    const int bh = (ph_h + g.pad) >> 1, bw = (ph_w + g.pad) >> 1;
+    int tapo[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        const int jh = t >> 1, jw = t & 1;
-        tapk[t] = (k0h + 2 * jh) * 4 + k0w + 2 * jw;
-        tapo[t] = (r0 + bh - jh - g.lo) * kTwWin + (bw - jw - g.lo);
-    }
+    for (int t = 0; t < 4; ++t) tapo[t] = (r0 + bh - (t >> 1) - g.lo) * kTwWin + (bw - (t & 1) - g.lo);
+    // rows of this phase inside the output: 2u + ph_h < Ho; a wave whose
+    // four rows all lie below takes part in the copies and barriers only
+    const bool act = 2 * (u0 + r0) + ph_h < g.Ho;
 
-    f32x16 acc[kThRows];
-#pragma unroll
-    for (int r = 0; r < kThRows; ++r) acc[r] = f32x16{};
-    th_stage(thlds, thlds + kThWUnits, g, wr, xr, 0, co0, n, ih0, iw0, wave, lane);
-    if (g.nchunk > 1) th_stage(thlds + kThBuf, thlds + kThBuf + kThWUnits, g, wr, xr, 1, co0, n, ih0, iw0, wave, lane);
-    int bc = 0;   // buffer of chunk kc
-    for (int kc = 0; kc < g.nchunk; ++kc) {
-        // this wave's copies of chunk kc have landed (those of kc+1 may still
-        // be in flight: loads complete in order), then the barrier for
-        // everyone's; it also frees the buffer of chunk kc-1 for chunk kc+2
-        if (kc + 1 < g.nchunk) __builtin_amdgcn_s_waitcnt(0x0f77);  // vmcnt(7)
-        else __builtin_amdgcn_s_waitcnt(0x0f70);                    // vmcnt(0)
-        th_barrier();
-        const int bn = bc == 0 ? 2 : bc - 1;   // buffer of chunk kc+2 (= that of kc-1)
-        uint4* const cur = thlds + bc * kThBuf;
-        uint4* const nxt = thlds + bn * kThBuf;
-        th_chunk(cur, cur + kThWUnits, nxt, nxt + kThWUnits, acc, g, wr, xr, kc + 2 < g.nchunk ? kc + 2 : -1,
-                 co0, n, ih0, iw0, wave, lane, tapk, tapo);
-        bc = bc == 2 ? 0 : bc + 1;
-    }
-
-    // epilogue: lane holds position (r, lane % 32), output channels
-    // 8q + 4*(lane/32) + (0..3) in acc[r][4q + 0..3]
+    // accumulators start at the bias: lane holds channels co0 + 32i + 8q +
+    // 4*(lane/32) + (0..3) in acc[i][r][4q + 0..3]
     const __amdgpu_buffer_rsrc_t br = make_rsrc(bias, BIAS ? (uint32_t)g.Cout * 4u : 0u);
-    float4 b4[4];
+    f32x16 acc[2][kThRows];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int co = co0 + 8 * q + 4 * (lane >> 5);
-        b4[q] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (BIAS) b4[q] = __builtin_bit_cast(float4, load16(br, co < g.Cout ? co * 4 : kOOB));
+    for (int i = 0; i < 2; ++i) {
+        f32x16 b0 = f32x16{};
+        if (BIAS)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int co = co0 + 32 * i + 8 * q + 4 * (lane >> 5);
+                const float4 b4 = __builtin_bit_cast(float4, load16(br, co < g.Cout ? co * 4 : kOOB));
+                b0[4 * q] = b4.x;
+                b0[4 * q + 1] = b4.y;
+                b0[4 * q + 2] = b4.z;
+                b0[4 * q + 3] = b4.w;
+            }
+#pragma unroll
+        for (int r = 0; r < kThRows; ++r) acc[i][r] = b0;
     }
+
+    th_stage_x(xbuf, g, xr, 0, 0, 6, n, ih0, iw0, wave, lane);
+    th_stage_w(wbuf, g, wr, 0, 0, co0, wave, lane);
+    for (int b = 0; b < g.nblk; ++b) {
+        const bool more = b + 1 < g.nblk;   // the next block's window is copied during this one
+        uint4* const xc = xbuf + (b & 1) * kThXUnits;
+        uint4* const xn = xbuf + ((b + 1) & 1) * kThXUnits;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            // This wave's copies of this step's weights have landed: issued at
+            // the start of the previous step, they are followed only by that
+            // step's window copies for this block (if it issued any); the
+            // first step also needs all of this block's window.  Loads
+            // complete in order.  Then the barrier for everyone's copies; it
+            // also frees the buffers the copies below overwrite (the previous
+            // step's weights, the previous block's window).
+            if (t == 0 || !more) __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
+            else if (t == 3) __builtin_amdgcn_s_waitcnt(0x0f71);       // vmcnt(1)
+            else __builtin_amdgcn_s_waitcnt(0x0f72);                   // vmcnt(2)
+            th_barrier();
+            if (t < 3) th_stage_w(wbuf + ((t + 1) & 1) * kThWUnits, g, wr, b, t + 1, co0, wave, lane);
+            else if (more) th_stage_w(wbuf, g, wr, b + 1, 0, co0, wave, lane);
+            if (more) th_stage_x(xn, g, xr, b + 1, th_xj(t), th_xj(t + 1), n, ih0, iw0, wave, lane);
+            if (act) th_step(wbuf + (t & 1) * kThWUnits, xc, acc, p, tapo[t], lane);
+        }
+    }
+    if (!act) return;
+
     if (g.Cout % 8 == 0) {
-        // Two lane swaps regroup a row's 32 x 32 block so that each lane holds
-        // 8 consecutive channels (16 bytes) of one position: channels
-        // co0 + cl .. +7 of position 16*h + lane % 16 (h = 0, 1), and one
-        // store instruction writes 64 contiguous bytes of each of 16 pixels,
-        // with the streaming (nt) policy (measured 46.1 -> 39.7 us on the
-        // 4x4 stride-2 256->128 layer against 8-byte stores).
+        // Per position row: both channel blocks packed (th_pack), then
+        // regrouped with 8-lane row shifts (DPP) so that lane l holds
+        // channels cl2 = cl + 32*((l/8) % 2) of position (l % 8) (+8 in the
+        // second register): one store instruction writes the 64 channels
+        // (128 contiguous bytes) of each of 8 pixels, whole lines, with the
+        // streaming (nt) policy.
         const int cl = ((lane >> 4) & 1) * 16 + (lane >> 5) * 8;
+        const int co = co0 + cl + ((lane & 8) ? 32 : 0);
 #pragma unroll
         for (int r = 0; r < kThRows; ++r) {
             const int oh = 2 * (u0 + r0 + r) + ph_h;
-            uint32_t pk[4][2];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                float v[4] = {acc[r][4 * q] + b4[q].x, acc[r][4 * q + 1] + b4[q].y, acc[r][4 * q + 2] + b4[q].z,
-                              acc[r][4 * q + 3] + b4[q].w};
-                if (RELU)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) v[i] = fmaxf(v[i], 0.0f);
-                pk[q][0] = pack_bf16x2(v[0], v[1]);
-                pk[q][1] = pack_bf16x2(v[2], v[3]);
-            }
-            uint32_t r8[2][4];
-#pragma unroll
-            for (int pr = 0; pr < 2; ++pr)
-#pragma unroll
-                for (int w = 0; w < 2; ++w) {
-                    const auto sw = __builtin_amdgcn_permlane32_swap(pk[2 * pr][w], pk[2 * pr + 1][w], false, false);
-                    r8[pr][w] = sw[0];
-                    r8[pr][2 + w] = sw[1];
-                }
-            uint32_t out[2][4];
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                const auto sw = __builtin_amdgcn_permlane16_swap(r8[0][d], r8[1][d], false, false);
-                out[0][d] = sw[0];
-                out[1][d] = sw[1];
-            }
+            uint32_t o0[2][4], o1[2][4];
+            th_pack<RELU>(acc[0][r], o0);
+            th_pack<RELU>(acc[1][r], o1);
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                const int ow = 2 * (v0 + 16 * h + (lane & 15)) + ph_w;
-                const int co = co0 + cl;
-                const bool ok = oh < g.Ho && ow < g.Wo && co < g.Cout;
-                store16<kStoreStream>(yr, ok ? (((n * g.Ho + oh) * g.Wo + ow) * g.Cout + co) * 2 : kOOB,
-                                      make_uint4(out[h][0], out[h][1], out[h][2], out[h][3]));
+                uint32_t ra_[4], rb_[4];
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    // lanes 8..15 of each row: block 1's piece from 8 lanes lower
+                    ra_[d] = __builtin_amdgcn_update_dpp(o0[h][d], o1[h][d], 0x118 /* row_shr:8 */, 0xf, 0xc, false);
+                    // lanes 0..7 of each row: block 0's piece from 8 lanes higher
+                    rb_[d] = __builtin_amdgcn_update_dpp(o1[h][d], o0[h][d], 0x108 /* row_shl:8 */, 0xf, 0x3, false);
+                }
+                const int owa = 2 * (v0 + 16 * h + (lane & 7)) + ph_w, owb = owa + 16;
+                const bool oka = oh < g.Ho && owa < g.Wo && co < g.Cout;
+                const bool okb = oh < g.Ho && owb < g.Wo && co < g.Cout;
+                store16<kStoreStream>(yr, oka ? (((n * g.Ho + oh) * g.Wo + owa) * g.Cout + co) * 2 : kOOB,
+                                      make_uint4(ra_[0], ra_[1], ra_[2], ra_[3]));
+                store16<kStoreStream>(yr, okb ? (((n * g.Ho + oh) * g.Wo + owb) * g.Cout + co) * 2 : kOOB,
+                                      make_uint4(rb_[0], rb_[1], rb_[2], rb_[3]));
             }
         }
         return;
     }
     const int ow = 2 * (v0 + (lane & 31)) + ph_w;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int co = co0 + 8 * q + 4 * (lane >> 5);
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int r = 0; r < kThRows; ++r) {
-            const int oh = 2 * (u0 + r0 + r) + ph_h;
-            float v[4] = {acc[r][4 * q] + b4[q].x, acc[r][4 * q + 1] + b4[q].y, acc[r][4 * q + 2] + b4[q].z,
-                          acc[r][4 * q + 3] + b4[q].w};
-            if (RELU)
+        for (int q = 0; q < 4; ++q) {
+            const int co = co0 + 32 * i + 8 * q + 4 * (lane >> 5);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) v[i] = fmaxf(v[i], 0.0f);
-            const bool ok = oh < g.Ho && ow < g.Wo && co < g.Cout;
-            store8(yr, ok ? (((n * g.Ho + oh) * g.Wo + ow) * g.Cout + co) * 2 : kOOB,
-                   make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])));
+            for (int r = 0; r < kThRows; ++r) {
+                const int oh = 2 * (u0 + r0 + r) + ph_h;
+                float v[4] = {acc[i][r][4 * q], acc[i][r][4 * q + 1], acc[i][r][4 * q + 2], acc[i][r][4 * q + 3]};
+                if (RELU)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = fmaxf(v[e], 0.0f);
+                const bool ok = oh < g.Ho && ow < g.Wo && co < g.Cout;
+                store8(yr, ok ? (((n * g.Ho + oh) * g.Wo + ow) * g.Cout + co) * 2 : kOOB,
+                       make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])));
+            }
         }
-    }
 }
 
 template <bool BIAS, bool RELU>
@@ -462,7 +525,7 @@ hipError_t launch_tconv_halo(const Shape& s, const void* x, const void* w_packed
     g.nbu = ((s.Ho + 1) / 2 + kThPos - 1) / kThPos;
     g.nbv = ((s.Wo + 1) / 2 + kTwPos - 1) / kTwPos;
     g.ncb = (s.Cout + kThCo - 1) / kThCo;
-    g.nchunk = s.Cin / 32;
+    g.nblk = (s.Cin + kThBK - 1) / kThBK;
     const bf16_t* xt = static_cast<const bf16_t*>(x);
     const bf16_t* wt = static_cast<const bf16_t*>(w_packed);
     bf16_t* yt = static_cast<bf16_t*>(y);
