@@ -130,6 +130,8 @@ HALO = [
     (1, 32, 6, 5, 40, 2, 1),      # padding 2
     (2, 96, 4, 3, 8, 3, 0),       # padding 3, three channel chunks
     (1, 32, 1, 1, 4, 1, 0),       # a single input pixel
+    (2, 160, 11, 37, 192, 1, 1),  # three channel blocks, the last half past Cin; three channel groups; two column tiles
+    (1, 192, 9, 30, 72, 2, 1),    # three whole channel blocks; a partial second channel group
 ]
 
 
