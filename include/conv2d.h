@@ -260,7 +260,8 @@ int conv2d_fwd_winograd_nhwc(const void* x, const void* w_wino, const float* bia
  * pixels whose rows land in distinct output pixels.  CONV2D_PATH_IGEMM_HALO
  * for stride 2 with a 4x4 kernel (dilation 1, groups 1, padding <= 3, bf16,
  * Cin % 32 == 0, Cout % 4 == 0): each workgroup stages one input window per
- * channel chunk in LDS and computes all four output phases from it.
+ * block of 64 input channels in LDS and computes all four output phases from
+ * it.
  * CONV2D_PATH_IGEMM_GATHER
  * (bf16, Cin/G % 8 == 0, Cout/G % 4 == 0) splits the output into its S x S
  * phases (rows and columns of one residue mod S); each phase is an implicit
