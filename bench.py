@@ -50,9 +50,10 @@ layer's total bytes (context for their HBM fractions).
 ``--power SECONDS`` adds ``sustained``: after the timed steps the layer runs
 back to back for SECONDS while amd-smi reads the socket power and the
 graphics clock every two seconds (the clock the chip holds under the kernel,
-against the 2.4 GHz the spec peaks assume).  A single-layer run of the 3x3
-headline layer (the default) records 6 s of it unless --power is given; it
-never enters value or the roofline figures.
+against the 2.4 GHz the spec peaks assume).  It never enters value or the
+roofline figures, and the default line does not take it (so a kernel trace
+of the default command covers exactly the launches the line is computed
+from).
 """
 from __future__ import annotations
 
@@ -281,16 +282,6 @@ def time_nchw_entry(c2, ly, x, w, b, ho, wo, tdt, dt_lib, dev, stream, steps, fl
 
 
 HEADLINE_LAYER = "2:0"
-HEADLINE_POWER_SECONDS = 6.0
-
-
-def power_seconds_default(a):
-    """Seconds of the sustained power/clock sample: --power when given, else
-    a short one for a single-layer run of the headline layer, else none."""
-    if a.power is not None:
-        return max(0.0, a.power)
-    headline = not a.all and not a.separable and not a.winograd and a.layer == HEADLINE_LAYER
-    return HEADLINE_POWER_SECONDS if headline else 0.0
 
 
 def smi_sample(gpu):
@@ -675,10 +666,9 @@ def main(argv=None):
                     help="force the library's kernel path (conv2d_set_path_override) for the timed layers")
     ap.add_argument("--launch-times", action="store_true",
                     help="add every timed launch's duration (us, in launch order) to the JSON line")
-    ap.add_argument("--power", type=float, default=None, metavar="SECONDS",
+    ap.add_argument("--power", type=float, default=0.0, metavar="SECONDS",
                     help="after the timed steps, launch the layer back to back for SECONDS and read the "
-                         "socket power and graphics clock with amd-smi every two seconds (default: 6 for "
-                         "a single-layer run of the 3x3 headline layer, else 0)")
+                         "socket power and graphics clock with amd-smi every two seconds")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-nchw", action="store_true",
@@ -716,7 +706,6 @@ def main(argv=None):
         for ln in hbm_ceiling(a.steps):
             print(json.dumps(ln), flush=True)
         return 0
-    a.power = power_seconds_default(a)
     _builder().ensure_built()  # rebuilds a missing or stale library
     if a.winograd and not a.all:
         cid, li = (int(v) for v in a.layer.split(":"))

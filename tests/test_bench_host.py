@@ -1,6 +1,6 @@
 """Host-side pieces of bench.py: the launch-duration statistics, the amd-smi
-reading behind ``--power`` and when it runs by default, and the refusal of
-more than one GPU.  No GPU is used."""
+reading behind ``--power``, and the refusal of more than one GPU.  No GPU
+is used."""
 import os
 import subprocess
 import sys
@@ -73,18 +73,3 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
-
-
-def test_power_sample_defaults_to_the_headline_run_only():
-    def args(**kw):
-        d = dict(power=None, all=False, separable=False, winograd=False, layer=bench.HEADLINE_LAYER)
-        d.update(kw)
-        return types.SimpleNamespace(**d)
-    assert bench.power_seconds_default(args()) == bench.HEADLINE_POWER_SECONDS > 0
-    assert bench.power_seconds_default(args(layer="5:3")) == 0.0
-    assert bench.power_seconds_default(args(all=True)) == 0.0
-    assert bench.power_seconds_default(args(winograd=True)) == 0.0
-    assert bench.power_seconds_default(args(separable=True)) == 0.0
-    assert bench.power_seconds_default(args(power=0.0)) == 0.0
-    assert bench.power_seconds_default(args(layer="6:0", power=3.0)) == 3.0
-
